@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Throughput of GroupQueryAttention over a shared KV buffer on one MI355X.
+
+Prints ONE JSON line. The headline step is the fp16 split-KV decode
+(B=16, H=32, Hkv=8, D=128, M=4096, past lengths U{512..4095}, seed 2):
+`value` is its algorithmic HBM bytes per step / wall time per step (GB/s).
+The same line carries the bf16 causal prefill (B=4, H=32, Hkv=8, D=128,
+S=2048, rotary; TFLOP/s over causal pairs), the fp16 ragged continuation
+(B=8, H=28, Hkv=4, S=128) and the bf16 sliding-window decode (B=8, M=W=4096,
+cache full, evict one row per step), each with its roofline fraction.
+
+Timing: inputs are resident in HBM before the timed region; each step rotates
+over enough independent input sets (>= 1 GiB) that the 256 MB Infinity Cache
+cannot serve repeated reads. HIP events recorded on the launch stream around
+each call give the per-call device time; wall time over K steps (synchronised
+on both sides) gives ms_per_step.
+
+The CPU baseline times the fp64 oracle (as it stands) on a bounded sample of
+the decode workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, 2.5 PFLOP/s
+METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GPU"
+POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
+MIN_ROTATION_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# input sets
+# ----------------------------------------------------------------------------
+
+class DevSet:
+    """One independent set of device inputs for a case (same lengths)."""
+
+    def __init__(self, case, seed, torch, canonical=False):
+        import gpu_helpers as H
+        dt = H.torch_dtype(case.dtype)
+        self.case = case
+        if canonical:
+            d = H.DevCase(case)
+            self.q, self.k_new, self.v_new = d.q, d.k_new, d.v_new
+            self.k_cache, self.v_cache = d.k_cache, d.v_cache
+            self.cos, self.sin = d.cos, d.sin
+        else:
+            g = torch.Generator(device="cuda").manual_seed(seed)
+
+            def rnd(shape):
+                return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dt)
+
+            B, S, H_, Hkv, D, M = (case.batch, case.new_tokens, case.num_heads, case.kv_num_heads,
+                                   case.head_size, case.max_seq_len)
+            self.q, self.k_new, self.v_new = rnd((B, S, H_ * D)), rnd((B, S, Hkv * D)), rnd((B, S, Hkv * D))
+            self.k_cache, self.v_cache = rnd((B, Hkv, M, D)), rnd((B, Hkv, M, D))
+            lens = torch.as_tensor(case.seqlens_k, device="cuda").long()
+            dead = torch.arange(M, device="cuda")[None, :] >= lens[:, None]
+            for c in (self.k_cache, self.v_cache):
+                c.view(torch.int16)[dead[:, None, :, None].expand_as(c)] = np.int16(
+                    np.uint16(POISON16[case.dtype]).view(np.int16))
+            self.cos = self.sin = None
+            if case.cos is not None:
+                self.cos = torch.from_numpy(case.cos).cuda()
+                self.sin = torch.from_numpy(case.sin).cuda()
+        self.lens_host = np.asarray(case.seqlens_k, np.int32).copy()
+        self.lens_dev = torch.from_numpy(self.lens_host.copy()).cuda()
+        self.out = torch.empty_like(self.q)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.q, self.k_new, self.v_new,
+                                                           self.k_cache, self.v_cache))
+
+
+def make_sets(case, torch, base_seed):
+    first = DevSet(case, base_seed, torch, canonical=True)
+    n = max(4, math.ceil(MIN_ROTATION_BYTES / first.nbytes()))
+    return [first] + [DevSet(case, base_seed * 1000 + i, torch) for i in range(1, n)]
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (what the method must move or compute per call)
+# ----------------------------------------------------------------------------
+
+def decode_bytes(case, lens_attended, window=-1):
+    """K and V rows attended (incl. the new token), new rows written, Q read, O written."""
+    e = 4 if case.dtype == "fp32" else 2
+    B, H, Hkv, D = case.batch, case.num_heads, case.kv_num_heads, case.head_size
+    rows = 0
+    for L in lens_attended:
+        n = L + 1 if window <= 0 else min(L + 1, window)
+        rows += n
+    return rows * Hkv * D * e * 2 + B * Hkv * D * e * 2 + 2 * B * H * D * e
+
+
+def prefill_flops(case):
+    """4*D flops (QK^T and PV) per visible (query, key) pair."""
+    S, D, H = case.new_tokens, case.head_size, case.num_heads
+    W = case.local_window_size
+    pairs = 0
+    for L in case.seqlens_k:
+        L = int(L)
+        for i in range(S):
+            p = L + i
+            lo = max(0, p - W + 1) if W > 0 else 0
+            pairs += p - lo + 1
+    return 4.0 * D * pairs * H
+
+
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
+
+def time_calls(torch, sets, call, steps, warmup):
+    """Run warmup + steps calls rotating over sets; returns (wall_ms/step, event_ms list)."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s = sets[(warmup + i) % len(sets)]
+        ev[i][0].record(stream)
+        call(s)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall, per
+
+
+def stats(per):
+    a = np.sort(np.asarray(per))
+    return {"mean_ms": float(a.mean()), "median_ms": float(np.median(a)),
+            "p10_ms": float(a[int(0.1 * (len(a) - 1))]), "p90_ms": float(a[int(0.9 * (len(a) - 1))])}
+
+
+def decode_call(gqa):
+    def call(s):
+        c = s.case
+        gqa.gqa_attention_decode(s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.lens_host, s.lens_dev,
+                                 s.out, scale=c.scale, local_window_size=c.local_window_size,
+                                 cos_cache=s.cos, sin_cache=s.sin)
+    return call
+
+
+def prefill_call(gqa):
+    def call(s):
+        c = s.case
+        gqa.gqa_attention_prefill(s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.lens_host, s.lens_dev,
+                                  s.out, scale=c.scale, local_window_size=c.local_window_size,
+                                  cos_cache=s.cos, sin_cache=s.sin,
+                                  rotary_interleaved=c.rotary_interleaved)
+    return call
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(case, budget_s=12.0):
+    from oracle import gqa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    nb = 4
+    sub = case.copy()
+    sub.batch = nb
+    for f in ("seqlens_k", "q", "k_new", "v_new", "k_cache", "v_cache"):
+        setattr(sub, f, getattr(case, f)[:nb].copy())
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        st, out, *_ = O.gqa_attention(sub, "decode")
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    byts = decode_bytes(sub, [int(x) for x in sub.seqlens_k]) * reps
+    return {"value": byts / el / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, decode of the first {nb} of 16 sequences "
+                       f"(past lengths {sub.seqlens_k.tolist()}), {reps} repetitions in {el:.1f} s; "
+                       f"{len(os.sched_getaffinity(0))} host cores visible, {blas} BLAS threads; "
+                       f"{platform.processor() or platform.machine()}")}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="c2,c3,c4,c5", help="workloads to run (c2 is the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the op is not sharded across "
+                                   "GPUs (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import torch
+    import gqa_inputs as gi
+    import grouped_query_kv_amd as gqa
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    which = set(args.only.split(","))
+    result = {}
+
+    # --- headline: fp16 split-KV decode -------------------------------------
+    c2 = gi.config(2)
+    log(f"[bench] C2 decode sets: building (lens={c2.seqlens_k.tolist()})")
+    sets = make_sets(c2, torch, 2)
+    log(f"[bench] C2 decode: {len(sets)} input sets, timing {args.steps} steps")
+    wall, per = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
+    c2_bytes = decode_bytes(c2, [int(x) for x in c2.seqlens_k])
+    st2 = stats(per)
+    achieved = c2_bytes / (st2["mean_ms"] * 1e-3) / 1e9
+    value = c2_bytes / (wall * 1e-3) / 1e9
+    del sets
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if "c3" in which:
+        c3 = gi.config(3)
+        log("[bench] C3 prefill sets: building")
+        sets = make_sets(c3, torch, 3)
+        steps = max(5, args.steps // 2)
+        log(f"[bench] C3 prefill: {len(sets)} input sets, timing {steps} steps")
+        w3, per3 = time_calls(torch, sets, prefill_call(gqa), steps, max(2, args.warmup // 2))
+        fl = prefill_flops(c3)
+        s3 = stats(per3)
+        tf = fl / (s3["mean_ms"] * 1e-3) / 1e12
+        extra["prefill_c3"] = {"workload": "bf16 causal prefill B=4 H=32 Hkv=8 D=128 S=2048 rotary",
+                               "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
+                               "ms_per_call_wall": w3, "flops": fl, **s3}
+        del sets
+        torch.cuda.empty_cache()
+    if "c4" in which:
+        c4 = gi.config(4)
+        log("[bench] C4 continuation sets: building")
+        sets = make_sets(c4, torch, 4)
+        log(f"[bench] C4 continuation: {len(sets)} input sets")
+        w4, per4 = time_calls(torch, sets, prefill_call(gqa), args.steps, args.warmup)
+        fl = prefill_flops(c4)
+        s4 = stats(per4)
+        tf = fl / (s4["mean_ms"] * 1e-3) / 1e12
+        extra["continuation_c4"] = {"workload": "fp16 ragged continuation B=8 H=28 Hkv=4 D=128 S=128",
+                                    "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
+                                    "ms_per_call_wall": w4, "flops": fl,
+                                    "lens": c4.seqlens_k.tolist(), **s4}
+        del sets
+        torch.cuda.empty_cache()
+    if "c5" in which:
+        c5 = gi.config(5)
+        log("[bench] C5 window decode sets: building")
+        sets = make_sets(c5, torch, 5)
+        log(f"[bench] C5 window decode: {len(sets)} input sets")
+        w5, per5 = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
+        s5 = stats(per5)
+        att = decode_bytes(c5, [4095] * 8, window=4096)
+        shift = 8 * 8 * 4095 * 128 * 2 * 2 * 2      # read + write of every kept row, K and V
+        extra["window_decode_c5"] = {
+            "workload": "bf16 sliding-window decode B=8 H=32 Hkv=8 D=128 M=W=4096, full cache",
+            "step_gbs_vs_fused_minimum": (att + shift // 2) / (s5["mean_ms"] * 1e-3) / 1e9,
+            "step_bytes_unfused": att + shift, "attention_bytes": att,
+            "ms_per_call_wall": w5, **s5}
+        del sets
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        cpu = cpu_baseline(c2)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "fp16 decode, B=16 H=32 Hkv=8 D=128 M=4096, past lengths U{512..4095} "
+                               "(seed 2), 1 new token per sequence",
+                   "global_batch": 16, "seq_len": 4096, "parallelism": "none (1 GPU)",
+                   "seqlens_k": c2.seqlens_k.tolist()},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode call (all launches of gqa_attention_decode)",
+                     "bytes_per_call": c2_bytes, **st2},
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

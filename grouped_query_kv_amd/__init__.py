@@ -1,0 +1,265 @@
+"""Python binding of libgqa.so: GroupQueryAttention over a shared KV buffer.
+
+Argument marshalling only. Every step of the op (rotary, eviction, append,
+attention, split merge) runs in the HIP kernels behind the C ABI declared in
+include/gqa.h; this module reads shapes off torch tensors, checks that they
+agree, and passes raw device pointers and the current HIP stream. There is no
+CPU or PyTorch fallback: if the library has not been built, importing this
+package raises.
+
+The functions carry the C entry points' names:
+  gqa_append_kv, gqa_attention_prefill, gqa_attention_decode,
+  gqa_evict_window, gqa_workspace_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa.so")
+
+GQA_OK, GQA_ERR_NO_ROOM, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(6)
+GQA_FP32, GQA_FP16, GQA_BF16 = 0, 1, 2
+STATUS_NAMES = {0: "ok", 1: "no_room", 2: "invalid_arg", 3: "unsupported", 4: "workspace", 5: "hip"}
+EXPORTED = ("gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill", "gqa_attention_decode",
+            "gqa_evict_window", "gqa_status_string", "gqa_last_error")
+
+
+class GQAError(RuntimeError):
+    """A non-OK status from the library; `.status` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("new_tokens", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("kv_num_heads", ctypes.c_int32),
+                ("head_size", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("local_window_size", ctypes.c_int32),
+                ("cos_cache", ctypes.c_void_p), ("sin_cache", ctypes.c_void_p),
+                ("rotary_rows", ctypes.c_int32), ("rotary_interleaved", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m grouped_query_kv_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32P, VP = ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+    lib.gqa_workspace_bytes.argtypes = [P]
+    lib.gqa_workspace_bytes.restype = ctypes.c_size_t
+    lib.gqa_append_kv.argtypes = [P, ctypes.POINTER(Options), VP, VP, VP, VP, I32P, VP, VP]
+    lib.gqa_append_kv.restype = ctypes.c_int
+    for name in ("gqa_attention_prefill", "gqa_attention_decode"):
+        f = getattr(lib, name)
+        f.argtypes = [P, ctypes.POINTER(Options), VP, VP, VP, VP, VP, I32P, VP, VP, VP,
+                      ctypes.c_size_t, VP]
+        f.restype = ctypes.c_int
+    lib.gqa_evict_window.argtypes = [P, ctypes.c_int32, VP, VP, I32P, VP, I32P, VP, ctypes.c_size_t, VP]
+    lib.gqa_evict_window.restype = ctypes.c_int
+    lib.gqa_status_string.argtypes = [ctypes.c_int]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_last_error.argtypes = []
+    lib.gqa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != GQA_OK:
+        msg = (lib.gqa_last_error() or b"").decode() or lib.gqa_status_string(status).decode()
+        raise GQAError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: GQA_FP32, torch.float16: GQA_FP16, torch.bfloat16: GQA_BF16}
+    if t.dtype not in m:
+        raise GQAError(GQA_ERR_INVALID_ARG, f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _host_lengths(seqlens_k_host, B: int):
+    a = np.ascontiguousarray(np.asarray(seqlens_k_host.cpu() if hasattr(seqlens_k_host, "cpu")
+                                        else seqlens_k_host), dtype=np.int32)
+    if a.shape != (B,):
+        raise GQAError(GQA_ERR_INVALID_ARG, f"seqlens_k_host has shape {a.shape}, expected ({B},)")
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _cache_shape(k_cache, v_cache):
+    if k_cache.dim() != 4 or tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise GQAError(GQA_ERR_INVALID_ARG, "k_cache / v_cache must both be [B, Hkv, M, D]")
+    if k_cache.dtype != v_cache.dtype:
+        raise GQAError(GQA_ERR_INVALID_ARG, "k_cache and v_cache dtypes differ")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def _same_buffer(past, present, what: str):
+    # The op may bind one tensor to both past and present; we require it and
+    # check the addresses at run time.
+    if present is not None and present.data_ptr() != past.data_ptr():
+        raise GQAError(GQA_ERR_INVALID_ARG, f"past_{what} and present_{what} must share one buffer")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise GQAError(GQA_ERR_INVALID_ARG, "tensors must be contiguous")
+
+
+def make_shape(B, S, H, Hkv, D, M, dtype) -> Shape:
+    return Shape(B, S, H, Hkv, D, M, dtype)
+
+
+def make_options(scale=0.0, local_window_size=-1, cos_cache=None, sin_cache=None,
+                 rotary_interleaved=False) -> Options:
+    rows = int(cos_cache.shape[0]) if cos_cache is not None else 0
+    return Options(float(scale), int(local_window_size), _ptr(cos_cache), _ptr(sin_cache), rows,
+                   int(bool(rotary_interleaved)))
+
+
+_workspaces = {}
+
+
+def gqa_workspace_bytes(B, S, H, Hkv, D, M, dtype: int) -> int:
+    return int(lib.gqa_workspace_bytes(ctypes.byref(make_shape(B, S, H, Hkv, D, M, dtype))))
+
+
+def workspace_for(shape: Shape, device):
+    """A zero-filled workspace for this shape, cached per device and size.
+
+    Calls that share a cached workspace must not overlap in time (same stream
+    or synchronised streams)."""
+    n = int(lib.gqa_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        return None, 0
+    key = (str(device), n)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = _torch().zeros(n, dtype=_torch().uint8, device=device)
+        _workspaces[key] = ws
+    return ws, n
+
+
+def _kv_common(k_new, k_cache, v_cache, num_heads):
+    B, S, hkvd = (int(x) for x in k_new.shape)
+    Bc, Hkv, M, D = _cache_shape(k_cache, v_cache)
+    if Bc != B or hkvd != Hkv * D:
+        raise GQAError(GQA_ERR_INVALID_ARG, "k_new must be [B, S, Hkv*D] matching the cache")
+    return B, S, Hkv, M, D
+
+
+def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev, *,
+                  cos_cache=None, sin_cache=None, rotary_interleaved=False,
+                  present_key=None, present_value=None, stream=None):
+    """Append S new rows per sequence at seqlens_k (rotary on K if tables given)."""
+    _same_buffer(k_cache, present_key, "key")
+    _same_buffer(v_cache, present_value, "value")
+    _contig(k_new, v_new, k_cache, v_cache, cos_cache, sin_cache)
+    if tuple(k_new.shape) != tuple(v_new.shape) or k_new.dim() != 3:
+        raise GQAError(GQA_ERR_INVALID_ARG, "k_new / v_new must both be [B, S, Hkv*D]")
+    B, S, Hkv, M, D = _kv_common(k_new, k_cache, v_cache, None)
+    shape = make_shape(B, S, Hkv, Hkv, D, M, dtype_code(k_cache))
+    opts = make_options(0.0, -1, cos_cache, sin_cache, rotary_interleaved)
+    hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
+    _check(lib.gqa_append_kv(ctypes.byref(shape), ctypes.byref(opts), _ptr(k_new), _ptr(v_new),
+                             _ptr(k_cache), _ptr(v_cache), hp, _ptr(seqlens_k_dev), _stream(stream)))
+
+
+def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev, out,
+               scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
+               present_key, present_value, workspace, stream):
+    _same_buffer(k_cache, present_key, "key")
+    _same_buffer(v_cache, present_value, "value")
+    _contig(q, k_new, v_new, k_cache, v_cache, cos_cache, sin_cache)
+    if q.dim() != 3 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.dim() != 3:
+        raise GQAError(GQA_ERR_INVALID_ARG, "q must be [B, S, H*D], k_new/v_new [B, S, Hkv*D]")
+    B, S, Hkv, M, D = _kv_common(k_new, k_cache, v_cache, None)
+    if int(q.shape[0]) != B or int(q.shape[1]) != S or int(q.shape[2]) % D:
+        raise GQAError(GQA_ERR_INVALID_ARG, "q must be [B, S, H*D] with the cache's D")
+    H = int(q.shape[2]) // D
+    if q.dtype != k_cache.dtype or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise GQAError(GQA_ERR_INVALID_ARG, "q, k_new, v_new and the caches must share a dtype")
+    if out is None:
+        out = _torch().empty_like(q)
+    _contig(out)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise GQAError(GQA_ERR_INVALID_ARG, "out must match q")
+    shape = make_shape(B, S, H, Hkv, D, M, dtype_code(q))
+    opts = make_options(scale, local_window_size, cos_cache, sin_cache, rotary_interleaved)
+    hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
+    if workspace is None:
+        ws, nbytes = workspace_for(shape, q.device)
+    else:
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    _check(fn(ctypes.byref(shape), ctypes.byref(opts), _ptr(q), _ptr(k_new), _ptr(v_new),
+              _ptr(k_cache), _ptr(v_cache), hp, _ptr(seqlens_k_dev), _ptr(out), _ptr(ws),
+              nbytes, _stream(stream)))
+    return out
+
+
+def gqa_attention_prefill(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
+                          out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
+                          sin_cache=None, rotary_interleaved=False, present_key=None,
+                          present_value=None, workspace=None, stream=None):
+    """The whole op for S >= 1 new tokens; returns out [B, S, H*D]."""
+    return _attention(lib.gqa_attention_prefill, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
+                      seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
+                      rotary_interleaved, present_key, present_value, workspace, stream)
+
+
+def gqa_attention_decode(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
+                         out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
+                         sin_cache=None, rotary_interleaved=False, present_key=None,
+                         present_value=None, workspace=None, stream=None):
+    """The whole op for one new token per sequence; returns out [B, 1, H*D]."""
+    return _attention(lib.gqa_attention_decode, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
+                      seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
+                      rotary_interleaved, present_key, present_value, workspace, stream)
+
+
+def gqa_evict_window(k_cache, v_cache, seqlens_k_host, seqlens_k_dev, incoming: int, *,
+                     workspace=None, stream=None):
+    """Compact each sequence so `incoming` tokens fit; returns the new host lengths."""
+    _contig(k_cache, v_cache)
+    B, Hkv, M, D = _cache_shape(k_cache, v_cache)
+    shape = make_shape(B, 0, Hkv, Hkv, D, M, dtype_code(k_cache))
+    hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
+    after = np.zeros(B, np.int32)
+    if workspace is None:
+        ws, nbytes = workspace_for(shape, k_cache.device)
+    else:
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    _check(lib.gqa_evict_window(ctypes.byref(shape), int(incoming), _ptr(k_cache), _ptr(v_cache), hp,
+                                _ptr(seqlens_k_dev), after.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                _ptr(ws), nbytes, _stream(stream)))
+    return after

@@ -1,0 +1,125 @@
+// Append: scatter the S new K/V rows of every (b, kv head) into the shared
+// BNSH buffer at row L'_b + i. Source rows [B, S, Hkv*D] are read in their
+// own order (fully coalesced); each destination row is one contiguous run.
+// Rotary (on K only) uses the fp64 rounding rule of rotate_pair.
+#include "gqa_device.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+// Destination row of sequence b's first new token. With a window the buffer
+// was just compacted, so the append starts at min(L, M - S).
+__device__ inline int dest_base(const int32_t* lens, int b, int S, int M, bool evicted) {
+  int L = clamp_len(lens[b], 0, M);
+  if (evicted) L = L < M - S ? L : M - S;
+  return clamp_len(L, 0, M - S);
+}
+
+// One thread per `U`-sized unit of a row; the flat source index is the unit
+// index itself because [B, S, Hkv, D] flattens in the same order.
+template <class U>
+__global__ void __launch_bounds__(256) copy_rows_kernel(const U* __restrict__ src,
+                                                        U* __restrict__ dst,
+                                                        const int32_t* __restrict__ lens, int B,
+                                                        int S, int Hkv, int M, int upr,
+                                                        int evicted) {
+  const int64_t total = int64_t(B) * S * Hkv * upr;
+  for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < total;
+       idx += int64_t(gridDim.x) * blockDim.x) {
+    int64_t r = idx;
+    const int u = int(r % upr); r /= upr;
+    const int g = int(r % Hkv); r /= Hkv;
+    const int i = int(r % S);
+    const int b = int(r / S);
+    const int row = dest_base(lens, b, S, M, evicted != 0) + i;
+    dst[((int64_t(b) * Hkv + g) * M + row) * upr + u] = src[idx];
+  }
+}
+
+// One thread per rotary pair of K.
+template <class T>
+__global__ void __launch_bounds__(256) rotary_rows_kernel(
+    const typename T::bits* __restrict__ src, typename T::bits* __restrict__ dst,
+    const int32_t* __restrict__ lens, int B, int S, int Hkv, int D, int M,
+    const float* __restrict__ cosv, const float* __restrict__ sinv, int rot_rows,
+    int interleaved, int evicted) {
+  const int half = D / 2;
+  const int64_t total = int64_t(B) * S * Hkv * half;
+  for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < total;
+       idx += int64_t(gridDim.x) * blockDim.x) {
+    int64_t r = idx;
+    const int j = int(r % half); r /= half;
+    const int g = int(r % Hkv); r /= Hkv;
+    const int i = int(r % S);
+    const int b = int(r / S);
+    const int pos = clamp_len(clamp_len(lens[b], 0, M) + i, 0, rot_rows - 1);
+    const int e1 = interleaved ? 2 * j : j;
+    const int e2 = interleaved ? 2 * j + 1 : j + half;
+    const int64_t s0 = ((int64_t(b) * S + i) * Hkv + g) * D;
+    typename T::bits a = src[s0 + e1], c = src[s0 + e2];
+    rotate_pair<T>(a, c, cosv[int64_t(pos) * half + j], sinv[int64_t(pos) * half + j]);
+    const int row = dest_base(lens, b, S, M, evicted != 0) + i;
+    const int64_t d0 = ((int64_t(b) * Hkv + g) * M + row) * D;
+    dst[d0 + e1] = a;
+    dst[d0 + e2] = c;
+  }
+}
+
+int grid_for(int64_t total) {
+  int64_t blocks = (total + 255) / 256;
+  const int64_t cap = 256 * 64;  // enough workgroups to fill the chip many times
+  return int(blocks < 1 ? 1 : (blocks > cap ? cap : blocks));
+}
+
+hipError_t copy_rows(const void* src, void* dst, const Problem& p, bool evicted,
+                     hipStream_t st) {
+  const int row_bytes = p.D * (p.dtype == GQA_FP32 ? 4 : 2);
+  const int64_t rows = int64_t(p.B) * p.S * p.Hkv;
+  if (row_bytes % 16 == 0) {
+    const int upr = row_bytes / 16;
+    hipLaunchKernelGGL(copy_rows_kernel<uint4>, dim3(grid_for(rows * upr)), dim3(256), 0, st,
+                       static_cast<const uint4*>(src), static_cast<uint4*>(dst), p.lens_dev,
+                       p.B, p.S, p.Hkv, p.M, upr, int(evicted));
+  } else if (row_bytes % 4 == 0) {
+    const int upr = row_bytes / 4;
+    hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, dim3(grid_for(rows * upr)), dim3(256), 0,
+                       st, static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst),
+                       p.lens_dev, p.B, p.S, p.Hkv, p.M, upr, int(evicted));
+  } else {
+    const int upr = row_bytes / 2;
+    hipLaunchKernelGGL(copy_rows_kernel<uint16_t>, dim3(grid_for(rows * upr)), dim3(256), 0,
+                       st, static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
+                       p.lens_dev, p.B, p.S, p.Hkv, p.M, upr, int(evicted));
+  }
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t rotary_rows(const Problem& p, bool evicted, hipStream_t st) {
+  const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 2);
+  using Bits = typename T::bits;
+  hipLaunchKernelGGL(rotary_rows_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
+                     static_cast<const Bits*>(p.k_new), static_cast<Bits*>(p.k_cache),
+                     p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,
+                     p.interleaved, int(evicted));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const Problem& p, bool evicted, hipStream_t st) {
+  if (p.B == 0 || p.S == 0) return hipSuccess;
+  hipError_t e;
+  if (p.rot) {
+    if (p.dtype == GQA_FP32) e = rotary_rows<F32>(p, evicted, st);
+    else if (p.dtype == GQA_FP16) e = rotary_rows<F16>(p, evicted, st);
+    else e = rotary_rows<BF16>(p, evicted, st);
+  } else {
+    e = copy_rows(p.k_new, p.k_cache, p, evicted, st);
+  }
+  if (e != hipSuccess) return e;
+  return copy_rows(p.v_new, p.v_cache, p, evicted, st);
+}
+
+}  // namespace gqa

@@ -1,0 +1,167 @@
+// Window eviction: for every (b, kv head) with L_b + incoming > M, drop the
+// oldest d_b = L_b + incoming - M rows and move rows [d_b, L_b) to
+// [0, L_b - d_b), in place, for K and V. The buffer must stay where it is, so
+// this is a memmove towards lower rows.
+//
+// Parallel form (d <= kEvictHaloMax): the destination range is cut into
+// chunks of C rows, one workgroup each. Chunk k reads source rows
+// [kC + d, (k+1)C + d); the last d of those are the first d rows chunk k+1
+// overwrites. A first kernel copies those "halo" rows of every chunk to the
+// workspace; the second kernel then loads each chunk's sources (own rows from
+// the cache, halo rows from the workspace), waits at a workgroup barrier so
+// every read of the chunk has returned, and stores the shifted rows. No
+// workgroup ever reads a row another workgroup writes in the same kernel.
+//
+// Serial form (larger d): one workgroup per (b, kv head, K|V) walks the rows
+// upwards in blocks; a block's sources lie at or above every row written so
+// far, and each block's loads finish (barrier) before its stores.
+#include "gqa_device.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+struct EvictArgs {
+  char* k_cache;
+  char* v_cache;
+  char* halo;          // workspace scratch
+  const int32_t* lens;
+  int B, Hkv, M, incoming;
+  int upr;             // units per row
+  int chunk_rows;      // C
+  int nchunks;         // ceil(M / C): halo slot stride
+};
+
+// (b, kv head, K|V) of this workgroup: y = g * 2 + kv, z = b.
+template <class U>
+__device__ inline U* cache_rows(const EvictArgs& a, int b, int y) {
+  const int g = y >> 1;
+  char* base = (y & 1) ? a.v_cache : a.k_cache;
+  return reinterpret_cast<U*>(base) + (int64_t(b) * a.Hkv + g) * a.M * int64_t(a.upr);
+}
+
+template <class U>
+__device__ inline U* halo_rows(const EvictArgs& a, int b, int y, int k) {
+  return reinterpret_cast<U*>(a.halo) +
+         (((int64_t(b) * a.Hkv * 2 + y) * a.nchunks + k) * kEvictHaloMax) * int64_t(a.upr);
+}
+
+__device__ inline int drop_of(const EvictArgs& a, int b, int* Lout) {
+  const int L = clamp_len(a.lens[b], 0, a.M);
+  *Lout = L;
+  const int d = L + a.incoming - a.M;
+  return d > 0 ? (d < L ? d : L) : 0;
+}
+
+template <class U>
+__global__ void __launch_bounds__(kEvictThreads) halo_kernel(EvictArgs a) {
+  const int k = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
+  int L;
+  const int d = drop_of(a, b, &L);
+  if (d == 0 || d > kEvictHaloMax) return;
+  const int C = a.chunk_rows, keep = L - d;
+  if ((k + 1) * C >= keep) return;  // chunk k + 1 does not exist: nobody overwrites
+  const U* src = cache_rows<U>(a, b, y) + int64_t(k + 1) * C * a.upr;
+  U* dst = halo_rows<U>(a, b, y, k);
+  for (int u = threadIdx.x; u < d * a.upr; u += blockDim.x) dst[u] = src[u];
+}
+
+template <class U>
+__global__ void __launch_bounds__(kEvictThreads) shift_kernel(EvictArgs a) {
+  const int k = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
+  int L;
+  const int d = drop_of(a, b, &L);
+  if (d == 0 || d > kEvictHaloMax) return;
+  const int C = a.chunk_rows, keep = L - d;
+  const int row0 = k * C;
+  if (row0 >= keep) return;
+  const int rows = (keep - row0) < C ? (keep - row0) : C;
+  const bool next_exists = row0 + C < keep;
+  U* rowsp = cache_rows<U>(a, b, y);
+  const U* halo = halo_rows<U>(a, b, y, k);
+  const int units = rows * a.upr;
+  U v[kEvictUnitsPerThread];
+#pragma unroll
+  for (int n = 0; n < kEvictUnitsPerThread; ++n) {
+    const int u = threadIdx.x + n * kEvictThreads;
+    if (u < units) {
+      const int r = u / a.upr, c = u - r * a.upr;
+      const int src = row0 + r + d;
+      v[n] = (next_exists && src >= row0 + C) ? halo[int64_t(src - row0 - C) * a.upr + c]
+                                               : rowsp[int64_t(src) * a.upr + c];
+    }
+  }
+  __syncthreads();  // every source of this chunk has been read
+#pragma unroll
+  for (int n = 0; n < kEvictUnitsPerThread; ++n) {
+    const int u = threadIdx.x + n * kEvictThreads;
+    if (u < units) rowsp[int64_t(row0) * a.upr + u] = v[n];
+  }
+}
+
+template <class U>
+__global__ void __launch_bounds__(kEvictThreads) serial_kernel(EvictArgs a) {
+  const int y = blockIdx.x, b = blockIdx.y;
+  int L;
+  const int d = drop_of(a, b, &L);
+  if (d == 0) return;
+  const int keep = L - d;
+  U* rowsp = cache_rows<U>(a, b, y);
+  const int per_block = kEvictThreads * kEvictUnitsPerThread;  // units per pass
+  const int64_t total = int64_t(keep) * a.upr;
+  const int64_t shift = int64_t(d) * a.upr;
+  for (int64_t base = 0; base < total; base += per_block) {
+    U v[kEvictUnitsPerThread];
+#pragma unroll
+    for (int n = 0; n < kEvictUnitsPerThread; ++n) {
+      const int64_t u = base + threadIdx.x + n * kEvictThreads;
+      if (u < total) v[n] = rowsp[u + shift];
+    }
+    __syncthreads();  // this pass's sources are all read before any store
+#pragma unroll
+    for (int n = 0; n < kEvictUnitsPerThread; ++n) {
+      const int64_t u = base + threadIdx.x + n * kEvictThreads;
+      if (u < total) rowsp[u] = v[n];
+    }
+  }
+}
+
+template <class U>
+hipError_t run(const EvictArgs& a, int max_drop, hipStream_t st) {
+  if (max_drop <= kEvictHaloMax) {
+    const dim3 grid(a.nchunks, a.Hkv * 2, a.B);
+    if (a.nchunks > 1) {
+      hipLaunchKernelGGL(halo_kernel<U>, dim3(a.nchunks - 1, a.Hkv * 2, a.B),
+                         dim3(kEvictThreads), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(shift_kernel<U>, grid, dim3(kEvictThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(serial_kernel<U>, dim3(a.Hkv * 2, a.B), dim3(kEvictThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_evict(const Problem& p, int incoming, int max_drop, void* ws,
+                        const WorkspaceLayout& lay, hipStream_t st) {
+  if (p.B == 0 || max_drop <= 0) return hipSuccess;
+  const int row_bytes = p.D * (p.dtype == GQA_FP32 ? 4 : 2);
+  const EvictGeometry eg = evict_geometry(row_bytes);
+  EvictArgs a;
+  a.k_cache = static_cast<char*>(p.k_cache);
+  a.v_cache = static_cast<char*>(p.v_cache);
+  a.halo = static_cast<char*>(ws) + lay.scratch;
+  a.lens = p.lens_dev;
+  a.B = p.B; a.Hkv = p.Hkv; a.M = p.M; a.incoming = incoming;
+  a.upr = row_bytes / eg.unit;
+  a.chunk_rows = eg.chunk_rows;
+  a.nchunks = ceil_div(p.M, eg.chunk_rows);
+  if (eg.unit == 16) return run<uint4>(a, max_drop, st);
+  if (eg.unit == 4) return run<uint32_t>(a, max_drop, st);
+  return run<uint16_t>(a, max_drop, st);
+}
+
+}  // namespace gqa

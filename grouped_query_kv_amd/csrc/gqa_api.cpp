@@ -1,0 +1,298 @@
+// Host side of the C ABI: argument validation (complete before any launch),
+// workspace carving and kernel dispatch. See include/gqa.h for the contract.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+thread_local char g_err[512] = "";
+
+gqa_status fail(gqa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gqa_status hip_fail(hipError_t e, const char* where) {
+  return fail(GQA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int elem_bytes(int dtype) { return dtype == GQA_FP32 ? 4 : 2; }
+
+enum Entry { kAppend, kPrefill, kDecode };
+
+// Shape checks shared by every entry point.
+gqa_status check_shape(const gqa_shape* s, bool need_heads) {
+  if (!s) return fail(GQA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->dtype != GQA_FP32 && s->dtype != GQA_FP16 && s->dtype != GQA_BF16)
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
+  if (s->batch < 0) return fail(GQA_ERR_INVALID_ARG, "batch %d < 0", s->batch);
+  if (s->kv_num_heads < 1) return fail(GQA_ERR_INVALID_ARG, "kv_num_heads %d < 1", s->kv_num_heads);
+  if (need_heads) {
+    if (s->num_heads < 1) return fail(GQA_ERR_INVALID_ARG, "num_heads %d < 1", s->num_heads);
+    if (s->num_heads % s->kv_num_heads)
+      return fail(GQA_ERR_INVALID_ARG, "num_heads %d not a multiple of kv_num_heads %d",
+                  s->num_heads, s->kv_num_heads);
+  }
+  if (s->head_size < 1 || s->head_size > 256)
+    return fail(GQA_ERR_INVALID_ARG, "head_size %d outside 1..256", s->head_size);
+  if (s->max_seq_len < 1) return fail(GQA_ERR_INVALID_ARG, "max_seq_len %d < 1", s->max_seq_len);
+  return GQA_OK;
+}
+
+gqa_status check_lengths(const gqa_shape* s, const int32_t* host, const int32_t* dev) {
+  if (s->batch == 0) return GQA_OK;
+  if (!host) return fail(GQA_ERR_INVALID_ARG, "seqlens_k_host is NULL");
+  if (!dev) return fail(GQA_ERR_INVALID_ARG, "seqlens_k_dev is NULL");
+  for (int b = 0; b < s->batch; ++b)
+    if (host[b] < 0 || host[b] > s->max_seq_len)
+      return fail(GQA_ERR_INVALID_ARG, "seqlens_k[%d] = %d outside 0..%d", b, host[b],
+                  s->max_seq_len);
+  return GQA_OK;
+}
+
+// Full validation of an append / attention call; fills `p` on success.
+gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const void* q,
+                    const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* lens_host, const int32_t* lens_dev, void* out,
+                    Problem* p, bool* needs_evict, int* max_drop) {
+  gqa_status st = check_shape(s, true);
+  if (st != GQA_OK) return st;
+  if (!o) return fail(GQA_ERR_INVALID_ARG, "options is NULL");
+  const int B = s->batch, S = s->new_tokens, D = s->head_size, M = s->max_seq_len;
+  if (S < 0) return fail(GQA_ERR_INVALID_ARG, "new_tokens %d < 0", S);
+  if (entry != kAppend && S < 1) return fail(GQA_ERR_INVALID_ARG, "new_tokens must be >= 1");
+  if (entry == kDecode && S != 1) return fail(GQA_ERR_INVALID_ARG, "decode needs new_tokens == 1");
+  const int W = o->local_window_size;
+  if (!(W == -1 || (W >= 1 && W <= M)))
+    return fail(GQA_ERR_INVALID_ARG, "local_window_size %d not -1 or 1..%d", W, M);
+  if (!isfinite(o->scale)) return fail(GQA_ERR_INVALID_ARG, "scale is not finite");
+  st = check_lengths(s, lens_host, lens_dev);
+  if (st != GQA_OK) return st;
+  const bool rot = o->cos_cache != nullptr || o->sin_cache != nullptr;
+  int maxlen = 0;
+  for (int b = 0; b < B; ++b) maxlen = std::max(maxlen, lens_host[b]);
+  if (rot) {
+    if (!o->cos_cache || !o->sin_cache)
+      return fail(GQA_ERR_INVALID_ARG, "cos_cache and sin_cache must be given together");
+    if (D % 2) return fail(GQA_ERR_INVALID_ARG, "rotary needs an even head_size (got %d)", D);
+    if (B > 0 && S > 0 && (int64_t)maxlen + S > (int64_t)o->rotary_rows)
+      return fail(GQA_ERR_INVALID_ARG, "rotary table has %d rows, positions reach %d",
+                  o->rotary_rows, maxlen + S - 1);
+  }
+  const bool work = B > 0 && S > 0;
+  if (work) {
+    if (!k_new || !v_new || !k_cache || !v_cache)
+      return fail(GQA_ERR_INVALID_ARG, "a K/V pointer is NULL");
+    if (entry != kAppend && (!q || !out)) return fail(GQA_ERR_INVALID_ARG, "q or out is NULL");
+  }
+  const bool windowed = W > 0 && entry != kAppend;
+  *needs_evict = false;
+  *max_drop = 0;
+  if (windowed) {
+    if (S > M) return fail(GQA_ERR_INVALID_ARG, "new_tokens %d > max_seq_len %d", S, M);
+    for (int b = 0; b < B; ++b) *max_drop = std::max(*max_drop, lens_host[b] + S - M);
+    *needs_evict = *max_drop > 0;
+  } else {
+    for (int b = 0; b < B; ++b)
+      if (lens_host[b] + S > M)
+        return fail(GQA_ERR_NO_ROOM, "sequence %d: %d past + %d new > max_seq_len %d", b,
+                    lens_host[b], S, M);
+  }
+  if (*needs_evict && S > 1)
+    return fail(GQA_ERR_UNSUPPORTED,
+                "window eviction with more than one new token is not implemented");
+  Problem& P = *p;
+  P.B = B; P.S = S; P.H = s->num_heads; P.Hkv = s->kv_num_heads; P.G = P.H / P.Hkv;
+  P.D = D; P.M = M; P.dtype = s->dtype; P.window = W;
+  P.scale = o->scale != 0.0f ? o->scale : 1.0f / sqrtf((float)D);
+  P.rot = rot; P.cos = o->cos_cache; P.sin = o->sin_cache; P.rot_rows = o->rotary_rows;
+  P.interleaved = o->rotary_interleaved != 0;
+  P.q = q; P.k_new = k_new; P.v_new = v_new; P.k_cache = k_cache; P.v_cache = v_cache;
+  P.out = out; P.lens_dev = lens_dev; P.lens_host = lens_host;
+  return GQA_OK;
+}
+
+gqa_status check_workspace(const gqa_shape* s, void* ws, size_t bytes, WorkspaceLayout* lay) {
+  *lay = workspace_layout(*s);
+  if (lay->total == 0) return GQA_OK;
+  if (!ws) return fail(GQA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", lay->total);
+  if (bytes < lay->total)
+    return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, lay->total);
+  return GQA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The whole op for one call. S == 1 takes the split-KV decode route.
+gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options* opts,
+                         const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* lens_host, const int32_t* lens_dev,
+                         void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = '\0';
+  Problem P;
+  bool needs_evict;
+  int max_drop;
+  gqa_status st = validate(entry, shape, opts, q, k_new, v_new, k_cache, v_cache, lens_host,
+                           lens_dev, out, &P, &needs_evict, &max_drop);
+  if (st != GQA_OK) return st;
+  WorkspaceLayout lay;
+  st = check_workspace(shape, ws, ws_bytes, &lay);
+  if (st != GQA_OK) return st;
+  if (P.B == 0) return GQA_OK;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (needs_evict) {
+    e = launch_evict(P, P.S, max_drop, ws, lay, hs);
+    if (e != hipSuccess) return hip_fail(e, "eviction");
+  }
+  const bool evicted_lengths = P.window > 0;
+  if (P.S == 1 && decode_fast_supported(P)) {
+    e = launch_decode_fast(P, ws, lay, hs);
+    if (e != hipSuccess) return hip_fail(e, "decode");
+    return GQA_OK;
+  }
+  e = launch_append(P, evicted_lengths, hs);
+  if (e != hipSuccess) return hip_fail(e, "append");
+  if (prefill_fast_supported(P)) {
+    e = launch_prefill_fast(P, hs);
+    if (e != hipSuccess) return hip_fail(e, "prefill");
+  } else {
+    e = launch_attention_simple(P, hs);
+    if (e != hipSuccess) return hip_fail(e, "attention");
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(const gqa_shape& s) {
+  WorkspaceLayout l{};
+  const int64_t B = s.batch, H = s.num_heads, Hkv = s.kv_num_heads, D = s.head_size;
+  const int64_t M = s.max_seq_len;
+  if (B <= 0 || Hkv <= 0 || D <= 0 || M <= 0) return l;
+  const int64_t G = H > 0 && H % Hkv == 0 ? H / Hkv : 1;
+  // decode merge counters, one per (b, kv head, head group)
+  const int64_t hg = (G + kDecodeMaxHG - 1) / kDecodeMaxHG;
+  l.counters = 0;
+  l.counters_bytes = align256(size_t(B * Hkv * hg) * sizeof(int32_t));
+  // decode partials: [B, Hkv, hg, splits, HG_max, D + 2] fp32
+  int64_t partial = 0;
+  if (D == 128 && s.dtype != GQA_FP32) {
+    const int64_t splits = (M + kDecodeMinChunk - 1) / kDecodeMinChunk;
+    partial = B * Hkv * hg * splits * kDecodeMaxHG * (D + 2) * 4;
+  }
+  // eviction halos: [B, Hkv, 2, chunks, halo rows, row bytes]
+  const int64_t row_bytes = D * (s.dtype == GQA_FP32 ? 4 : 2);
+  const EvictGeometry eg = evict_geometry((int)row_bytes);
+  const int64_t chunks = (M + eg.chunk_rows - 1) / eg.chunk_rows;
+  const int64_t halo = B * Hkv * 2 * chunks * kEvictHaloMax * row_bytes;
+  l.scratch = l.counters_bytes;
+  l.scratch_bytes = align256(size_t(std::max(partial, halo)));
+  l.total = l.scratch + l.scratch_bytes;
+  return l;
+}
+
+}  // namespace gqa
+
+using namespace gqa;
+
+extern "C" {
+
+size_t gqa_workspace_bytes(const gqa_shape* shape) {
+  if (!shape) return 0;
+  return workspace_layout(*shape).total;
+}
+
+gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts, const void* k_new,
+                         const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* seqlens_k_host, const int32_t* seqlens_k_dev,
+                         void* stream) {
+  g_err[0] = '\0';
+  Problem P;
+  bool needs_evict;
+  int max_drop;
+  gqa_status st = validate(kAppend, shape, opts, nullptr, k_new, v_new, k_cache, v_cache,
+                           seqlens_k_host, seqlens_k_dev, nullptr, &P, &needs_evict, &max_drop);
+  if (st != GQA_OK) return st;
+  if (P.B == 0 || P.S == 0) return GQA_OK;
+  hipError_t e = launch_append(P, false, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append");
+  return GQA_OK;
+}
+
+gqa_status gqa_attention_prefill(const gqa_shape* shape, const gqa_options* opts, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const int32_t* seqlens_k_host,
+                                 const int32_t* seqlens_k_dev, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return run_attention(kPrefill, shape, opts, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
+                       seqlens_k_dev, out, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_attention_decode(const gqa_shape* shape, const gqa_options* opts, const void* q,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const int32_t* seqlens_k_host,
+                                const int32_t* seqlens_k_dev, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return run_attention(kDecode, shape, opts, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
+                       seqlens_k_dev, out, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming, void* k_cache,
+                            void* v_cache, const int32_t* seqlens_k_host,
+                            const int32_t* seqlens_k_dev, int32_t* seqlens_after_host,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  gqa_status st = check_shape(shape, false);
+  if (st != GQA_OK) return st;
+  const int B = shape->batch, M = shape->max_seq_len;
+  if (incoming < 0 || incoming > M)
+    return fail(GQA_ERR_INVALID_ARG, "incoming %d outside 0..%d", incoming, M);
+  st = check_lengths(shape, seqlens_k_host, seqlens_k_dev);
+  if (st != GQA_OK) return st;
+  if (B > 0 && !seqlens_after_host) return fail(GQA_ERR_INVALID_ARG, "seqlens_after_host is NULL");
+  int max_drop = 0;
+  for (int b = 0; b < B; ++b) max_drop = std::max(max_drop, seqlens_k_host[b] + incoming - M);
+  if (max_drop > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "cache is NULL");
+  WorkspaceLayout lay;
+  st = check_workspace(shape, workspace, workspace_bytes, &lay);
+  if (st != GQA_OK) return st;
+  if (max_drop > 0) {
+    Problem P{};
+    P.B = B; P.S = incoming; P.H = shape->kv_num_heads; P.Hkv = shape->kv_num_heads; P.G = 1;
+    P.D = shape->head_size; P.M = M; P.dtype = shape->dtype; P.window = M;
+    P.k_cache = k_cache; P.v_cache = v_cache; P.lens_dev = seqlens_k_dev;
+    P.lens_host = seqlens_k_host;
+    hipError_t e = launch_evict(P, incoming, max_drop, workspace, lay,
+                                reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "eviction");
+  }
+  for (int b = 0; b < B; ++b) seqlens_after_host[b] = std::min(seqlens_k_host[b], M - incoming);
+  return GQA_OK;
+}
+
+const char* gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NO_ROOM: return "no room to append: past + new exceeds max_seq_len";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* gqa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal interface between the validating host layer (gqa_api.cpp) and the
+// kernel launchers (*.hip). Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gqa.h"
+
+namespace gqa {
+
+// Everything a launcher needs, already validated against the host lengths.
+struct Problem {
+  int B, S, H, Hkv, G, D, M;
+  int dtype;              // gqa_dtype
+  int window;             // -1 off, else 1..M
+  float scale;            // resolved (never 0)
+  // rotary (rot == 0: none)
+  int rot;
+  const float* cos;
+  const float* sin;
+  int rot_rows;
+  int interleaved;
+  // tensors
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* out;
+  const int32_t* lens_dev;
+  const int32_t* lens_host;
+};
+
+// Workspace carving (byte offsets from the workspace base). The layout is a
+// function of the shape only, so one allocation serves every call.
+struct WorkspaceLayout {
+  size_t counters;        // int32 [B, Hkv, hg_max] merge counters (kept zero)
+  size_t counters_bytes;
+  size_t scratch;         // shared by decode partials and eviction halos
+  size_t scratch_bytes;
+  size_t total;
+};
+
+// Decode: fast split-KV kernel limits.
+constexpr int kDecodeBlockKeys = 64;     // keys per wave iteration
+constexpr int kDecodeWaves = 4;          // waves per workgroup
+constexpr int kDecodeMaxHG = 8;          // query heads per workgroup (MFMA N padded to 16)
+constexpr int kDecodeMinChunk = 64;      // smallest split, bounds the partial slots
+
+// Eviction: rows per workgroup chunk is chosen so a chunk is 64 KiB; halo
+// copies are used up to this many dropped rows.
+constexpr int kEvictHaloMax = 32;
+constexpr int kEvictThreads = 256;
+constexpr int kEvictUnitsPerThread = 16;
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Eviction copy unit and rows per workgroup chunk for a row of `row_bytes`.
+struct EvictGeometry {
+  int unit;        // bytes moved per access: 16, 4 or 2
+  int chunk_rows;  // rows per workgroup chunk (>= 1)
+};
+inline EvictGeometry evict_geometry(int row_bytes) {
+  EvictGeometry g;
+  g.unit = (row_bytes % 16 == 0) ? 16 : ((row_bytes % 4 == 0) ? 4 : 2);
+  const int chunk_bytes = kEvictThreads * kEvictUnitsPerThread * g.unit;
+  g.chunk_rows = chunk_bytes / row_bytes > 0 ? chunk_bytes / row_bytes : 1;
+  return g;
+}
+
+WorkspaceLayout workspace_layout(const gqa_shape& s);
+
+// Launchers. They assume validated arguments and return the first HIP error.
+hipError_t launch_append(const Problem& p, bool evicted_lengths, hipStream_t st);
+
+// Eviction for `incoming` tokens; max_drop = max_b d_b from the host lengths.
+hipError_t launch_evict(const Problem& p, int incoming, int max_drop, void* ws,
+                        const WorkspaceLayout& lay, hipStream_t st);
+
+// Plain attention (any dtype, D <= 256): reads keys from the cache, which
+// must already hold this call's appended rows.
+hipError_t launch_attention_simple(const Problem& p, hipStream_t st);
+
+// Fast decode (fp16/bf16, D == 128, S == 1): fused append + split-KV + merge.
+bool decode_fast_supported(const Problem& p);
+hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
+                              hipStream_t st);
+
+// Fast prefill (fp16/bf16, D == 128): MFMA flash attention over the cache.
+bool prefill_fast_supported(const Problem& p);
+hipError_t launch_prefill_fast(const Problem& p, hipStream_t st);
+
+}  // namespace gqa

@@ -1,0 +1,188 @@
+/*
+ * gqa.h - GroupQueryAttention over a shared-buffer KV cache, for gfx950.
+ *
+ * The operation (from the pages, by title and section):
+ *  - "Clarification about GroupQueryAttention behavior" (onnxruntime
+ *    discussion), question: past_key and present_key may be one tensor in
+ *    BNSH layout [batch, kv_num_heads, max_sequence_length, head_size];
+ *    answer: a runtime check that both point to the same address, and the
+ *    operator fails when there is no room to append; sliding-window
+ *    follow-up: the op keeps the min(total, capacity) most recent tokens,
+ *    contiguously.
+ *  - "[TorchOnnxToTorch] Add pad+scatter KV cache and mask to GQA"
+ *    (torch-mlir pull request), paragraph 1: Q/K/V arrive as
+ *    [batch, seq, heads*head_size]; rotary positions are past_len + arange;
+ *    K is rotated with kv_num_heads; seqlens_k is 0 for an empty past; the
+ *    output is [batch, seq, hidden]. Paragraph 2: new K/V are scattered at
+ *    the seqlens_k positions of the buffer; causal visibility is
+ *    k_pos <= past_len + q_pos; seqlens_k is int32.
+ *  - "KV Cache" (rocMLIR discussion), worked example and notes: per head
+ *    softmax(Q K^T) V where the key axis grows inside a max_seq_len buffer
+ *    and the key-tile loop ends at the current length instead of masking
+ *    the whole buffer.
+ *
+ * Notation: B batch, S new tokens per sequence, H num_heads, Hkv
+ * kv_num_heads (H % Hkv == 0, G = H / Hkv, query head h reads KV head
+ * h / G), D head_size, M max_seq_len (= buffer length = window capacity),
+ * L_b = seqlens_k[b] = tokens already valid in sequence b's buffer rows.
+ *
+ * Layouts (all row-major, contiguous, element type = shape->dtype):
+ *   q      [B, S, H*D]          k_new, v_new [B, S, Hkv*D]
+ *   out    [B, S, H*D]          k_cache, v_cache [B, Hkv, M, D] (BNSH)
+ *   cos_cache, sin_cache: fp32 [rotary_rows, D/2]
+ *
+ * Semantics of one attention call (prefill or decode):
+ *   1. rotary (if cos/sin given) on Q (H heads) and K (Hkv heads) at
+ *      positions L_b + i; pairs (j, j + D/2), or (2j, 2j+1) when
+ *      rotary_interleaved; each rotated value is the fp64 expression
+ *      x1*c - x2*s (resp. x2*c + x1*s) rounded to fp32 then to dtype,
+ *      both nearest-even (exact products, so the cache is reproducible
+ *      bit for bit);
+ *   2. window eviction (only when local_window_size > 0 and L_b + S > M):
+ *      rows [d, L_b) move to [0, L_b - d) with d = L_b + S - M;
+ *   3. append: cache[b, g, L'_b + i, :] = K/V row (b, i, g); no other byte
+ *      of either cache is written;
+ *   4. attention: query i of head h at position p = L'_b + i sees key j iff
+ *      j <= p and (window off or j >= p - W + 1); out = softmax(scale *
+ *      q k^T) v with fp32 accumulation; bytes of the cache past L'_b + S are
+ *      never read.
+ *
+ * Ownership and threading: every pointer except *_host arguments is device
+ * memory owned by the caller. The library never allocates, frees or
+ * synchronises; all work is enqueued on `stream` (a hipStream_t, NULL =
+ * the null stream) and the call returns before it completes. The library
+ * keeps no state between calls except the error-message buffer, which is
+ * thread-local.
+ *
+ * Errors: every argument is validated before the first launch, so any
+ * status other than GQA_OK and GQA_ERR_HIP guarantees that nothing was
+ * enqueued and both caches are untouched. GQA_ERR_HIP means a launch
+ * failed; cache contents are then undefined and the workspace must be
+ * zero-filled again before reuse. gqa_last_error() returns a message for
+ * the most recent failing call on this thread.
+ *
+ * seqlens_k_host and seqlens_k_dev must hold the same values (the host copy
+ * validates and sizes the launch; kernels read the device copy). If they
+ * differ the results are undefined, but every access stays inside the
+ * buffers whose sizes the shape implies.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NO_ROOM = 1,      /* some L_b + S > M with the window off */
+  GQA_ERR_INVALID_ARG = 2,  /* bad shape, option, pointer or length */
+  GQA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (see below) */
+  GQA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than needed */
+  GQA_ERR_HIP = 5           /* a HIP launch failed */
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_FP32 = 0, GQA_FP16 = 1, GQA_BF16 = 2 } gqa_dtype;
+
+typedef struct gqa_shape {
+  int32_t batch;         /* B >= 0 (0: nothing to do) */
+  int32_t new_tokens;    /* S >= 1 for attention, >= 0 for append */
+  int32_t num_heads;     /* H >= 1 */
+  int32_t kv_num_heads;  /* Hkv >= 1, H % Hkv == 0 */
+  int32_t head_size;     /* 1 <= D <= 256 (even with rotary) */
+  int32_t max_seq_len;   /* M >= 1: buffer rows per (b, kv head) */
+  int32_t dtype;         /* gqa_dtype */
+} gqa_shape;
+
+typedef struct gqa_options {
+  float scale;                 /* 0 -> 1/sqrt(D); otherwise finite */
+  int32_t local_window_size;   /* -1: off; otherwise 1 <= W <= M */
+  const float* cos_cache;      /* NULL: no rotary; else [rotary_rows, D/2] */
+  const float* sin_cache;      /* given together with cos_cache */
+  int32_t rotary_rows;         /* rows in the tables; need L_b + S <= rows */
+  int32_t rotary_interleaved;  /* 0: rotate-half pairs; 1: adjacent pairs */
+} gqa_options;
+
+/*
+ * Bytes of workspace the attention and eviction entry points need for this
+ * shape, for any seqlens_k (an upper bound over all lengths 0..M). The
+ * workspace must be zero-filled before its first use; each successful call
+ * leaves it reusable (its counters return to zero). 0 means none is needed.
+ */
+size_t gqa_workspace_bytes(const gqa_shape* shape);
+
+/*
+ * Append half (steps 1 and 3 for K/V only): rotary on k_new when tables are
+ * given, then the in-place scatter at L_b. No eviction: any L_b + S > M
+ * returns GQA_ERR_NO_ROOM, window or not. opts->scale and the window are
+ * ignored. Source: pad+scatter pull request, paragraph 2; shared-buffer
+ * question and answer of the GroupQueryAttention clarification.
+ */
+gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts,
+                         const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache,
+                         const int32_t* seqlens_k_host, const int32_t* seqlens_k_dev,
+                         void* stream);
+
+/*
+ * The whole op for S >= 1 new tokens per sequence (steps 1-4): fused
+ * flash-style attention on MFMA for fp16/bf16 with D = 128, a plain
+ * kernel otherwise. With a window, S > 1 and an eviction needed by some
+ * sequence, returns GQA_ERR_UNSUPPORTED (attention would need the
+ * pre-eviction keys). Source: all three pages as summarised above; the
+ * key-tile loop ends at each sequence's length ("KV Cache", notes and
+ * short-term plan).
+ */
+gqa_status gqa_attention_prefill(const gqa_shape* shape, const gqa_options* opts,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache,
+                                 const int32_t* seqlens_k_host, const int32_t* seqlens_k_dev,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * The whole op for exactly one new token per sequence (S must be 1):
+ * split-KV attention in which each workgroup streams one slice of a
+ * sequence's valid keys once and the last workgroup of the sequence merges
+ * the slices by log-sum-exp. With a window and L_b = M it evicts one row
+ * first instead of failing. Source: as for prefill; decoding phase of the
+ * "KV Cache" worked example.
+ */
+gqa_status gqa_attention_decode(const gqa_shape* shape, const gqa_options* opts,
+                                const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache,
+                                const int32_t* seqlens_k_host, const int32_t* seqlens_k_dev,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Eviction half (step 2 alone): make room for `incoming` tokens
+ * (0 <= incoming <= M) in every sequence by dropping its oldest
+ * d_b = max(0, L_b + incoming - M) rows and shifting the rest to row 0, in
+ * place. Writes seqlens_after_host[b] = min(L_b, M - incoming) (host
+ * memory, B entries) before returning; updating the device copy of the
+ * lengths is the caller's job. Uses shape->batch, kv_num_heads, head_size,
+ * max_seq_len and dtype only. Source: sliding-window follow-up of the
+ * GroupQueryAttention clarification (keep the most recent tokens,
+ * contiguously; each step's eviction costs a copy of the cache).
+ */
+gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming,
+                            void* k_cache, void* v_cache,
+                            const int32_t* seqlens_k_host, const int32_t* seqlens_k_dev,
+                            int32_t* seqlens_after_host,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gqa_status_string(gqa_status status);
+
+/* Message for the most recent failing call on this thread ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

@@ -1,0 +1,187 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol
+the header declares, and validation rejects bad calls before any launch.
+
+Every call here fails validation, so no device memory is ever touched (the
+"device" pointers are dummies). The expected status of each case follows the
+oracle's validation rules where the oracle has one.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gqa_inputs as gi
+from oracle import gqa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000   # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def g():
+    import grouped_query_kv_amd as gqa
+    return gqa
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "gqa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(gqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(g):
+    names = declared_functions()
+    assert set(names) == {"gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill",
+                          "gqa_attention_decode", "gqa_evict_window", "gqa_status_string",
+                          "gqa_last_error"}
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(g):
+    for code in range(6):
+        assert g.lib.gqa_status_string(code)
+    assert b"no room" in g.lib.gqa_status_string(g.GQA_ERR_NO_ROOM)
+
+
+def _shape(g, B=2, S=3, H=4, Hkv=2, D=8, M=16, dtype=0):
+    return g.Shape(B, S, H, Hkv, D, M, dtype)
+
+
+def _call(g, entry, shape, opts=None, lens=(0, 0), ws_bytes=1 << 30, ws=FAKE, incoming=1):
+    opts = opts or g.Options(0.0, -1, None, None, 0, 0)
+    hl = np.asarray(lens, np.int32)
+    hp = hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    if entry == "append":
+        return g.lib.gqa_append_kv(ctypes.byref(shape), ctypes.byref(opts), FAKE, FAKE, FAKE, FAKE,
+                                   hp, FAKE, None)
+    if entry == "evict":
+        after = np.zeros(max(1, len(lens)), np.int32)
+        return g.lib.gqa_evict_window(ctypes.byref(shape), incoming, FAKE, FAKE, hp, FAKE,
+                                      after.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      ws, ws_bytes, None)
+    fn = g.lib.gqa_attention_decode if entry == "decode" else g.lib.gqa_attention_prefill
+    return fn(ctypes.byref(shape), ctypes.byref(opts), FAKE, FAKE, FAKE, FAKE, FAKE, hp, FAKE,
+              FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("entry", ["append", "prefill"])
+def test_no_room_when_past_plus_new_exceeds_buffer(g, entry):
+    st = _call(g, entry, _shape(g, S=3, M=16), lens=(13, 14))
+    assert st == g.GQA_ERR_NO_ROOM
+    assert b"sequence 1" in g.lib.gqa_last_error()
+
+
+def test_no_room_in_decode_without_window(g):
+    st = _call(g, "decode", _shape(g, S=1, M=16), lens=(16, 0))
+    assert st == g.GQA_ERR_NO_ROOM
+
+
+def test_no_room_matches_oracle_rule():
+    # the oracle agrees on which of these fit: L + S == M fits, M + 1 does not
+    fits = gi.make_case("x", "fp32", 2, 3, 4, 2, 8, 16, [13, 0], 0)
+    assert O.validate(fits, "prefill") == O.OK
+    over = gi.make_case("x", "fp32", 2, 3, 4, 2, 8, 16, [14, 0], 0)
+    assert O.validate(over, "prefill") == O.NO_ROOM
+
+
+INVALID = [
+    ("prefill", dict(H=3), {}),                         # H % Hkv
+    ("prefill", dict(S=0), {}),
+    ("decode", dict(S=2), {}),
+    ("prefill", dict(D=0), {}),
+    ("prefill", dict(D=257), {}),
+    ("prefill", dict(M=0), {}),
+    ("prefill", dict(dtype=7), {}),
+    ("prefill", dict(B=-1), {}),
+    ("prefill", {}, dict(window=0)),
+    ("prefill", {}, dict(window=17)),
+    ("prefill", {}, dict(lens=(-1, 0))),
+    ("prefill", {}, dict(lens=(17, 0))),
+    ("prefill", {}, dict(scale=float("nan"))),
+    ("prefill", dict(D=7), dict(rotary=True)),          # odd D with rotary
+    ("prefill", {}, dict(rotary=True, rows=4, lens=(2, 0))),   # positions beyond the table
+    ("append", dict(S=-1), {}),
+]
+
+
+@pytest.mark.parametrize("entry,shape_kw,kw", INVALID)
+def test_invalid_arguments(g, entry, shape_kw, kw):
+    shape = _shape(g, **shape_kw)
+    rot = kw.get("rotary", False)
+    opts = g.Options(kw.get("scale", 0.0), kw.get("window", -1), FAKE if rot else None,
+                     FAKE if rot else None, kw.get("rows", 64), 0)
+    st = _call(g, entry, shape, opts, lens=kw.get("lens", (0, 0)))
+    assert st == g.GQA_ERR_INVALID_ARG, g.lib.gqa_last_error()
+    assert g.lib.gqa_last_error()
+
+
+def test_window_with_multi_token_eviction_is_unsupported(g):
+    opts = g.Options(0.0, 16, None, None, 0, 0)
+    st = _call(g, "prefill", _shape(g, S=3, M=16), opts, lens=(15, 0))
+    assert st == g.GQA_ERR_UNSUPPORTED
+
+
+def test_workspace_too_small(g):
+    need = g.lib.gqa_workspace_bytes(ctypes.byref(_shape(g, S=1, D=128, dtype=1)))
+    assert need > 0
+    st = _call(g, "decode", _shape(g, S=1, D=128, dtype=1), lens=(3, 4), ws_bytes=need - 1)
+    assert st == g.GQA_ERR_WORKSPACE
+    st = _call(g, "decode", _shape(g, S=1, D=128, dtype=1), lens=(3, 4), ws=None)
+    assert st == g.GQA_ERR_WORKSPACE
+
+
+def test_workspace_bound_is_independent_of_lengths(g):
+    a = g.gqa_workspace_bytes(16, 1, 32, 8, 128, 4096, g.GQA_FP16)
+    b = g.gqa_workspace_bytes(16, 1, 32, 8, 128, 4096, g.GQA_FP16)
+    assert a == b and a % 256 == 0
+    assert g.gqa_workspace_bytes(0, 1, 32, 8, 128, 4096, g.GQA_FP16) == 0
+
+
+def test_evict_validation(g):
+    sh = _shape(g, S=0, M=16)
+    assert _call(g, "evict", sh, lens=(3, 4), incoming=17) == g.GQA_ERR_INVALID_ARG
+    assert _call(g, "evict", sh, lens=(3, 4), incoming=-1) == g.GQA_ERR_INVALID_ARG
+    assert _call(g, "evict", sh, lens=(3, 20), incoming=1) == g.GQA_ERR_INVALID_ARG
+    assert _call(g, "evict", sh, lens=(16, 4), incoming=2, ws=None) == g.GQA_ERR_WORKSPACE
+
+
+def test_evict_without_drops_is_a_host_only_noop(g):
+    # nothing to drop: returns the new lengths and launches nothing
+    hl = np.array([3, 4], np.int32)
+    after = np.zeros(2, np.int32)
+    st = g.lib.gqa_evict_window(ctypes.byref(_shape(g, S=0, M=16)), 5, FAKE, FAKE,
+                                hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), FAKE,
+                                after.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), FAKE, 1 << 30,
+                                None)
+    assert st == g.GQA_OK and after.tolist() == [3, 4]
+
+
+def test_empty_batch_is_a_noop(g):
+    assert _call(g, "prefill", _shape(g, B=0), lens=()) == g.GQA_OK
+    assert _call(g, "append", _shape(g, B=0), lens=()) == g.GQA_OK
+    assert _call(g, "append", _shape(g, S=0), lens=(1, 2)) == g.GQA_OK
+
+
+def test_binding_rejects_separate_past_and_present(g):
+    torch = pytest.importorskip("torch")
+    kc = torch.zeros(1, 1, 8, 4)
+    vc = torch.zeros(1, 1, 8, 4)
+    other = torch.zeros(1, 1, 8, 4)
+    kn = torch.zeros(1, 1, 4)
+    with pytest.raises(g.GQAError) as e:
+        g.gqa_append_kv(kn, kn, kc, vc, np.zeros(1, np.int32), None, present_key=other, stream=0)
+    assert e.value.status == g.GQA_ERR_INVALID_ARG
+
+
+def test_binding_surfaces_no_room(g):
+    torch = pytest.importorskip("torch")
+    kc = torch.zeros(1, 1, 8, 4)
+    kn = torch.zeros(1, 2, 4)
+    with pytest.raises(g.GQAError) as e:
+        g.gqa_append_kv(kn, kn, kc, kc.clone(), np.array([7], np.int32), kc, stream=0)
+    assert e.value.status == g.GQA_ERR_NO_ROOM

@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Caches must match bit for bit (every byte outside the appended rows included,
+so a stray write or a read of the NaN poison past the length shows up);
+outputs must be finite and within max abs error 1e-4 (fp32) or 2e-2
+(fp16/bf16) of the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gqa_inputs as gi
+from oracle import gqa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_query_kv_amd  # noqa: F401  (fails loudly if the library is missing)
+    return torch
+
+
+from gpu_helpers import (DevCase, assert_bits_equal, assert_close, oracle_sampled,  # noqa: E402
+                         out_f64, to_dev)
+
+
+def check_full(case, entry="prefill", what=""):
+    """Run one call on the GPU and compare everything with the oracle."""
+    say(f"[gpu] {what or case.name}: B={case.batch} S={case.new_tokens} H={case.num_heads} "
+        f"Hkv={case.kv_num_heads} D={case.head_size} M={case.max_seq_len} dt={case.dtype} "
+        f"W={case.local_window_size} rot={case.cos is not None} lens={list(case.seqlens_k)[:8]}")
+    st, want, kc, vc, lens_after = O.gqa_attention(case, entry)
+    assert st == O.OK
+    dev = DevCase(case)
+    out = dev.run(entry)
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, f"{what} k_cache")
+    assert_bits_equal(gv, vc, f"{what} v_cache")
+    err = assert_close(out_f64(out, case.dtype), want, case.dtype, what)
+    say(f"[gpu]   max abs error {err:.3e}")
+    return dev, kc, vc, lens_after, err
+
+
+# --------------------------------------------------------------------------
+# C1: the worked example (prefill 32, then decode to 33)
+# --------------------------------------------------------------------------
+
+def test_c1_prefill_then_decode():
+    c1 = gi.config(1, step=1)
+    dev, kc, vc, lens, _ = check_full(c1, "prefill", "C1 step 1")
+    c2 = gi.config(1, step=2)
+    c2.k_cache, c2.v_cache = kc, vc                 # continue from step 1's cache
+    st, want, kc2, vc2, _ = O.gqa_attention(c2, "decode")
+    d2 = DevCase(c2)
+    d2.k_cache, d2.v_cache = dev.k_cache, dev.v_cache  # same buffer, stays in place
+    ptr = dev.k_cache.data_ptr()
+    out = d2.run("decode")
+    assert dev.k_cache.data_ptr() == ptr
+    gk, gv = d2.caches()
+    assert_bits_equal(gk, kc2, "C1 step 2 k_cache")
+    assert_bits_equal(gv, vc2, "C1 step 2 v_cache")
+    assert_close(out_f64(out, "fp32"), want, "fp32", "C1 step 2")
+
+
+# --------------------------------------------------------------------------
+# small randomised shapes: tile edges, ragged lengths, groups, windows, rotary
+# --------------------------------------------------------------------------
+
+SMALL = [
+    # dtype, B, S, H, Hkv, D, M, lens, window, rotary, interleaved, entry
+    ("fp16", 3, 1, 8, 2, 128, 300, [0, 63, 257], -1, False, 0, "decode"),
+    ("bf16", 2, 1, 32, 8, 128, 600, [64, 511], -1, False, 0, "decode"),
+    ("fp16", 4, 1, 28, 4, 128, 1100, [127, 128, 129, 1099], -1, False, 0, "decode"),
+    ("bf16", 2, 1, 8, 8, 128, 200, [5, 199], -1, True, 0, "decode"),
+    ("fp16", 2, 1, 16, 2, 128, 300, [299, 17], 64, False, 0, "decode"),
+    ("bf16", 2, 1, 16, 1, 128, 256, [256, 256], 256, False, 0, "decode"),     # full: evict 1
+    ("fp32", 2, 1, 6, 3, 64, 80, [0, 79], -1, True, 1, "decode"),
+    ("fp16", 2, 1, 4, 2, 64, 100, [10, 99], -1, False, 0, "decode"),
+    ("bf16", 2, 37, 8, 2, 128, 400, [0, 200], -1, False, 0, "prefill"),
+    ("fp16", 2, 64, 28, 4, 128, 300, [63, 1], -1, False, 0, "prefill"),
+    ("bf16", 1, 130, 32, 8, 128, 512, [0], -1, True, 0, "prefill"),
+    ("fp16", 3, 17, 8, 1, 128, 128, [0, 50, 111], -1, True, 1, "prefill"),
+    ("bf16", 2, 33, 16, 2, 128, 200, [100, 0], 40, False, 0, "prefill"),
+    ("fp16", 2, 5, 12, 4, 64, 64, [3, 59], -1, False, 0, "prefill"),
+    ("fp32", 2, 9, 4, 2, 8, 40, [0, 31], 7, False, 0, "prefill"),
+    ("bf16", 2, 3, 2, 1, 256, 40, [10, 0], -1, True, 0, "prefill"),
+    ("fp16", 1, 1, 1, 1, 8, 1, [0], -1, False, 0, "prefill"),               # M = 1
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[f"{s[0]}-{s[-1]}-{i}" for i, s in enumerate(SMALL)])
+def test_small_shapes(spec):
+    dt, B, S, H, Hkv, D, M, lens, W, rot, inter, entry = spec
+    case = gi.make_case("small", dt, B, S, H, Hkv, D, M, lens, seed=sum(map(ord, repr(spec))) % 1000,
+                        window=W, rotary=rot, interleaved=inter,
+                        rotary_rows=(M + S if rot else None))
+    check_full(case, entry, f"small {spec}")
+
+
+# --------------------------------------------------------------------------
+# the halves: append and eviction on their own
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,D,rot", [("fp16", 128, False), ("bf16", 64, True), ("fp32", 8, True),
+                                      ("fp16", 6, False)])
+def test_append_by_index_code(dt, D, rot):
+    B, S, Hkv, M = 3, 5, 2, 40
+    case = gi.make_case("append", dt, B, S, 2 * Hkv, Hkv, D, M, [0, 17, 35], 3, rotary=rot,
+                        rotary_rows=M)
+    code = np.arange(B * S * Hkv * D, dtype=np.float64).reshape(B, S, Hkv * D) % 1000
+    case.k_new = gi.to_bits(code, dt)
+    case.v_new = gi.to_bits(-code, dt)
+    say(f"[gpu] append {dt} D={D} rot={rot}")
+    st, kc, vc = O.gqa_append_kv(case)
+    dev = DevCase(case)
+    dev.append()
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "append k_cache")
+    assert_bits_equal(gv, vc, "append v_cache")
+
+
+@pytest.mark.parametrize("dt,D,M,lens,incoming", [
+    ("bf16", 128, 4096, [4096, 4095, 100, 0], 1),        # one-row drop, halo path
+    ("fp16", 128, 700, [700, 690, 650, 10], 30),         # several rows, halo path
+    ("fp32", 8, 3000, [3000, 2999, 1500, 2990], 200),    # large drop, serial path
+    ("fp16", 6, 513, [513, 300, 513, 0], 1),             # 12-byte rows
+    ("bf16", 64, 64, [64, 64, 10, 64], 64),              # drop everything
+])
+def test_evict_window_half(dt, D, M, lens, incoming):
+    import grouped_query_kv_amd as gqa
+    case = gi.make_case("evict", dt, len(lens), 1, 2, 2, D, M, lens, 4)
+    say(f"[gpu] evict {dt} D={D} M={M} lens={lens} incoming={incoming}")
+    st, kc, vc, after = O.gqa_evict_window(case, incoming)
+    dev = DevCase(case)
+    got_after = gqa.gqa_evict_window(dev.k_cache, dev.v_cache, dev.lens_host, dev.lens_dev, incoming)
+    assert got_after.tolist() == after.tolist()
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "evict k_cache")
+    assert_bits_equal(gv, vc, "evict v_cache")
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size
+# --------------------------------------------------------------------------
+
+def test_c2_decode_full():
+    check_full(gi.config(2), "decode", "C2")
+
+
+def test_c5_window_decode_rolling_steps():
+    import grouped_query_kv_amd as gqa
+    case = gi.config(5)
+    rng = np.random.default_rng(55)
+    dev = DevCase(case)
+    ptr = dev.k_cache.data_ptr()
+    for step in range(4):
+        say(f"[gpu] C5 rolling step {step}")
+        st, want, kc, vc, lens = O.gqa_attention(case, "decode")
+        assert st == O.OK and lens.tolist() == [4096] * 8
+        out = dev.run("decode")
+        gk, gv = dev.caches()
+        assert_bits_equal(gk, kc, f"C5 step {step} k_cache")
+        assert_bits_equal(gv, vc, f"C5 step {step} v_cache")
+        assert_close(out_f64(out, "bf16"), want, "bf16", f"C5 step {step}")
+        assert dev.k_cache.data_ptr() == ptr
+        nxt = gi.next_decode_tokens(case, rng)
+        nxt.k_cache, nxt.v_cache = kc, vc
+        case = nxt
+        dev.case = case
+        for name in ("q", "k_new", "v_new"):
+            getattr(dev, name).copy_(to_dev(getattr(case, name), "bf16"))
+    # the same full cache with the window off has no room
+    case.local_window_size = -1
+    dev.case = case
+    with pytest.raises(gqa.GQAError) as e:
+        dev.run("decode")
+    assert e.value.status == gqa.GQA_ERR_NO_ROOM
+
+
+def test_c3_prefill_full_sampled():
+    case = gi.config(3)
+    rows = {0: [0, 1, 2, 63, 64, 127, 128, 1000, 2047], 1: [5, 511, 512, 2046],
+            2: [0, 2047], 3: [1023, 1024, 1025]}
+    say("[gpu] C3 prefill (sampled rows vs oracle, full caches)")
+    want, kc, vc = oracle_sampled(case, rows)
+    dev = DevCase(case)
+    out = dev.run("prefill")
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "C3 k_cache")
+    assert_bits_equal(gv, vc, "C3 v_cache")
+    got = out_f64(out, "bf16")
+    worst = max(assert_close(got[b, r], want[b], "bf16", f"C3 b={b}") for b, r in rows.items())
+    say(f"[gpu]   max abs error {worst:.3e}")
+
+
+def test_c4_continuation_full_sampled():
+    case = gi.config(4)
+    rows = {b: [0, 1, 63, 64, 126, 127] for b in range(case.batch)}
+    say(f"[gpu] C4 continuation lens={case.seqlens_k.tolist()}")
+    want, kc, vc = oracle_sampled(case, rows)
+    dev = DevCase(case)
+    out = dev.run("prefill")
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "C4 k_cache")
+    assert_bits_equal(gv, vc, "C4 v_cache")
+    got = out_f64(out, "fp16")
+    worst = max(assert_close(got[b, r], want[b], "fp16", f"C4 b={b}") for b, r in rows.items())
+    say(f"[gpu]   max abs error {worst:.3e}")
+
+
+# --------------------------------------------------------------------------
+# prefill then decodes equals a one-shot prefill (the worked example's story)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp32", 8)])
+def test_prefill_then_decodes_match_one_shot(dt, D):
+    import torch
+    n, k = 70, 5
+    full = gi.make_case("inc", dt, 2, n + k, 8, 2, D, 128, [0, 0], 77, rotary=True, rotary_rows=128)
+    st, ref, _, _, _ = O.gqa_attention(full)
+    part = full.copy()
+    part.new_tokens = n
+    part.q, part.k_new, part.v_new = full.q[:, :n], full.k_new[:, :n], full.v_new[:, :n]
+    say(f"[gpu] incremental {dt}: prefill {n} then {k} decodes")
+    dev = DevCase(part)
+    out = dev.run("prefill")
+    assert_close(out_f64(out, dt), ref[:, :n], dt, "prefill part")
+    for s in range(k):
+        step = full.copy()
+        step.new_tokens = 1
+        step.q, step.k_new, step.v_new = (x[:, n + s:n + s + 1].copy() for x in (full.q, full.k_new, full.v_new))
+        dev.case = step
+        dev.q, dev.k_new, dev.v_new = (to_dev(getattr(step, a), dt) for a in ("q", "k_new", "v_new"))
+        dev.set_lengths([n + s, n + s])
+        out = dev.run("decode")
+        assert_close(out_f64(out, dt)[:, 0], ref[:, n + s], dt, f"decode {s}")
+    torch.cuda.synchronize()
