@@ -53,8 +53,12 @@ __device__ inline void rotate_pair(typename T::bits& a, typename T::bits& b, flo
   const double dc = static_cast<double>(c), ds = static_cast<double>(s);
   const double y1 = x1 * dc - x2 * ds;
   const double y2 = x2 * dc + x1 * ds;
-  a = T::from_float(static_cast<float>(y1));
-  b = T::from_float(static_cast<float>(y2));
+  float f1 = static_cast<float>(y1), f2 = static_cast<float>(y2);
+  // The compiler would otherwise fold fp64->fp32->fp16 into one fp64->fp16
+  // rounding, which differs from the two-step rule exactly at fp16 ties.
+  asm volatile("" : "+v"(f1), "+v"(f2));
+  a = T::from_float(f1);
+  b = T::from_float(f2);
 }
 
 // ----------------------------------------------------------------------------

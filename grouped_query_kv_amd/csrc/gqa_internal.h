@@ -44,7 +44,7 @@ struct WorkspaceLayout {
 };
 
 // Decode: fast split-KV kernel limits.
-constexpr int kDecodeBlockKeys = 64;     // keys per wave iteration
+constexpr int kDecodeBlockKeys = 32;     // keys per wave iteration
 constexpr int kDecodeWaves = 4;          // waves per workgroup
 constexpr int kDecodeMaxHG = 8;          // query heads per workgroup (MFMA N padded to 16)
 constexpr int kDecodeMinChunk = 64;      // smallest split, bounds the partial slots
