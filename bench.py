@@ -11,9 +11,10 @@ cache full, evict one row per step), each with its roofline fraction.
 
 Timing: inputs are resident in HBM before the timed region; each step rotates
 over enough independent input sets (>= 1 GiB) that the 256 MB Infinity Cache
-cannot serve repeated reads. HIP events recorded on the launch stream around
-each call give the per-call device time; wall time over K steps (synchronised
-on both sides) gives ms_per_step.
+cannot serve repeated reads. Wall time over K back-to-back steps
+(synchronised on both sides) gives ms_per_step and `value`; a second pass of
+the same K steps with HIP events recorded on the launch stream around each
+call gives the per-call device time used for the roofline fraction.
 
 The CPU baseline times the fp64 oracle (as it stands) on a bounded sample of
 the decode workload on this host's cores.
@@ -128,22 +129,29 @@ def prefill_flops(case):
 # ----------------------------------------------------------------------------
 
 def time_calls(torch, sets, call, steps, warmup):
-    """Run warmup + steps calls rotating over sets; returns (wall_ms/step, event_ms list)."""
+    """Warmup, then two passes of `steps` calls rotating over the input sets.
+
+    Pass 1 (the timed region): barrier + synchronize, the calls back to back,
+    synchronize; returns wall ms per step. Pass 2: the same calls, each
+    bracketed by HIP events recorded on the launch stream; returns the list
+    of per-call device times in ms (the kernel time the roofline uses).
+    """
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         call(sets[i % len(sets)])
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        s = sets[(warmup + i) % len(sets)]
-        ev[i][0].record(stream)
-        call(s)
-        ev[i][1].record(stream)
+        call(sets[(warmup + i) % len(sets)])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(sets[(warmup + i) % len(sets)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     return wall, per
 

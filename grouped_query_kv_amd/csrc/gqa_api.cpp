@@ -185,12 +185,11 @@ WorkspaceLayout workspace_layout(const gqa_shape& s) {
   const int64_t hg = (G + kDecodeMaxHG - 1) / kDecodeMaxHG;
   l.counters = 0;
   l.counters_bytes = align256(size_t(B * Hkv * hg) * sizeof(int32_t));
-  // decode partials: [B, Hkv, hg, splits, HG_max, D + 2] fp32
+  // decode partials: one slot of [HG_max, D + 2] fp32 per (workgroup, unit)
+  // pair that can meet: at most (workgroups + units) slots
   int64_t partial = 0;
-  if (D == 128 && s.dtype != GQA_FP32) {
-    const int64_t splits = (M + kDecodeMinChunk - 1) / kDecodeMinChunk;
-    partial = B * Hkv * hg * splits * kDecodeMaxHG * (D + 2) * 4;
-  }
+  if (D == 128 && s.dtype != GQA_FP32)
+    partial = (kDecodeMaxWorkgroups + B * Hkv * hg) * int64_t(kDecodeMaxHG) * (D + 2) * 4;
   // eviction halos: [B, Hkv, 2, chunks, halo rows, row bytes]
   const int64_t row_bytes = D * (s.dtype == GQA_FP32 ? 4 : 2);
   const EvictGeometry eg = evict_geometry((int)row_bytes);

@@ -44,10 +44,16 @@ struct WorkspaceLayout {
 };
 
 // Decode: fast split-KV kernel limits.
-constexpr int kDecodeBlockKeys = 32;     // keys per wave iteration
-constexpr int kDecodeWaves = 4;          // waves per workgroup
-constexpr int kDecodeMaxHG = 8;          // query heads per workgroup (MFMA N padded to 16)
-constexpr int kDecodeMinChunk = 64;      // smallest split, bounds the partial slots
+#ifndef GQA_DECODE_WG_WAVES
+#define GQA_DECODE_WG_WAVES 8
+#endif
+constexpr int kDecodeWaves = GQA_DECODE_WG_WAVES;  // waves per workgroup
+#ifndef GQA_DECODE_WORKGROUPS
+#define GQA_DECODE_WORKGROUPS 256
+#endif
+constexpr int kDecodeMaxWorkgroups = GQA_DECODE_WORKGROUPS;  // per launch: one per CU, all resident
+constexpr int kDecodeMaxHG = 16;         // query heads per unit (the 16 MFMA columns)
+constexpr int kDecodeArgBatch = 64;      // largest batch the fast decode plans in its arguments
 
 // Eviction: rows per workgroup chunk is chosen so a chunk is 64 KiB; halo
 // copies are used up to this many dropped rows.
