@@ -29,17 +29,26 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// MFMA 32x32x16 for the storage dtype, the packed fp32 -> dtype conversion
+// (v_cvt_pk_*_f32, nearest-even) and a two-element sum on the dot unit.
 template <class T> struct Mma32;
 template <> struct Mma32<F16> {
   __device__ static inline f32x16 run(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  // two fp32 -> fp16 (nearest-even), packed
   __device__ static inline uint32_t pack2(float x, float y) {
-    return uint32_t(F16::from_float(x)) | (uint32_t(F16::from_float(y)) << 16);
+    const f16x2 v = {static_cast<_Float16>(x), static_cast<_Float16>(y)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  // acc + lo + hi of a packed pair
+  __device__ static inline float dot_ones(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                  __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
   }
 };
 template <> struct Mma32<BF16> {
@@ -48,19 +57,26 @@ template <> struct Mma32<BF16> {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack2(float x, float y) {
-    return uint32_t(BF16::from_float(x)) | (uint32_t(BF16::from_float(y)) << 16);
+    const bf16x2 v = {static_cast<__bf16>(x), static_cast<__bf16>(y)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float dot_ones(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
   }
 };
 
 constexpr int kD = 128;
 constexpr int kBK = 64;                       // keys per tile
-constexpr int kRows = 128;                    // query rows per workgroup
 constexpr int kThreads = 256;
 constexpr int kKStride = kD + 8;              // K tile row stride in halves (272 B)
-constexpr int kVStride = kBK + 8;             // V^T tile row stride in halves (144 B)
 constexpr int kKTile = kBK * kKStride;        // halves
-constexpr int kVTile = kD * kVStride;         // halves
+constexpr int kVTile = kD * kBK;              // V^T tile, 128 B rows, swizzled
 constexpr float kLog2e = 1.4426950408889634f;
+// The running maximum used in the exponent is refreshed only when a score
+// exceeds it by more than this many binary orders, so weights stay <= 2^8:
+// exact in fp32, representable in fp16/bf16 with full relative precision.
+constexpr float kRescaleSlack = 8.f;
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -73,7 +89,8 @@ struct PrefillArgs {
   int B, S, H, Hkv, G, M, W;
   int rot, rot_rows, interleaved;
   int n_rb;           // row blocks per (b, kv head)
-  float scale_log2;
+  float scale_log2;   // |scale| * log2(e)
+  uint32_t q_sign;    // 0x80008000 when the scale is negative: Q is negated (exact)
 };
 
 // Rotate one row's 8 B-operand chunks in place. Chunk ks holds dims
@@ -117,17 +134,33 @@ __device__ inline void rotate_q(uint4 (&qv)[8], int c, const float* cosr, const 
   }
 }
 
-// Staging of one 64-key tile: thread (kq = tid / 16, dg = tid % 16) moves keys
-// 4 kq .. 4 kq + 3, dims 8 dg .. 8 dg + 7, of K and V. Rows at or past the
-// valid length are not read; zeros are staged.
+// ---------------------------------------------------------------------------
+// Staging of one 64-key tile. Thread (wave w, lane) moves keys 16 w + 4 qd + j
+// (j = 0..3), dims 8 dg .. 8 dg + 7, of K and V, with dg and qd drawn from the
+// lane bits so that each 16-lane group of a store covers 8 dim groups x 2 key
+// quads: the V^T stores below are then free of bank conflicts. Rows at or past
+// the valid length are not read; zeros are staged.
+//
+// V^T layout: row d holds the tile's 64 keys in MFMA k order (within every 16
+// keys, key 8a + 4c + r sits at 8c + 4a + r, matching the P^T operand the
+// score layout hands over), as eight 16-byte chunks whose order is XOR-swizzled
+// by vt_swz(d) so that the lanes of a read (consecutive d) and of a store
+// (d = 8 dg + e) hit distinct banks.
+// ---------------------------------------------------------------------------
 struct Stage {
   uint4 k[4];
   uint4 v[4];
 };
 
+__device__ inline int stage_dg(int tid) { return (tid & 7) | (((tid >> 4) & 1) << 3); }
+__device__ inline int stage_kq(int tid) {
+  return 4 * (tid >> 6) + ((((tid >> 3) & 1) << 1) | ((tid >> 5) & 1));
+}
+__device__ inline int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
 __device__ inline void stage_load(Stage& st, const uint16_t* kc, const uint16_t* vc, int tb,
                                   int kvalid, int tid) {
-  const int kq = tid >> 4, dg = tid & 15;
+  const int kq = stage_kq(tid), dg = stage_dg(tid);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = tb + 4 * kq + j;
@@ -142,13 +175,13 @@ __device__ inline void stage_load(Stage& st, const uint16_t* kc, const uint16_t*
 }
 
 __device__ inline void stage_store(const Stage& st, uint16_t* ks, uint16_t* vs, int tid) {
-  const int kq = tid >> 4, dg = tid & 15;
+  const int kq = stage_kq(tid), dg = stage_dg(tid);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     *reinterpret_cast<uint4*>(ks + (4 * kq + j) * kKStride + 8 * dg) = st.k[j];
-  // V^T[d][pos]: within each 16 keys, key 8a + 4c + r sits at 8c + 4a + r
   const int u = kq >> 2, qd = kq & 3;                       // qd = 2a + c
-  const int pos = 16 * u + 4 * (((qd & 1) << 1) | (qd >> 1));
+  const int perm = ((qd & 1) << 1) | (qd >> 1);             // 2c + a
+  const int chunk = 2 * u + (perm >> 1), sub = perm & 1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int w = e >> 1, sh = 16 * (e & 1);
@@ -159,17 +192,119 @@ __device__ inline void stage_store(const Stage& st, uint16_t* ks, uint16_t* vs, 
     uint2 pk;
     pk.x = x0 | (x1 << 16);
     pk.y = x2 | (x3 << 16);
-    *reinterpret_cast<uint2*>(vs + (8 * dg + e) * kVStride + pos) = pk;
+    const int d = 8 * dg + e;
+    *reinterpret_cast<uint2*>(vs + d * kBK + 8 * (chunk ^ vt_swz(d)) + 4 * sub) = pk;
   }
 }
 
+// ---------------------------------------------------------------------------
+// Online softmax of one 32-key half of S^T for the lane's row (16 scores here,
+// the other 16 in lane ^ 32), then P^T packed as the PV B operand.
+// ---------------------------------------------------------------------------
+struct RowState {
+  float m_run;   // running max of score * cs (-inf before the first visible key)
+  float m_use;   // reference max in the exponent (finite)
+  float l;       // this lane's share of the sum of the packed weights
+};
+
+template <class T, bool kMask>
+__device__ inline void softmax_half(f32x16& s, RowState& rs, f32x16 (&o)[4], uint4 (&pk)[2],
+                                    float cs, int lim_hi, int span) {
+  if (kMask) {
+    // key offset within the lane's keys: 8 (v / 4) + v % 4; visible iff
+    // 0 <= lim_hi - offset <= span (causal limit and window start together)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int off = 8 * (v >> 2) + (v & 3);
+      s[v] = uint32_t(lim_hi - off) <= uint32_t(span) ? s[v] : -INFINITY;
+    }
+  }
+  float tmax = s[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                     false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float tm = tmax * cs;
+  if (__any(tm > rs.m_run + kRescaleSlack)) {
+    const float m_new = fmaxf(rs.m_run, tm);
+    const float use_new = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(rs.m_use - use_new);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+    rs.l *= alpha;
+    rs.m_run = m_new;
+    rs.m_use = use_new;
+  }
+  const float mu = rs.m_use;
+  uint32_t w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * e], cs, -mu));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * e + 1], cs, -mu));
+    w[e] = Mma32<T>::pack2(p0, p1);
+    rs.l = Mma32<T>::dot_ones(w[e], rs.l);
+  }
+  pk[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  pk[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// S^T (32 keys of half h) = K Q^T for the lane's row
+template <class T>
+__device__ inline f32x16 scores_half(const uint16_t* ks, const uint4 (&qv)[8], int h, int col,
+                                     int c) {
+  const uint16_t* krow = ks + (32 * h + col) * kKStride + 8 * c;
+  f32x16 sc = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow), qv[0], f32x16{});
+#pragma unroll
+  for (int kk = 1; kk < 8; ++kk)
+    sc = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * kk), qv[kk], sc);
+  return sc;
+}
+
+// O^T += V^T P^T over the 32 keys of half h
+template <class T>
+__device__ inline void pv_half(const uint16_t* vs, const uint4 (&pk)[2], f32x16 (&o)[4], int h,
+                               int col, int c) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + col;
+    const uint16_t* vrow = vs + d * kBK;
+    const int sw = vt_swz(d);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 va = *reinterpret_cast<const uint4*>(vrow + 8 * ((4 * h + 2 * u + c) ^ sw));
+      o[dt] = Mma32<T>::run(va, pk[u], o[dt]);
+    }
+  }
+}
+
+// One 64-key tile for the lane's row: both score halves are issued before the
+// first softmax so the second runs on the matrix cores meanwhile.
+template <class T, bool kMask>
+__device__ inline void tile_step(const uint16_t* ks, const uint16_t* vs, const uint4 (&qv)[8],
+                                 f32x16 (&o)[4], RowState& rs, float cs, int lim_hi, int span,
+                                 int col, int c) {
+  f32x16 s0 = scores_half<T>(ks, qv, 0, col, c);
+  f32x16 s1 = scores_half<T>(ks, qv, 1, col, c);
+  uint4 pk[2];
+  softmax_half<T, kMask>(s0, rs, o, pk, cs, lim_hi, span);
+  pv_half<T>(vs, pk, o, 0, col, c);
+  softmax_half<T, kMask>(s1, rs, o, pk, cs, lim_hi - 32, span);
+  pv_half<T>(vs, pk, o, 1, col, c);
+}
+
+// One workgroup = 4 waves x 32 query rows of one (b, kv head).
 template <class T>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKTile];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, c = lane >> 5;     // S^T column (= row of this wave), k half
+  const int col = lane & 31, c = lane >> 5;     // S^T column (= the lane's row), k half
   const int units = a.B * a.Hkv;
   const int rb = a.n_rb - 1 - int(blockIdx.x) / units;    // longest row blocks first
   const int bg = int(blockIdx.x) % units;
@@ -179,19 +314,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const int L = clamp_len(a.lens[b], 0, a.M - S);
   const int kvalid = L + S;
 
-  // rows of this workgroup / wave / lane
-  const int r0 = rb * kRows;
+  const int r0 = rb * 128;
   const int wr0 = r0 + 32 * wave;
   const bool wave_has_rows = wr0 < nrows;
-  const int my_r = wr0 + col;
-  const bool row_ok = my_r < nrows;
-  const int my_i = row_ok ? my_r / G : S - 1;
-  const int my_h = g * G + (row_ok ? my_r % G : 0);
-  const int my_p = L + my_i;                              // causal limit
-  const int my_ws = a.W > 0 ? my_p - a.W + 1 : 0;          // window start
+  const int r = wr0 + col;
+  const bool row_ok = r < nrows;
+  const int my_i = row_ok ? r / G : S - 1;
+  const int my_h = g * G + (row_ok ? r % G : 0);
+  const int my_p = L + my_i;                                // causal limit
+  const int my_ws = a.W > 0 ? max(0, my_p - a.W + 1) : 0;   // window start
 
   // workgroup and wave key ranges
-  const int wg_ilo = r0 / G, wg_ihi = min(S - 1, (r0 + kRows - 1) / G);
+  const int wg_ilo = r0 / G, wg_ihi = min(S - 1, (r0 + 127) / G);
   const int w_ilo = min(S - 1, wr0 / G), w_ihi = min(S - 1, (wr0 + 31) / G);
   const int wg_kstart = a.W > 0 ? max(0, L + wg_ilo - a.W + 1) : 0;
   const int wg_kend = L + wg_ihi + 1;
@@ -212,6 +346,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       rotate_q<T>(qv, c, a.cosv + int64_t(pos) * (kD / 2), a.sinv + int64_t(pos) * (kD / 2),
                   a.interleaved);
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qv[ks].x ^= a.q_sign; qv[ks].y ^= a.q_sign; qv[ks].z ^= a.q_sign; qv[ks].w ^= a.q_sign;
+    }
   }
 
   const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
@@ -223,7 +361,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  RowState rs{-INFINITY, 0.f, 0.f};
+  const float cs = a.scale_log2;
+  const int span = my_p - my_ws;
 
   const int t_begin = wg_kstart / kBK;
   const int t_end = (wg_kend + kBK - 1) / kBK;
@@ -238,78 +378,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     const bool more = t + 1 < t_end;
     if (more) stage_load(st, kc, vc, tb + kBK, kvalid, tid);
 
-    const bool active = wave_has_rows && tb < w_kend && tb + kBK > w_kstart;
-    if (active) {
-      const uint16_t* ks = lds_k[buf];
-      const uint16_t* vs = lds_v[buf];
-      // ---- S^T = K Q^T: two 32-key halves of the tile ----
-      f32x16 s[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
-        const uint16_t* krow = ks + (32 * h + col) * kKStride + 8 * c;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          s[h] = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * kk), qv[kk], s[h]);
-      }
-      // ---- scale, mask (boundary tiles only), online softmax ----
+    if (wave_has_rows && tb < w_kend && tb + kBK > w_kstart) {
       const bool full = tb + kBK - 1 <= w_full_hi && tb >= w_full_lo;
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[h][v] * a.scale_log2;
-          if (!full) {
-            const int key = tb + 32 * h + 8 * (v >> 2) + 4 * c + (v & 3);
-            x = (key <= my_p && key >= my_ws) ? x : -INFINITY;
-          }
-          s[h][v] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      if (__any(m_new != m_run)) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-      }
-      l_run *= alpha;
-      m_run = m_new;
-      uint4 pk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(s[u >> 1][8 * (u & 1) + e] - m_use);
-          l_run += p[e];
-        }
-        pk[u].x = Mma32<T>::pack2(p[0], p[1]);
-        pk[u].y = Mma32<T>::pack2(p[2], p[3]);
-        pk[u].z = Mma32<T>::pack2(p[4], p[5]);
-        pk[u].w = Mma32<T>::pack2(p[6], p[7]);
-      }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vrow = vs + (32 * dt + col) * kVStride + 8 * c;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[dt] = Mma32<T>::run(*reinterpret_cast<const uint4*>(vrow + 16 * u), pk[u], o[dt]);
-      }
+      const int lim_hi = my_p - (tb + 4 * c);
+      if (full)
+        tile_step<T, false>(lds_k[buf], lds_v[buf], qv, o, rs, cs, lim_hi, span, col, c);
+      else
+        tile_step<T, true>(lds_k[buf], lds_v[buf], qv, o, rs, cs, lim_hi, span, col, c);
     }
     if (more) stage_store(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
     __syncthreads();
   }
 
   if (!row_ok) return;
-  l_run += __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_run;
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs.l), __float_as_uint(rs.l),
+                                                    false, false);
+  const float inv = 1.f / (__uint_as_float(lsw[0]) + __uint_as_float(lsw[1]));
   uint16_t* orow = a.out + ((int64_t(b) * S + my_i) * a.H + my_h) * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -339,8 +423,9 @@ hipError_t launch_prefill_fast(const Problem& p, hipStream_t st) {
   a.cosv = p.cos; a.sinv = p.sin;
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window;
   a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
-  a.n_rb = ceil_div(p.S * p.G, kRows);
-  a.scale_log2 = p.scale * kLog2e;
+  a.n_rb = ceil_div(p.S * p.G, 128);
+  a.scale_log2 = fabsf(p.scale) * kLog2e;
+  a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
   const int blocks = a.n_rb * p.B * p.Hkv;
   if (blocks == 0) return hipSuccess;
   if (p.dtype == GQA_FP16)
