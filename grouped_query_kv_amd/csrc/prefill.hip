@@ -69,9 +69,6 @@ template <> struct Mma32<BF16> {
 constexpr int kD = 128;
 constexpr int kBK = 64;                       // keys per tile
 constexpr int kThreads = 256;
-constexpr int kKStride = kD + 8;              // K tile row stride in halves (272 B)
-constexpr int kKTile = kBK * kKStride;        // halves
-constexpr int kVTile = kD * kBK;              // V^T tile, 128 B rows, swizzled
 constexpr float kLog2e = 1.4426950408889634f;
 // The running maximum used in the exponent is refreshed only when a score
 // exceeds it by more than this many binary orders, so weights stay <= 2^8:
@@ -135,71 +132,81 @@ __device__ inline void rotate_q(uint4 (&qv)[8], int c, const float* cosr, const 
 }
 
 // ---------------------------------------------------------------------------
-// Staging of one 64-key tile. Thread (wave w, lane) moves keys 16 w + 4 qd + j
-// (j = 0..3), dims 8 dg .. 8 dg + 7, of K and V, with dg and qd drawn from the
-// lane bits so that each 16-lane group of a store covers 8 dim groups x 2 key
-// quads: the V^T stores below are then free of bank conflicts. Rows at or past
-// the valid length are not read; zeros are staged.
-//
-// V^T layout: row d holds the tile's 64 keys in MFMA k order (within every 16
-// keys, key 8a + 4c + r sits at 8c + 4a + r, matching the P^T operand the
-// score layout hands over), as eight 16-byte chunks whose order is XOR-swizzled
-// by vt_swz(d) so that the lanes of a read (consecutive d) and of a store
-// (d = 8 dg + e) hit distinct banks.
+// Tiles in LDS. K and V tiles are row-major, 64 keys x 256 bytes, filled
+// straight from HBM by buffer_load_dwordx4 ... lds (no register staging): one
+// instruction moves four 256-byte rows, lane i writing 16-byte slot i. The
+// buffer range ends at the valid length, so rows past it read as zeros.
+// Within a row the sixteen 16-byte chunks are XOR-swizzled per key so that
+// the operand reads below are free of bank conflicts (16 lanes of a b128
+// read, 32 lanes of a b64 read per cycle):
+//   K: chunk ^ (key & 15)     (b128 reads of 16 consecutive keys)
+//   V: chunk ^ 4 (key & 3)    (transposing b64 reads, 4 keys x 2 dim groups)
 // ---------------------------------------------------------------------------
-struct Stage {
-  uint4 k[4];
-  uint4 v[4];
+constexpr int kTileBytes = kBK * kD * 2;      // 16 KB
+
+__device__ inline int swz_k(int key) { return key & 15; }
+__device__ inline int swz_v(int key) { return (key & 3) << 2; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Per-lane byte offsets of the tile loads, relative to the tile's first key.
+// Wave w moves rows 16 w + 4 q + lane / 16 (q = 0..3); the swizzle depends on
+// the row only through key & 15 = (4 q + lane / 16) & 15 (tiles start at
+// multiples of 64), so four offsets per lane cover every tile.
+struct LoadOffsets {
+  int k[4];
+  int v;         // V: swizzle independent of q; quad q adds 1024 q
 };
 
-__device__ inline int stage_dg(int tid) { return (tid & 7) | (((tid >> 4) & 1) << 3); }
-__device__ inline int stage_kq(int tid) {
-  return 4 * (tid >> 6) + ((((tid >> 3) & 1) << 1) | ((tid >> 5) & 1));
-}
-__device__ inline int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
-__device__ inline void stage_load(Stage& st, const uint16_t* kc, const uint16_t* vc, int tb,
-                                  int kvalid, int tid) {
-  const int kq = stage_kq(tid), dg = stage_dg(tid);
+__device__ inline LoadOffsets load_offsets(int wave, int lane) {
+  LoadOffsets lo;
+  const int lr = lane >> 4, slot = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = tb + 4 * kq + j;
-    if (row < kvalid) {
-      st.k[j] = *reinterpret_cast<const uint4*>(kc + int64_t(row) * kD + 8 * dg);
-      st.v[j] = *reinterpret_cast<const uint4*>(vc + int64_t(row) * kD + 8 * dg);
-    } else {
-      st.k[j] = make_uint4(0, 0, 0, 0);
-      st.v[j] = make_uint4(0, 0, 0, 0);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int rrow = 16 * wave + 4 * q + lr;
+    lo.k[q] = rrow * 256 + 16 * (slot ^ swz_k(rrow));
   }
+  lo.v = (16 * wave + lr) * 256 + 16 * (slot ^ swz_v(lr));
+  return lo;
 }
 
-__device__ inline void stage_store(const Stage& st, uint16_t* ks, uint16_t* vs, int tid) {
-  const int kq = stage_kq(tid), dg = stage_dg(tid);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<uint4*>(ks + (4 * kq + j) * kKStride + 8 * dg) = st.k[j];
-  const int u = kq >> 2, qd = kq & 3;                       // qd = 2a + c
-  const int perm = ((qd & 1) << 1) | (qd >> 1);             // 2c + a
-  const int chunk = 2 * u + (perm >> 1), sub = perm & 1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1, sh = 16 * (e & 1);
-    const uint32_t x0 = ((&st.v[0].x)[w] >> sh) & 0xFFFFu;
-    const uint32_t x1 = ((&st.v[1].x)[w] >> sh) & 0xFFFFu;
-    const uint32_t x2 = ((&st.v[2].x)[w] >> sh) & 0xFFFFu;
-    const uint32_t x3 = ((&st.v[3].x)[w] >> sh) & 0xFFFFu;
-    uint2 pk;
-    pk.x = x0 | (x1 << 16);
-    pk.y = x2 | (x3 << 16);
-    const int d = 8 * dg + e;
-    *reinterpret_cast<uint2*>(vs + d * kBK + 8 * (chunk ^ vt_swz(d)) + 4 * sub) = pk;
-  }
+// Issue this wave's share (16 rows) of one tile: quad q covers rows
+// 16 w + 4 q .. + 3. The instruction's immediate offset moves both the
+// memory address and the LDS destination, so V (one offset pattern) steps
+// through its quads with it from one LDS base; K (a different swizzle per
+// quad) uses per-quad lane offsets and LDS bases. Each tile gets its own
+// buffer range, starting at its first key and ending at the valid length:
+// the range check covers the lane and immediate offsets but not the scalar
+// one, so the tile base goes into the descriptor.
+template <bool kIsV, int Q>
+__device__ inline void quad_load(__amdgpu_buffer_rsrc_t rsrc, unsigned char* tile,
+                                 const LoadOffsets& lo, int wave) {
+  if (kIsV)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 16 * wave * 256), 16, lo.v, 0,
+                                             1024 * Q, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (16 * wave + 4 * Q) * 256),
+                                             16, lo.k[Q], 0, 0, 0);
+}
+
+template <bool kIsV>
+__device__ inline void tile_load(const uint16_t* base, int kvalid, unsigned char* tile, int t0,
+                                 const LoadOffsets& lo, int wave) {
+  t0 = __builtin_amdgcn_readfirstlane(t0);      // the tile start is wave-uniform
+  const int rows = max(0, kvalid - t0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base + int64_t(t0) * kD), 0, rows * kD * 2, 0x00020000);
+  quad_load<kIsV, 0>(rsrc, tile, lo, wave);
+  quad_load<kIsV, 1>(rsrc, tile, lo, wave);
+  quad_load<kIsV, 2>(rsrc, tile, lo, wave);
+  quad_load<kIsV, 3>(rsrc, tile, lo, wave);
 }
 
 // ---------------------------------------------------------------------------
-// Online softmax of one 32-key half of S^T for the lane's row (16 scores here,
-// the other 16 in lane ^ 32), then P^T packed as the PV B operand.
+// Online softmax of one 64-key tile of S^T for the lane's row (32 scores
+// here, the other 32 in lane ^ 32), then P^T packed as the PV B operand.
 // ---------------------------------------------------------------------------
 struct RowState {
   float m_run;   // running max of score * cs (-inf before the first visible key)
@@ -208,20 +215,22 @@ struct RowState {
 };
 
 template <class T, bool kMask>
-__device__ inline void softmax_half(f32x16& s, RowState& rs, f32x16 (&o)[4], uint4 (&pk)[2],
+__device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4], uint4 (&pk)[4],
                                     float cs, int lim_hi, int span) {
   if (kMask) {
-    // key offset within the lane's keys: 8 (v / 4) + v % 4; visible iff
+    // key offset within the lane's keys: 32 h + 8 (v / 4) + v % 4; visible iff
     // 0 <= lim_hi - offset <= span (causal limit and window start together)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int off = 8 * (v >> 2) + (v & 3);
-      s[v] = uint32_t(lim_hi - off) <= uint32_t(span) ? s[v] : -INFINITY;
-    }
-  }
-  float tmax = s[0];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
+      for (int v = 0; v < 16; ++v) {
+        const int off = 32 * h + 8 * (v >> 2) + (v & 3);
+        s[h][v] = uint32_t(lim_hi - off) <= uint32_t(span) ? s[h][v] : -INFINITY;
+      }
+  }
+  float tmax = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, fmaxf(s[0][v], s[1][v]));
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
                                                      false, false);
@@ -241,69 +250,78 @@ __device__ inline void softmax_half(f32x16& s, RowState& rs, f32x16 (&o)[4], uin
     rs.m_use = use_new;
   }
   const float mu = rs.m_use;
-  uint32_t w[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * e], cs, -mu));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * e + 1], cs, -mu));
-    w[e] = Mma32<T>::pack2(p0, p1);
-    rs.l = Mma32<T>::dot_ones(w[e], rs.l);
+  for (int u = 0; u < 4; ++u) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 8 * (u & 1) + 2 * e;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][v], cs, -mu));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][v + 1], cs, -mu));
+      w[e] = Mma32<T>::pack2(p0, p1);
+      rs.l = Mma32<T>::dot_ones(w[e], rs.l);
+    }
+    pk[u] = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  pk[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  pk[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
-// S^T (32 keys of half h) = K Q^T for the lane's row
+// S^T (64 keys) = K Q^T for the lane's row; A = K rows (key 32 h + col,
+// dims 16 kk + 8 c .. + 7), B = Q^T.
 template <class T>
-__device__ inline f32x16 scores_half(const uint16_t* ks, const uint4 (&qv)[8], int h, int col,
-                                     int c) {
-  const uint16_t* krow = ks + (32 * h + col) * kKStride + 8 * c;
-  f32x16 sc = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow), qv[0], f32x16{});
+__device__ inline void scores_tile(const unsigned char* kt, const uint4 (&qv)[8], f32x16 (&s)[2],
+                                   int col, int c) {
 #pragma unroll
-  for (int kk = 1; kk < 8; ++kk)
-    sc = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * kk), qv[kk], sc);
-  return sc;
+  for (int h = 0; h < 2; ++h) {
+    const unsigned char* krow = kt + (32 * h + col) * 256;
+    const int sw = swz_k(col);
+    s[h] = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * (c ^ sw)), qv[0], f32x16{});
+#pragma unroll
+    for (int kk = 1; kk < 8; ++kk)
+      s[h] = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * ((2 * kk + c) ^ sw)),
+                           qv[kk], s[h]);
+  }
 }
 
-// O^T += V^T P^T over the 32 keys of half h
+// O^T += V^T P^T over the tile's 64 keys. The A operand (lane: dim d =
+// 32 dt + lane % 32, keys in the P^T order 16 u + 8 (e / 4) + 4 c + e % 4) comes
+// from two transposing reads: in each 16-lane group, lane j points at key
+// kb + j / 4, dims 4 (j % 4) .. + 3 of the group's 16 dims, and lane 4 a + e
+// receives dim 4 a + e of the four keys.
 template <class T>
-__device__ inline void pv_half(const uint16_t* vs, const uint4 (&pk)[2], f32x16 (&o)[4], int h,
-                               int col, int c) {
+__device__ inline void pv_tile(const unsigned char* vt, const uint4 (&pk)[4], f32x16 (&o)[4],
+                               int lane) {
+  const int j = lane & 15, c = lane >> 5, g1 = (lane >> 4) & 1;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int d = 32 * dt + col;
-    const uint16_t* vrow = vs + d * kBK;
-    const int sw = vt_swz(d);
+  for (int u = 0; u < 4; ++u) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 va = *reinterpret_cast<const uint4*>(vrow + 8 * ((4 * h + 2 * u + c) ^ sw));
-      o[dt] = Mma32<T>::run(va, pk[u], o[dt]);
+    for (int dt = 0; dt < 4; ++dt) {
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int key = 16 * u + 8 * r + 4 * c + (j >> 2);
+        const int ch = 4 * dt + 2 * g1 + ((j & 3) >> 1);
+        const unsigned char* ptr = vt + key * 256 + 16 * (ch ^ swz_v(key)) + 8 * (j & 1);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ptr));
+        const uint2 xx = __builtin_bit_cast(uint2, x);
+        w[2 * r] = xx.x;
+        w[2 * r + 1] = xx.y;
+      }
+      o[dt] = Mma32<T>::run(make_uint4(w[0], w[1], w[2], w[3]), pk[u], o[dt]);
     }
   }
 }
 
-// One 64-key tile for the lane's row: both score halves are issued before the
-// first softmax so the second runs on the matrix cores meanwhile.
-template <class T, bool kMask>
-__device__ inline void tile_step(const uint16_t* ks, const uint16_t* vs, const uint4 (&qv)[8],
-                                 f32x16 (&o)[4], RowState& rs, float cs, int lim_hi, int span,
-                                 int col, int c) {
-  f32x16 s0 = scores_half<T>(ks, qv, 0, col, c);
-  f32x16 s1 = scores_half<T>(ks, qv, 1, col, c);
-  uint4 pk[2];
-  softmax_half<T, kMask>(s0, rs, o, pk, cs, lim_hi, span);
-  pv_half<T>(vs, pk, o, 0, col, c);
-  softmax_half<T, kMask>(s1, rs, o, pk, cs, lim_hi - 32, span);
-  pv_half<T>(vs, pk, o, 1, col, c);
-}
-
-// One workgroup = 4 waves x 32 query rows of one (b, kv head).
+// One workgroup = 4 waves x 32 query rows of one (b, kv head). Software
+// pipeline per iteration t (one barrier): loads of K(t+2) and V(t+1) are in
+// flight while S(t+1) = K(t+1) Q^T runs on the matrix cores under the softmax
+// of tile t, then O += V(t) P(t).
 template <class T>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int col = lane & 31, c = lane >> 5;     // S^T column (= the lane's row), k half
   const int units = a.B * a.Hkv;
   const int rb = a.n_rb - 1 - int(blockIdx.x) / units;    // longest row blocks first
@@ -311,7 +329,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.G, S = a.S;
   const int nrows = S * G;
-  const int L = clamp_len(a.lens[b], 0, a.M - S);
+  // lengths are read through a vector load: mark them wave-uniform
+  const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.lens[b], 0, a.M - S));
   const int kvalid = L + S;
 
   const int r0 = rb * 128;
@@ -324,7 +343,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const int my_p = L + my_i;                                // causal limit
   const int my_ws = a.W > 0 ? max(0, my_p - a.W + 1) : 0;   // window start
 
-  // workgroup and wave key ranges
+  // workgroup and wave key ranges (tiles)
   const int wg_ilo = r0 / G, wg_ihi = min(S - 1, (r0 + 127) / G);
   const int w_ilo = min(S - 1, wr0 / G), w_ihi = min(S - 1, (wr0 + 31) / G);
   const int wg_kstart = a.W > 0 ? max(0, L + wg_ilo - a.W + 1) : 0;
@@ -333,6 +352,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const int w_kend = L + w_ihi + 1;
   const int w_full_lo = a.W > 0 ? L + w_ihi - a.W + 1 : 0;  // keys >= this: no window cut
   const int w_full_hi = L + w_ilo;                          // keys <= this: no causal cut
+  const int t_begin = __builtin_amdgcn_readfirstlane(wg_kstart / kBK);
+  const int t_end = __builtin_amdgcn_readfirstlane((wg_kend + kBK - 1) / kBK);
+  const int wt0 = wave_has_rows ? w_kstart / kBK : t_end;
+  const int wt1 = wave_has_rows ? (w_kend + kBK - 1) / kBK : t_end;
+
+  const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
+  const uint16_t* kc = a.k_cache + kvbase;
+  const uint16_t* vc = a.v_cache + kvbase;
+
+  // prologue loads: K(t_begin), V(t_begin), K(t_begin + 1)
+  const LoadOffsets lo = load_offsets(wave, lane);
+  tile_load<false>(kc, kvalid, lds_k[0], t_begin * kBK, lo, wave);
+  tile_load<true>(vc, kvalid, lds_v[0], t_begin * kBK, lo, wave);
+  if (t_begin + 1 < t_end) tile_load<false>(kc, kvalid, lds_k[1], (t_begin + 1) * kBK, lo, wave);
 
   // ---- Q^T (B operand): lane holds Q[row][16 ks + 8 c + e] ----
   uint4 qv[8];
@@ -352,10 +385,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     }
   }
 
-  const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
-  const uint16_t* kc = a.k_cache + kvbase;
-  const uint16_t* vc = a.v_cache + kvbase;
-
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -365,30 +394,39 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const float cs = a.scale_log2;
   const int span = my_p - my_ws;
 
-  const int t_begin = wg_kstart / kBK;
-  const int t_end = (wg_kend + kBK - 1) / kBK;
-  Stage st;
-  stage_load(st, kc, vc, t_begin * kBK, kvalid, tid);
-  stage_store(st, lds_k[0], lds_v[0], tid);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = t_begin; t < t_end; ++t) {
+  // one pipeline step; `cur` holds S(t), `next` receives S(t + 1)
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&next)[2]) {
     const int buf = (t - t_begin) & 1;
-    const int tb = t * kBK;
-    const bool more = t + 1 < t_end;
-    if (more) stage_load(st, kc, vc, tb + kBK, kvalid, tid);
-
-    if (wave_has_rows && tb < w_kend && tb + kBK > w_kstart) {
+    // K(t) and V(t - 1) are no longer read by anyone: refill their buffers
+    if (t + 2 < t_end) tile_load<false>(kc, kvalid, lds_k[buf], (t + 2) * kBK, lo, wave);
+    if (t + 1 < t_end) tile_load<true>(vc, kvalid, lds_v[buf ^ 1], (t + 1) * kBK, lo, wave);
+    if (t + 1 >= wt0 && t + 1 < wt1) scores_tile<T>(lds_k[buf ^ 1], qv, next, col, c);
+    if (t >= wt0 && t < wt1) {
+      const int tb = t * kBK;
       const bool full = tb + kBK - 1 <= w_full_hi && tb >= w_full_lo;
       const int lim_hi = my_p - (tb + 4 * c);
+      uint4 pk[4];
       if (full)
-        tile_step<T, false>(lds_k[buf], lds_v[buf], qv, o, rs, cs, lim_hi, span, col, c);
+        softmax_tile<T, false>(cur, rs, o, pk, cs, lim_hi, span);
       else
-        tile_step<T, true>(lds_k[buf], lds_v[buf], qv, o, rs, cs, lim_hi, span, col, c);
+        softmax_tile<T, true>(cur, rs, o, pk, cs, lim_hi, span);
+      pv_tile<T>(lds_v[buf], pk, o, lane);
     }
-    if (more) stage_store(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  f32x16 sa[2], sb[2];
+  if (t_begin >= wt0 && t_begin < wt1) scores_tile<T>(lds_k[0], qv, sa, col, c);
+  int t = t_begin;
+  for (; t + 1 < t_end; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
   }
+  if (t < t_end) step(t, sa, sb);
 
   if (!row_ok) return;
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs.l), __float_as_uint(rs.l),
@@ -410,7 +448,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_fast_supported(const Problem& p) {
-  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16);
+  // buffer ranges are 32-bit byte counts
+  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.M <= (1 << 23);
 }
 
 hipError_t launch_prefill_fast(const Problem& p, hipStream_t st) {
