@@ -4,35 +4,34 @@
 // The key axis of sequence b grows with every step and lives in a buffer of M
 // rows ("KV Cache" discussion, notes): only rows [kstart_b, L'_b] are read.
 //
-// Work layout ("stream-K" at workgroup granularity). A unit is one (sequence
-// b, kv head g, group hg of at most 16 of the query heads that share g). Its
+// Work layout ("stream-K" at wave granularity). A unit is one (sequence b,
+// kv head g, group hg of at most 16 of the query heads that share g). Its
 // valid keys are cut into 16-key blocks; the blocks of all units, in unit
-// order, form one list, and each workgroup of the launch (one per CU, all
-// resident) takes an equal contiguous slice of it, so every workgroup
-// streams the same number of bytes whatever the mix of lengths. Inside a
-// slice the waves of the workgroup take the blocks of each unit segment in
-// turn and combine their results in LDS at the segment's end. A unit the
-// slice holds whole is written out directly; a unit shared with neighbouring
-// slices gets one partial (unnormalised o, m, l) per workgroup, and the last
-// workgroup to bump the unit's counter merges them by log-sum-exp, writes
-// the output and resets the counter for the next call. Shared segments are
-// processed first so those merges happen early, not at the end of the run.
+// order, form one list, and every wave of the launch (a "worker") takes an
+// equal contiguous slice of it and streams it alone, two blocks in flight,
+// with no barrier until its slice is done. So every wave moves the same
+// number of bytes whatever the mix of lengths. A unit a wave holds whole is
+// written out by that wave. A unit cut by a slice boundary leaves one partial
+// (unnormalised o, m, l) per wave in the workgroup's LDS; at the end the
+// workgroup combines the partials of each such unit, writes the output if the
+// unit lies inside the workgroup, and otherwise stores one partial per
+// workgroup; the last workgroup to finish a unit merges those by log-sum-exp
+// and resets the unit's counter for the next call.
 //
 // Per block (16 keys, 8 KiB of K and V), both products on MFMA:
-//  * K and V rows are loaded fully coalesced (4 whole rows per instruction)
-//    while the previous block is computed (two register sets);
-//  * K goes through a per-wave LDS tile into the A layout of MFMA 16x16x32:
-//    S^T = K Q^T, keys as the 16 rows, the unit's query heads as the 16
-//    columns (Q^T stays in registers for the whole unit);
+//  * K rows are loaded straight into the A layout of MFMA 16x16x32: lane
+//    (n, q4) holds key n, dims 32 i + 8 q4 .. + 7 (i = 0..3); S^T = K Q^T with
+//    the unit's query heads as the 16 columns (Q^T stays in registers);
 //  * online softmax per head column in registers; the S^T tile is already
-//    the B operand P^T of the second product, so P never leaves registers;
-//  * V goes through a per-wave LDS tile stored transposed (4 consecutive keys
-//    per 8-byte word), giving the A operand V^T of MFMA 16x16x16:
-//    O^T += V^T P^T, 8 tiles of 16 head dims.
+//    the B operand P^T of the second product;
+//  * V rows go to a per-wave LDS tile as they were loaded (row-major, chunks
+//    XOR-swizzled), and transposing LDS reads (ds_read_b64_tr_b16) hand out
+//    the A operand V^T of MFMA 16x16x16: O^T += V^T P^T, 8 tiles of 16 dims.
 // The block holding the new token (row L'_b) takes that row from k_new/v_new
 // (K rotated under the fp64 rule when rotary is on) instead of the cache and
-// writes it into the cache: the append is fused. Rows past a unit's last key
-// are clamped to a valid row and their V is zeroed, so p = 0 meets 0.
+// writes it into the cache: the append is fused. Rows past the unit's last
+// key are clamped to a valid row; their scores are masked and their V is
+// zeroed, so p = 0 meets 0.
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
@@ -69,11 +68,15 @@ template <> struct Mma<BF16> {
 
 constexpr int kD = 128;
 constexpr int kKeys = 16;                         // keys per block
-constexpr int kKStride = kD + 8;                  // LDS K row stride (halves)
-constexpr int kVStride = kKeys + 4;               // LDS V^T row stride (halves, 40 B)
+constexpr int kVTileBytes = kKeys * kD * 2;       // per-wave V tile, 16 rows x 256 B
 constexpr int kSlotFloats = kDecodeMaxHG * (kD + 2);
 constexpr int kThreads = 64 * kDecodeWaves;
 constexpr int kMergeMax = 64;                  // partials one merge can weigh in LDS
+constexpr int kSlotBytes = kSlotFloats * 4;
+// per wave in LDS: partial slot 0, then an area holding the V tile while
+// streaming and partial slot 1 at the end
+constexpr int kWaveLds = 2 * kSlotBytes;
+constexpr float kRescaleSlack = 8.f;           // binary orders the reference max may lag
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -90,7 +93,7 @@ struct DecodeArgs {
   int B, H, Hkv, G, M, W;
   int rot, rot_rows, interleaved;
   int n_hg, hg_size;
-  int wgs;                              // workgroups in the launch
+  int workers;                          // waves in the launch that take a slice
   int64_t total;                        // T: blocks over all units
   float scale_log2;
   int32_t hl[kDecodeArgBatch];          // past lengths
@@ -138,8 +141,13 @@ __device__ inline Blk locate(const DecodeArgs& a, int64_t x) {
     if (x >= a.pb[b] && x < a.pb[b + 1]) k.b = b;
   const int nb = seq_of(a, k.b).nb;
   const int off = int(x - a.pb[k.b]);
-  k.ub = off / nb;
+  // callers pass x < total; the clamps keep every derived address inside the
+  // caches even if one did not
+  const int units = a.Hkv * a.n_hg;
+  k.ub = nb > 0 ? off / nb : 0;
+  k.ub = k.ub < units ? (k.ub > 0 ? k.ub : 0) : units - 1;
   k.i = off - k.ub * nb;
+  k.i = k.i < nb ? (k.i > 0 ? k.i : 0) : (nb > 0 ? nb - 1 : 0);
   set_unit(k, a);
   return k;
 }
@@ -159,43 +167,57 @@ __device__ inline Blk next_block(const DecodeArgs& a, const Blk& c) {
   return k;
 }
 
-// Rotate a query row held as 4 16-byte chunks, chunk i = dims 32 i + 8 q4 + e:
-// rotate-half pairs (d, d + 64) are chunks (i, i + 2) of the same lane,
-// interleaved pairs are neighbours inside a chunk.
+// Rotation of one lane's four 16-byte chunks of a row (chunk i = dims
+// 32 i + 8 q4 .. + 7), on named values so that no array is formed:
+// rotate-half pairs (d, d + 64) are chunks (0, 2) and (1, 3), element by
+// element; interleaved pairs are neighbours inside a chunk.
 template <class T>
-__device__ inline void rotate_row_chunks(uint4 (&c)[4], int q4, const float* cosr,
-                                         const float* sinr, int interleaved) {
+__device__ inline void rot_word_pair(uint32_t& x, uint32_t& y, int j, const float* cosr,
+                                     const float* sinr) {
   using Bits = typename T::bits;
-  Bits x[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[i][e] = Bits((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-  }
+  Bits x0 = Bits(x & 0xFFFFu), x1 = Bits(x >> 16), y0 = Bits(y & 0xFFFFu), y1 = Bits(y >> 16);
+  rotate_pair<T>(x0, y0, cosr[j], sinr[j]);
+  rotate_pair<T>(x1, y1, cosr[j + 1], sinr[j + 1]);
+  x = uint32_t(x0) | (uint32_t(x1) << 16);
+  y = uint32_t(y0) | (uint32_t(y1) << 16);
+}
+
+template <class T>
+__device__ inline void rot_half_chunks(uint4& a, uint4& b, int j0, const float* cosr,
+                                       const float* sinr) {
+  rot_word_pair<T>(a.x, b.x, j0, cosr, sinr);
+  rot_word_pair<T>(a.y, b.y, j0 + 2, cosr, sinr);
+  rot_word_pair<T>(a.z, b.z, j0 + 4, cosr, sinr);
+  rot_word_pair<T>(a.w, b.w, j0 + 6, cosr, sinr);
+}
+
+template <class T>
+__device__ inline void rot_inter_word(uint32_t& w, int j, const float* cosr, const float* sinr) {
+  using Bits = typename T::bits;
+  Bits x = Bits(w & 0xFFFFu), y = Bits(w >> 16);
+  rotate_pair<T>(x, y, cosr[j], sinr[j]);
+  w = uint32_t(x) | (uint32_t(y) << 16);
+}
+
+template <class T>
+__device__ inline void rot_inter_chunk(uint4& c, int j0, const float* cosr, const float* sinr) {
+  rot_inter_word<T>(c.x, j0, cosr, sinr);
+  rot_inter_word<T>(c.y, j0 + 1, cosr, sinr);
+  rot_inter_word<T>(c.z, j0 + 2, cosr, sinr);
+  rot_inter_word<T>(c.w, j0 + 3, cosr, sinr);
+}
+
+template <class T>
+__device__ inline void rotate4(uint4& c0, uint4& c1, uint4& c2, uint4& c3, int q4,
+                               const float* cosr, const float* sinr, int interleaved) {
   if (!interleaved) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 * i + 8 * q4 + e;
-        rotate_pair<T>(x[i][e], x[i + 2][e], cosr[j], sinr[j]);
-      }
+    rot_half_chunks<T>(c0, c2, 8 * q4, cosr, sinr);          // dims 8 q4 + e with + 64
+    rot_half_chunks<T>(c1, c3, 32 + 8 * q4, cosr, sinr);
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int j = (32 * i + 8 * q4 + e) >> 1;
-        rotate_pair<T>(x[i][e], x[i][e + 1], cosr[j], sinr[j]);
-      }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[i].x = uint32_t(x[i][0]) | (uint32_t(x[i][1]) << 16);
-    c[i].y = uint32_t(x[i][2]) | (uint32_t(x[i][3]) << 16);
-    c[i].z = uint32_t(x[i][4]) | (uint32_t(x[i][5]) << 16);
-    c[i].w = uint32_t(x[i][6]) | (uint32_t(x[i][7]) << 16);
+    rot_inter_chunk<T>(c0, 4 * q4, cosr, sinr);               // pair index (32 i + 8 q4 + e) / 2
+    rot_inter_chunk<T>(c1, 16 + 4 * q4, cosr, sinr);
+    rot_inter_chunk<T>(c2, 32 + 4 * q4, cosr, sinr);
+    rot_inter_chunk<T>(c3, 48 + 4 * q4, cosr, sinr);
   }
 }
 
@@ -205,48 +227,44 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// One block's K and V rows, lane (n, q4) holding dims 8 n .. 8 n + 7 of keys
-// 4 q4 + j (j = 0..3): every load instruction reads 4 whole rows. Named
-// members, passed by value: an indexed array here would end up in memory.
-struct Regs {
+// One block's K and V rows for lane (n, q4): key kb + n (clamped to kb past
+// the unit end), dims 32 i + 8 q4 .. + 7 in member i. Named members passed by
+// value: an indexed array here would end up in memory.
+struct KV {
   uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+};
+
+// Q^T of a unit for lane (n, q4): head n, dims 32 i + 8 q4 .. + 7 in member i.
+struct Q4 {
+  uint4 c0, c1, c2, c3;
 };
 
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ inline Regs load_regs(const DecodeArgs& a, const Blk& k, int n, int q4) {
-  const int key0 = k.kb + 4 * q4;
-  const int row0 = key0 < k.kend ? key0 : k.kb;
-  const int row1 = key0 + 1 < k.kend ? key0 + 1 : k.kb;
-  const int row2 = key0 + 2 < k.kend ? key0 + 2 : k.kb;
-  const int row3 = key0 + 3 < k.kend ? key0 + 3 : k.kb;
-  const uint16_t* kc = k.kc + 8 * n;
-  const uint16_t* vc = k.vc + 8 * n;
-  Regs r;
-  r.k0 = ld16(kc + row0 * kD);
-  r.k1 = ld16(kc + row1 * kD);
-  r.k2 = ld16(kc + row2 * kD);
-  r.k3 = ld16(kc + row3 * kD);
-  r.v0 = ld16(vc + row0 * kD);
-  r.v1 = ld16(vc + row1 * kD);
-  r.v2 = ld16(vc + row2 * kD);
-  r.v3 = ld16(vc + row3 * kD);
+__device__ inline KV load_kv(const Blk& k, int n, int q4) {
+  const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
+  const uint16_t* kp = k.kc + int64_t(row) * kD + 8 * q4;
+  const uint16_t* vp = k.vc + int64_t(row) * kD + 8 * q4;
+  KV r;
+  r.k0 = ld16(kp); r.k1 = ld16(kp + 32); r.k2 = ld16(kp + 64); r.k3 = ld16(kp + 96);
+  r.v0 = ld16(vp); r.v1 = ld16(vp + 32); r.v2 = ld16(vp + 64); r.v3 = ld16(vp + 96);
   return r;
 }
 
-// 16-bit element e of a 16-byte register group
-__device__ inline uint32_t h16(const uint4& u, int e) {
-  const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
+// V tile: row r holds key kb + r; its 16-byte chunk c sits at chunk
+// c ^ 2 (r & 7), so that the 32 lanes of a transposing read (8 rows x 2
+// chunks) hit distinct banks.
+__device__ inline int vchunk(int row, int c) { return c ^ ((row & 7) << 1); }
 
 struct Acc {
-  float m, l;          // running max (per head column) and this lane's partial sum
+  float m_run, m_use;  // running max of the head column (log2 units) and the reference in the exponent
+  float l;             // this lane's partial sum of the packed weights
   f32x4 o[8];          // O^T[16 dt + 4 q4 + r][head n]
 };
 
 __device__ inline void acc_reset(Acc& s) {
-  s.m = -INFINITY;
+  s.m_run = -INFINITY;
+  s.m_use = 0.f;
   s.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) s.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -257,73 +275,53 @@ __device__ inline uint32_t pack2(float x, float y) {
   return uint32_t(T::from_float(x)) | (uint32_t(T::from_float(y)) << 16);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <class T>
-__device__ inline void compute(Acc& s, Regs r, const uint4 (&qv)[4], const Blk& k,
-                               const DecodeArgs& a, int lane, uint16_t* klds, uint16_t* vlds) {
-  using Bits = typename T::bits;
+__device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
+                               const DecodeArgs& a, int lane, unsigned char* vt) {
   const int n = lane & 15, q4 = lane >> 4;
-  // ---- K rows into the LDS tile (row-major), V rows transposed ----
-  if (k.kb + kKeys > k.kend) {
-    // last block of the unit: rows past its end are clamped copies of row kb,
-    // which may be the unwritten new-token row; zero their V so that p = 0
-    // meets 0, not NaN, in the product
-    const int key0 = k.kb + 4 * q4;
+  if (k.kb + kKeys > k.kend && k.kb + n >= k.kend) {
+    // past the unit end: the clamped row may be the unwritten new-token row
     const uint4 z = make_uint4(0, 0, 0, 0);
-    if (key0 >= k.kend) r.v0 = z;
-    if (key0 + 1 >= k.kend) r.v1 = z;
-    if (key0 + 2 >= k.kend) r.v2 = z;
-    if (key0 + 3 >= k.kend) r.v3 = z;
+    r.v0 = z; r.v1 = z; r.v2 = z; r.v3 = z;
   }
-  {
-    uint16_t* kt = klds + 4 * q4 * kKStride + 8 * n;
-    *reinterpret_cast<uint4*>(kt) = r.k0;
-    *reinterpret_cast<uint4*>(kt + kKStride) = r.k1;
-    *reinterpret_cast<uint4*>(kt + 2 * kKStride) = r.k2;
-    *reinterpret_cast<uint4*>(kt + 3 * kKStride) = r.k3;
-    uint16_t* vt = vlds + 8 * n * kVStride + 4 * q4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 w;
-      w.x = h16(r.v0, e) | (h16(r.v1, e) << 16);
-      w.y = h16(r.v2, e) | (h16(r.v3, e) << 16);
-      *reinterpret_cast<uint2*>(vt + e * kVStride) = w;
-    }
-  }
-  if (k.Lp >= k.kb && k.Lp < k.kb + kKeys) {
-    // The new token: its K row (rotated from k_new) and V row (from v_new)
-    // replace the tile rows and go into the cache. Every head group of the
-    // kv head writes the same bytes.
-    const int t = k.Lp - k.kb;
-    const int64_t kvrow = (int64_t(k.b) * a.Hkv + k.g) * kD;
-    const Bits* knew = reinterpret_cast<const Bits*>(a.k_new) + kvrow;
-    const Bits* vnew = reinterpret_cast<const Bits*>(a.v_new) + kvrow;
-    const int64_t crow = ((int64_t(k.b) * a.Hkv + k.g) * a.M + k.Lp) * kD;
-    const int e1 = a.interleaved ? 2 * lane : lane;
-    const int e2 = a.interleaved ? 2 * lane + 1 : lane + kD / 2;
-    Bits x = knew[e1], y = knew[e2];
+  if (k.Lp >= k.kb && k.Lp < k.kb + kKeys && n == k.Lp - k.kb) {
+    // the new token: its K row (rotated from k_new) and V row (from v_new)
+    // replace the loaded ones and go into the cache; the head group 0 unit of
+    // the kv head writes them
+    const int64_t kvrow = (int64_t(k.b) * a.Hkv + k.g) * kD + 8 * q4;
+    const uint16_t* kn = a.k_new + kvrow;
+    const uint16_t* vn = a.v_new + kvrow;
+    r.k0 = ld16(kn); r.k1 = ld16(kn + 32); r.k2 = ld16(kn + 64); r.k3 = ld16(kn + 96);
     if (a.rot) {
       const int pos = clamp_len(clamp_len(a.hl[k.b], 0, a.M), 0, a.rot_rows - 1);
-      rotate_pair<T>(x, y, a.cosv[int64_t(pos) * (kD / 2) + lane],
-                     a.sinv[int64_t(pos) * (kD / 2) + lane]);
+      rotate4<T>(r.k0, r.k1, r.k2, r.k3, q4, a.cosv + int64_t(pos) * (kD / 2),
+                 a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
     }
-    Bits* trow = reinterpret_cast<Bits*>(klds + t * kKStride);
-    trow[e1] = x;
-    trow[e2] = y;
-    reinterpret_cast<Bits*>(a.k_cache)[crow + e1] = x;
-    reinterpret_cast<Bits*>(a.k_cache)[crow + e2] = y;
-    const Bits v1 = vnew[lane], v2 = vnew[lane + 64];
-    reinterpret_cast<Bits*>(vlds)[lane * kVStride + t] = v1;
-    reinterpret_cast<Bits*>(vlds)[(lane + 64) * kVStride + t] = v2;
-    reinterpret_cast<Bits*>(a.v_cache)[crow + lane] = v1;
-    reinterpret_cast<Bits*>(a.v_cache)[crow + lane + 64] = v2;
+    r.v0 = ld16(vn); r.v1 = ld16(vn + 32); r.v2 = ld16(vn + 64); r.v3 = ld16(vn + 96);
+    if (k.ub % a.n_hg == 0) {
+      const int64_t crow = ((int64_t(k.b) * a.Hkv + k.g) * a.M + k.Lp) * kD + 8 * q4;
+      uint4* kc = reinterpret_cast<uint4*>(a.k_cache + crow);
+      uint4* vc = reinterpret_cast<uint4*>(a.v_cache + crow);
+      kc[0] = r.k0; kc[4] = r.k1; kc[8] = r.k2; kc[12] = r.k3;
+      vc[0] = r.v0; vc[4] = r.v1; vc[8] = r.v2; vc[12] = r.v3;
+    }
   }
-  wave_lds_sync();
-  // ---- S^T = K Q^T: lane gets keys 4 q4 + r of head column n ----
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    acc = Mma<T>::qk(*reinterpret_cast<const uint4*>(klds + n * kKStride + 32 * i + 8 * q4),
-                     qv[i], acc);
+  // ---- V rows into the tile ----
+  {
+    unsigned char* row = vt + n * 256;
+    *reinterpret_cast<uint4*>(row + 16 * vchunk(n, q4)) = r.v0;
+    *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 4 + q4)) = r.v1;
+    *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 8 + q4)) = r.v2;
+    *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 12 + q4)) = r.v3;
+  }
+  // ---- S^T = K Q^T: lane gets keys 4 q4 + rr of head column n ----
+  f32x4 acc = Mma<T>::qk(r.k0, qv.c0, f32x4{0.f, 0.f, 0.f, 0.f});
+  acc = Mma<T>::qk(r.k1, qv.c1, acc);
+  acc = Mma<T>::qk(r.k2, qv.c2, acc);
+  acc = Mma<T>::qk(r.k3, qv.c3, acc);
   float sv[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr)
@@ -331,58 +329,51 @@ __device__ inline void compute(Acc& s, Regs r, const uint4 (&qv)[4], const Blk& 
   float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  if (__any(bm > s.m)) {               // rescale only when some head's max grows
-    const float mn = fmaxf(s.m, bm);
-    const float alpha = exp2f(s.m - mn);
+  if (__any(bm > s.m_run + kRescaleSlack)) {
+    const float mn = fmaxf(s.m_run, bm);
+    const float use = mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2f(s.m_use - use);
     s.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) s.o[dt] *= alpha;
-    s.m = mn;
+    s.m_run = mn;
+    s.m_use = use;
   }
   float p[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    p[rr] = exp2f(sv[rr] - s.m);
-    s.l += p[rr];
-  }
+  for (int rr = 0; rr < 4; ++rr) p[rr] = exp2f(sv[rr] - s.m_use);
   uint2 pb;                            // P^T: keys 4 q4 .. 4 q4 + 3 of head n
   pb.x = pack2<T>(p[0], p[1]);
   pb.y = pack2<T>(p[2], p[3]);
-  // ---- O^T += V^T P^T: A = V^T rows 16 dt + n, keys 4 q4 .. 4 q4 + 3 ----
+  // the row sum uses the weights as rounded for the product
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    s.o[dt] = Mma<T>::pv(*reinterpret_cast<const uint2*>(vlds + (16 * dt + n) * kVStride + 4 * q4),
-                         pb, s.o[dt]);
-  wave_lds_sync();   // the next block rewrites the tiles
-}
-
-// Q^T of one unit as the MFMA B operand: lane (n, q4) holds head n's dims
-// 32 i + 8 q4 .. (zeros for padding heads), rotated at position L_b.
-template <class T>
-__device__ inline void load_q(uint4 (&qv)[4], const DecodeArgs& a, const Blk& k, int lane) {
-  const int n = lane & 15, q4 = lane >> 4;
-  const int hg = k.ub % a.n_hg;
-  const int h0 = k.g * a.G + hg * a.hg_size;
-  const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
-  const uint16_t* qrow = a.q + (int64_t(k.b) * a.H + h0 + n) * kD + 8 * q4;
+  for (int rr = 0; rr < 4; ++rr)
+    s.l += T::to_float(typename T::bits(((rr < 2 ? pb.x : pb.y) >> (16 * (rr & 1))) & 0xFFFFu));
+  wave_lds_sync();
+  // ---- O^T += V^T P^T: transposing reads give lane (n, q4) dim 16 dt + n of
+  // keys 4 q4 .. 4 q4 + 3 (in each 16-lane group, lane j points at key
+  // 4 q4 + j / 4, dims 16 dt + 4 (j % 4) .. + 3) ----
+  const int trow = 4 * q4 + (n >> 2);
+  const unsigned char* tbase = vt + trow * 256 + 8 * ((n & 3) & 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    qv[i] = n < nheads ? ld16(qrow + 32 * i) : make_uint4(0, 0, 0, 0);
-  if (a.rot && n < nheads) {
-    const int pos = clamp_len(clamp_len(a.hl[k.b], 0, a.M), 0, a.rot_rows - 1);
-    rotate_row_chunks<T>(qv, q4, a.cosv + int64_t(pos) * (kD / 2),
-                         a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
+  for (int dt = 0; dt < 8; ++dt) {
+    const int c = 2 * dt + ((n & 3) >> 1);
+    const s16x4 x =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tbase + 16 * vchunk(trow, c)));
+    s.o[dt] = Mma<T>::pv(__builtin_bit_cast(uint2, x), pb, s.o[dt]);
   }
+  wave_lds_sync();   // the next block rewrites the tile
 }
 
-// The workgroup that owns global block x (slices [w T / N, (w + 1) T / N)).
-__device__ inline int owner_wg(const DecodeArgs& a, int64_t x) {
-  return int(((x + 1) * a.wgs - 1) / a.total);
+// The worker (wave of the launch) that owns global block x: worker w takes
+// the slice [w T / N, (w + 1) T / N).
+__device__ inline int owner_worker(const DecodeArgs& a, int64_t x) {
+  return int(((x + 1) * a.workers - 1) / a.total);
 }
 
-// Unit index and the workgroups sharing it.
+// Unit index, its heads and the workers sharing it.
 struct UnitInfo {
-  int unit, h0, nheads, wg_first, wg_last;
+  int unit, h0, nheads, w_first, w_last;
 };
 
 __device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub) {
@@ -393,8 +384,8 @@ __device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub) {
   u.unit = b * a.Hkv * a.n_hg + ub;
   const int nb = seq_of(a, b).nb;
   const int64_t x0 = a.pb[b] + int64_t(ub) * nb;
-  u.wg_first = owner_wg(a, x0);
-  u.wg_last = owner_wg(a, x0 + nb - 1);
+  u.w_first = owner_worker(a, x0);
+  u.w_last = owner_worker(a, x0 + nb - 1);
   return u;
 }
 
@@ -403,24 +394,126 @@ __device__ inline void store_out(const DecodeArgs& a, int b, int h, int d, float
   reinterpret_cast<typename T::bits*>(a.out)[(int64_t(b) * a.H + h) * kD + d] = T::from_float(v);
 }
 
-// Merge the partials of a shared unit (one per workgroup wg_first..wg_last),
-// write the output and reset the counter. All threads load at once.
+__device__ inline float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// End of one unit segment of this wave: normalise and write the output (the
+// wave saw the whole unit) or put the unnormalised partial (o, m, l) into the
+// wave's LDS slot. Lane (n, q4) holds head column n, dims 16 dt + 4 q4 + r.
+template <class T>
+__device__ inline void finish_segment(const DecodeArgs& a, const Acc& s, const Blk& k, bool shared,
+                                      float* slot, int lane) {
+  const int n = lane & 15, q4 = lane >> 4;
+  float l = s.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  const int hg = k.ub % a.n_hg;
+  const int h0 = k.g * a.G + hg * a.hg_size;
+  const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
+  if (n >= nheads) return;
+  if (!shared) {
+    const float inv = 1.f / l;
+    using Bits = typename T::bits;
+    Bits* orow = reinterpret_cast<Bits*>(a.out) + (int64_t(k.b) * a.H + h0 + n) * kD + 4 * q4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 w;
+      w.x = pack2<T>(s.o[dt][0] * inv, s.o[dt][1] * inv);
+      w.y = pack2<T>(s.o[dt][2] * inv, s.o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<f32x4*>(slot + n * kD + 16 * dt + 4 * q4) = s.o[dt];
+  if (q4 == 0) {
+    slot[kDecodeMaxHG * kD + n] = s.m_use;
+    slot[kDecodeMaxHG * kD + kDecodeMaxHG + n] = l;
+  }
+}
+
+// Raw Q rows of block k's unit: lane (n, q4) holds head n's dims 32 i + 8 q4.
+__device__ inline Q4 load_q_raw(const DecodeArgs& a, const Blk& k, int lane) {
+  const int n = lane & 15, q4 = lane >> 4;
+  const int hg = k.ub % a.n_hg;
+  const int h0 = k.g * a.G + hg * a.hg_size;
+  const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
+  const uint16_t* qrow = a.q + (int64_t(k.b) * a.H + h0 + (n < nheads ? n : 0)) * kD + 8 * q4;
+  Q4 q;
+  q.c0 = ld16(qrow); q.c1 = ld16(qrow + 32); q.c2 = ld16(qrow + 64); q.c3 = ld16(qrow + 96);
+  return q;
+}
+
+__device__ inline uint4 mask4(uint4 c, uint32_t m) {
+  return make_uint4(c.x & m, c.y & m, c.z & m, c.w & m);
+}
+
+// Rotate Q at position L_b and zero the padding heads (a mask, no select of
+// aggregates: the rows stay in registers).
+template <class T>
+__device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, int lane) {
+  const int n = lane & 15, q4 = lane >> 4;
+  const int hg = k.ub % a.n_hg;
+  const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
+  if (a.rot) {
+    const int pos = clamp_len(clamp_len(a.hl[k.b], 0, a.M), 0, a.rot_rows - 1);
+    rotate4<T>(q.c0, q.c1, q.c2, q.c3, q4, a.cosv + int64_t(pos) * (kD / 2),
+               a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
+  }
+  const uint32_t keep = n < nheads ? 0xFFFFFFFFu : 0u;
+  q.c0 = mask4(q.c0, keep); q.c1 = mask4(q.c1, keep);
+  q.c2 = mask4(q.c2, keep); q.c3 = mask4(q.c3, keep);
+  return q;
+}
+
+// Merge the workgroup partials of a unit (slots wg_first + unit .. wg_last +
+// unit) by log-sum-exp, write the output and reset the unit's counter. All
+// threads of the workgroup; `lds` holds 2 kMergeMax x 16 floats.
 template <class T>
 __device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds) {
   const int tid = threadIdx.x;
   const UnitInfo u = unit_info(a, b, ub);
-  const int count = u.wg_last - u.wg_first + 1;
-  auto ld = [](const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  const float* base = a.partials + int64_t(u.wg_first + u.unit) * kSlotFloats;
+  const int wg_first = u.w_first / kDecodeWaves, wg_last = u.w_last / kDecodeWaves;
+  const int count = wg_last - wg_first + 1;
+  const float* base = a.partials + int64_t(wg_first + u.unit) * kSlotFloats;
+  if (count <= 4) {
+    // usual case: every thread loads m, l and o of all partials for its
+    // output at once (one memory round trip), no LDS pass
+    for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
+      const int h = idx / kD, d = idx % kD;
+      float m[4], l[4], o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* sl = base + int64_t(j < count ? j : 0) * kSlotFloats;
+        m[j] = ld_agent(sl + kDecodeMaxHG * kD + h);
+        l[j] = ld_agent(sl + kDecodeMaxHG * kD + kDecodeMaxHG + h);
+        o[j] = ld_agent(sl + h * kD + d);
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) M = j < count ? fmaxf(M, m[j]) : M;
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = j < count ? __builtin_amdgcn_exp2f(m[j] - M) : 0.f;
+        L = fmaf(l[j], w, L);
+        O = fmaf(o[j], w, O);
+      }
+      store_out<T>(a, b, u.h0 + h, d, O / L);
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.counters + u.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   float* wm = lds;                                   // [count][16] -> weights
   float* wl = lds + kMergeMax * 16;                  // [count][16]
   for (int idx = tid; idx < count * 16; idx += kThreads) {
     const int j = idx >> 4, h = idx & 15;
     const float* sl = base + int64_t(j) * kSlotFloats;
-    wm[idx] = h < u.nheads ? ld(sl + kDecodeMaxHG * kD + h) : 0.f;
-    wl[idx] = h < u.nheads ? ld(sl + kDecodeMaxHG * kD + kDecodeMaxHG + h) : 0.f;
+    wm[idx] = h < u.nheads ? ld_agent(sl + kDecodeMaxHG * kD + h) : 0.f;
+    wl[idx] = h < u.nheads ? ld_agent(sl + kDecodeMaxHG * kD + kDecodeMaxHG + h) : 0.f;
   }
   __syncthreads();
   if (tid < u.nheads) {
@@ -443,7 +536,7 @@ __device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        x[j] = j0 + j < count ? ld(base + int64_t(j0 + j) * kSlotFloats + h * kD + d) : 0.f;
+        x[j] = j0 + j < count ? ld_agent(base + int64_t(j0 + j) * kSlotFloats + h * kD + d) : 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (j0 + j < count) acc = fmaf(x[j], wm[(j0 + j) * 16 + h], acc);
@@ -454,193 +547,152 @@ __device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds
   if (tid == 0) __hip_atomic_store(a.counters + u.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A segment: the blocks [start, end) of one unit inside a workgroup's slice.
-struct Seg {
-  Blk first;                 // block `start`
-  int64_t start, end;
-  bool shared;               // the unit has blocks outside the slice
-};
-
-// Block `off` blocks after `k` within the same unit.
-__device__ inline Blk advance_in_unit(Blk k, int off) {
-  k.i += off;
-  k.kb += kKeys * off;
-  return k;
-}
-
-// Segments of slice [S, E), in processing order: the shared ones first (the
-// unit running past the slice end, then the one starting before it), so
-// every shared unit is complete early and its merge overlaps the streaming
-// of the units the slice owns whole, which follow in order.
-struct SegPlan {
-  int64_t S, E;
-  Blk fb, lb;                // first block of the slice, first block of the last segment
-  int64_t f_end, l_start;
-  bool single, first_shared, last_shared;
-  int64_t own_s, own_e;      // owned range (whole units)
-};
-
-__device__ inline SegPlan make_plan(const DecodeArgs& a, int64_t S, int64_t E) {
-  SegPlan p;
-  p.S = S; p.E = E;
-  p.fb = locate(a, S);
-  const int64_t f_unit_end = S - p.fb.i + p.fb.nb;
-  p.f_end = f_unit_end < E ? f_unit_end : E;
-  p.single = p.f_end == E;
-  p.first_shared = p.fb.i > 0 || f_unit_end > E;
-  const Blk eb = locate(a, E - 1);
-  p.l_start = (E - 1) - eb.i;
-  if (p.l_start < S) p.l_start = S;
-  p.lb = advance_in_unit(eb, -int((E - 1) - p.l_start));
-  p.last_shared = !p.single && ((E - 1) - eb.i + eb.nb > E);
-  p.own_s = p.first_shared ? p.f_end : S;
-  p.own_e = (p.last_shared && !p.single) ? p.l_start : E;
-  if (p.own_e < p.own_s) p.own_e = p.own_s;
-  return p;
-}
-
-// One segment: this wave's blocks seg.start + wv, + 4, ... with two register
-// sets in turn, then the 4 waves combine in LDS and either write the output
-// (owned unit) or the workgroup's partial (shared unit).
-template <class T>
-__device__ inline void run_segment(const DecodeArgs& a, const Seg& sg, uint16_t* ktile,
-                                   uint16_t* vtile, float* comb, int wg) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = lane & 15, q4 = lane >> 4;
-  const int nseg = int(sg.end - sg.start);
-  Acc s;
-  acc_reset(s);
-  if (wv < nseg) {
-    Blk cur = advance_in_unit(sg.first, wv);
-    Regs rc = load_regs(a, cur, n, q4);
-    uint4 qv[4];
-    load_q<T>(qv, a, sg.first, lane);
-    for (int j = wv;;) {
-      const int jn = j + kDecodeWaves;
-      Blk nb = jn < nseg ? advance_in_unit(cur, kDecodeWaves) : cur;
-      Regs rn = load_regs(a, nb, n, q4);
-      compute<T>(s, rc, qv, cur, a, lane, ktile, vtile);
-      if (jn >= nseg) break;
-      cur = nb;
-      j = jn;
-      const int jn2 = j + kDecodeWaves;
-      nb = jn2 < nseg ? advance_in_unit(cur, kDecodeWaves) : cur;
-      rc = load_regs(a, nb, n, q4);
-      compute<T>(s, rn, qv, cur, a, lane, ktile, vtile);
-      if (jn2 >= nseg) break;
-      cur = nb;
-      j = jn2;
-    }
-  }
-  // ---- combine the 4 waves in LDS: per wave m[16], l[16], o[16][128] ----
-  float l = s.l;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  __syncthreads();                                  // tiles are free now
-  const UnitInfo u = unit_info(a, sg.first.b, sg.first.ub);
-  float* cw = comb + wv * (32 + 16 * kD);
-  if (q4 == 0) { cw[n] = s.m; cw[16 + n] = l; }
-  if (n < u.nheads) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<f32x4*>(cw + 32 + n * kD + 16 * dt + 4 * q4) = s.o[dt];
-  }
-  __syncthreads();
-  float* slot = a.partials + int64_t(wg + u.unit) * kSlotFloats;
-  for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
-    const int h = idx / kD, d = idx % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w)
-      if (w < nseg) M = fmaxf(M, comb[w * (32 + 16 * kD) + h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      if (w >= nseg) continue;                      // waves with no block in the segment
-      const float* c = comb + w * (32 + 16 * kD);
-      const float wgt = exp2f(c[h] - M);
-      L = fmaf(c[16 + h], wgt, L);
-      O = fmaf(c[32 + h * kD + d], wgt, O);
-    }
-    if (!sg.shared) {
-      store_out<T>(a, sg.first.b, u.h0 + h, d, O / L);
-    } else {
-      __hip_atomic_store(slot + h * kD + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (d == 0) {
-        __hip_atomic_store(slot + kDecodeMaxHG * kD + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(slot + kDecodeMaxHG * kD + kDecodeMaxHG + h, L, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  __syncthreads();                                  // the combine area is read
-}
-
+// One launch: workgroups of kDecodeWaves waves; every wave of the grid
+// streams its own slice (see the top of the file), then the workgroup
+// combines the partials its waves left.
 template <class T>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
-  // per-wave K and V^T tiles in one allocation, reused as the combine /
-  // merge area between segments
-  constexpr int kTileHalves = kKeys * kKStride + kD * kVStride;
-  static_assert(kDecodeWaves * kTileHalves * 2 >= kDecodeWaves * (32 + 16 * kD) * 4, "combine area");
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[kDecodeWaves * kTileHalves];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
+  __shared__ int sh_tab[kDecodeWaves][2][2];        // per wave, slot: (b, ub) or b = -1
   __shared__ int sh_flag[2];
-  float* comb = reinterpret_cast<float*>(tiles);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, q4 = lane >> 4;
   const int wg = blockIdx.x;
-  const int64_t S = (int64_t(wg) * a.total) / a.wgs;
-  const int64_t E = (int64_t(wg + 1) * a.total) / a.wgs;
-  if (S >= E) return;
-  uint16_t* ktile = tiles + wv * kTileHalves;
-  uint16_t* vtile = ktile + kKeys * kKStride;
-  const SegPlan plan = make_plan(a, S, E);
+  const int worker = wg * kDecodeWaves + wv;
+  float* slot0 = reinterpret_cast<float*>(lds + wv * kWaveLds);
+  float* slot1 = reinterpret_cast<float*>(lds + wv * kWaveLds + kSlotBytes);
+  unsigned char* vt = lds + wv * kWaveLds + kSlotBytes;     // the V tile while streaming
+  if (lane < 4) sh_tab[wv][lane >> 1][lane & 1] = -1;
 
-  // ---- phase A: the shared segments (unit past the slice end, then the
-  // unit begun before it), so that the merges they feed happen early ----
-  const bool do_last = plan.last_shared && !plan.single;
-  Seg shs[2];
-  int nsh = 0;
-  if (do_last) { shs[0].first = plan.lb; shs[0].start = plan.l_start; shs[0].end = E; shs[0].shared = true; nsh = 1; }
-  if (plan.first_shared) {
-    Seg& f = nsh ? shs[1] : shs[0];
-    f.first = plan.fb; f.start = S; f.end = plan.f_end; f.shared = true;
-    ++nsh;
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    if (k >= nsh) break;
-    run_segment<T>(a, shs[k], ktile, vtile, comb, wg);
-  }
-  if (nsh) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // partial stores have landed
-    __syncthreads();
-    if (tid < nsh) {
-      const Seg& sg = tid ? shs[1] : shs[0];
-      const UnitInfo u = unit_info(a, sg.first.b, sg.first.ub);
-      const int prev = __hip_atomic_fetch_add(a.counters + u.unit, 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-      sh_flag[tid] = prev == u.wg_last - u.wg_first;
+  const int64_t S = worker < a.workers ? (int64_t(worker) * a.total) / a.workers : 0;
+  const int64_t E = worker < a.workers ? (int64_t(worker + 1) * a.total) / a.workers : 0;
+  if (S < E) {
+    Blk cur = locate(a, S);
+    Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
+    KV rc = load_kv(cur, n, q4);
+    Acc s;
+    acc_reset(s);
+    bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
+
+    // Blocks move through three register sets: while block x is computed,
+    // x + 1 and x + 2 are in flight. `ahead` is the block whose loads go out
+    // next (x + 2), clamped to the slice's last block. Q rows are loaded when
+    // their unit starts (a small, cache-resident read).
+    Blk nxt = S + 1 < E ? next_block(a, cur) : cur;        // block x + 1
+    KV r1 = load_kv(nxt, n, q4);
+    Blk ahead = S + 2 < E ? next_block(a, nxt) : nxt;       // block x + 2
+
+    // one block: issue the loads of x + 2, compute x, close the segment at a
+    // unit end or at the slice end. Returns false after the slice's last block.
+    auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
+      const bool last = x + 1 >= E;
+      const bool unit_end = cur.i + 1 >= cur.nb;
+      r_fill = load_kv(ahead, n, q4);
+      compute<T>(s, r_cur, qv, cur, a, lane, vt);
+      if (unit_end || last) {
+        const bool shared = seg_shared || !unit_end;
+        if (shared) {
+          // the slice's last segment goes to slot 1 (over the V tile, free now)
+          finish_segment<T>(a, s, cur, true, last ? slot1 : slot0, lane);
+          if (lane == 0) {
+            sh_tab[wv][last ? 1 : 0][0] = cur.b;
+            sh_tab[wv][last ? 1 : 0][1] = cur.ub;
+          }
+        } else {
+          finish_segment<T>(a, s, cur, false, slot0, lane);
+        }
+        if (last) return false;
+        acc_reset(s);
+        seg_shared = false;
+        qv = finish_q<T>(load_q_raw(a, nxt, lane), a, nxt, lane);
+      }
+      cur = nxt;
+      nxt = ahead;
+      ahead = x + 3 < E ? next_block(a, ahead) : ahead;
+      return true;
+    };
+    KV r2;
+    for (int64_t x = S;; x += 3) {
+      if (!step(x, rc, r2)) break;
+      if (!step(x + 1, r1, rc)) break;
+      if (!step(x + 2, r2, r1)) break;
     }
-    __syncthreads();
-    if (sh_flag[0]) merge_unit<T>(a, shs[0].first.b, shs[0].first.ub, comb);
-    if (nsh > 1 && sh_flag[1]) merge_unit<T>(a, shs[1].first.b, shs[1].first.ub, comb);
   }
+  __syncthreads();
 
-  // ---- phase B: the units the slice owns whole, in order ----
-  if (plan.own_s >= plan.own_e) return;
-  Seg cur;
-  cur.first = plan.first_shared ? locate(a, plan.own_s) : plan.fb;
-  cur.start = plan.own_s;
-  cur.shared = false;
-  for (;;) {
-    const int64_t ue = cur.start - cur.first.i + cur.first.nb;
-    cur.end = ue < plan.own_e ? ue : plan.own_e;
-    run_segment<T>(a, cur, ktile, vtile, comb, wg);
-    if (cur.end >= plan.own_e) break;
-    cur.first = next_block(a, advance_in_unit(cur.first, int(cur.end - 1 - cur.start)));
-    cur.start = cur.end;
+  // ---- combine the partials of each cut unit in slice order. The table
+  // is read once (one LDS round trip); entries of a unit are consecutive in
+  // slice order (empty entries between them are skipped). ----
+  int tb[2 * kDecodeWaves], tu[2 * kDecodeWaves];
+#pragma unroll
+  for (int f = 0; f < 2 * kDecodeWaves; ++f) {
+    tb[f] = sh_tab[f >> 1][f & 1][0];
+    tu[f] = sh_tab[f >> 1][f & 1][1];
   }
+  int nglob = 0, gb0 = 0, gub0 = 0, gb1 = 0, gub1 = 0;
+  int prev_b = -1, prev_ub = -1;
+#pragma unroll
+  for (int e = 0; e < 2 * kDecodeWaves; ++e) {
+    const int b = tb[e], ub = tu[e];
+    if (b < 0 || (b == prev_b && ub == prev_ub)) continue;   // empty, or not a unit's first entry
+    prev_b = b; prev_ub = ub;
+    const UnitInfo u = unit_info(a, b, ub);
+    const bool inside = u.w_first >= wg * kDecodeWaves && u.w_last < (wg + 1) * kDecodeWaves;
+    float* gslot = a.partials + int64_t(wg + u.unit) * kSlotFloats;
+    for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
+      const int h = idx / kD, d = idx % kD;
+      // every entry of this unit: its m, l and o, loaded together
+      float m[2 * kDecodeWaves], l[2 * kDecodeWaves], o[2 * kDecodeWaves];
+#pragma unroll
+      for (int f = 0; f < 2 * kDecodeWaves; ++f) {
+        const bool mine = f >= e && tb[f] == b && tu[f] == ub;
+        const float* sl = reinterpret_cast<const float*>(lds + (f >> 1) * kWaveLds + (f & 1) * kSlotBytes);
+        m[f] = mine ? sl[kDecodeMaxHG * kD + h] : -INFINITY;
+        l[f] = mine ? sl[kDecodeMaxHG * kD + kDecodeMaxHG + h] : 0.f;
+        o[f] = mine ? sl[h * kD + d] : 0.f;
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int f = 0; f < 2 * kDecodeWaves; ++f) M = fmaxf(M, m[f]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int f = 0; f < 2 * kDecodeWaves; ++f) {
+        const float wgt = __builtin_amdgcn_exp2f(m[f] - M);     // 0 for the others
+        L = fmaf(l[f], wgt, L);
+        O = fmaf(o[f], wgt, O);
+      }
+      if (inside) {
+        store_out<T>(a, b, u.h0 + h, d, O / L);
+      } else {
+        __hip_atomic_store(gslot + h * kD + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(gslot + kDecodeMaxHG * kD + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(gslot + kDecodeMaxHG * kD + kDecodeMaxHG + h, L, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (!inside) {
+      if (nglob == 0) { gb0 = b; gub0 = ub; } else { gb1 = b; gub1 = ub; }
+      ++nglob;
+    }
+  }
+  if (nglob == 0) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial stores have landed
+  __syncthreads();
+  if (tid < nglob) {
+    const int b = tid ? gb1 : gb0, ub = tid ? gub1 : gub0;
+    const UnitInfo u = unit_info(a, b, ub);
+    const int prev = __hip_atomic_fetch_add(a.counters + u.unit, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    sh_flag[tid] = prev == u.w_last / kDecodeWaves - u.w_first / kDecodeWaves;
+  }
+  __syncthreads();
+  float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
+  if (sh_flag[0]) merge_unit<T>(a, gb0, gub0, mlds);
+  if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds);
 }
 
 }  // namespace
@@ -680,17 +732,17 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.pb[p.B] = int32_t(total);
   a.total = total;
   if (total == 0) return hipSuccess;
-  // workgroups: all resident at once, and no unit shared by more than
-  // kMergeMax of them
-  int64_t wgs = kDecodeMaxWorkgroups < total ? kDecodeMaxWorkgroups : total;
+  // workers (waves): at most one workgroup per CU, and no unit shared by
+  // more than kMergeMax of them
+  int64_t workers = kDecodeMaxWorkers < total ? kDecodeMaxWorkers : total;
   int64_t max_unit = 0;
   for (int b = 0; b < p.B; ++b) {
     const int64_t nb = p.B ? (a.pb[b + 1] - a.pb[b]) / units_per_seq : 0;
     max_unit = nb > max_unit ? nb : max_unit;
   }
-  while (wgs > 1 && max_unit * wgs > int64_t(kMergeMax - 1) * total) wgs /= 2;
-  a.wgs = int(wgs);
-  const int blocks = a.wgs;
+  while (workers > 1 && max_unit * workers > int64_t(kMergeMax - 1) * total) workers /= 2;
+  a.workers = int(workers);
+  const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
   if (p.dtype == GQA_FP16)
     hipLaunchKernelGGL(decode_kernel<F16>, dim3(blocks), dim3(kThreads), 0, st, a);
   else

@@ -52,6 +52,7 @@ constexpr int kDecodeWaves = GQA_DECODE_WG_WAVES;  // waves per workgroup
 #define GQA_DECODE_WORKGROUPS 256
 #endif
 constexpr int kDecodeMaxWorkgroups = GQA_DECODE_WORKGROUPS;  // per launch: one per CU, all resident
+constexpr int kDecodeMaxWorkers = kDecodeMaxWorkgroups * kDecodeWaves;  // waves taking a slice
 constexpr int kDecodeMaxHG = 16;         // query heads per unit (the 16 MFMA columns)
 constexpr int kDecodeArgBatch = 64;      // largest batch the fast decode plans in its arguments
 
