@@ -4,13 +4,15 @@
 // this is a memmove towards lower rows.
 //
 // Parallel form (d <= kEvictHaloMax): the destination range is cut into
-// chunks of C rows, one workgroup each. Chunk k reads source rows
-// [kC + d, (k+1)C + d); the last d of those are the first d rows chunk k+1
-// overwrites. A first kernel copies those "halo" rows of every chunk to the
-// workspace; the second kernel then loads each chunk's sources (own rows from
-// the cache, halo rows from the workspace), waits at a workgroup barrier so
-// every read of the chunk has returned, and stores the shifted rows. No
-// workgroup ever reads a row another workgroup writes in the same kernel.
+// chunks of C rows. Chunk k reads source rows [kC + d, (k+1)C + d); the last
+// d of those are the first d rows chunk k+1 overwrites. A first kernel copies
+// those "halo" rows of every chunk to the workspace. In the second kernel one
+// thread owns one 16-byte column of one chunk and walks it upwards, row r
+// taking the value of row r + d (own rows from the cache, halo rows from the
+// workspace): a thread only ever overwrites addresses it has already read
+// itself, so no barrier is needed and the loads of the next rows are in
+// flight while the current rows are stored. No thread reads a row another
+// thread writes in the same kernel.
 //
 // Serial form (larger d): one workgroup per (b, kv head, K|V) walks the rows
 // upwards in blocks; a block's sources lie at or above every row written so
@@ -66,9 +68,27 @@ __global__ void __launch_bounds__(kEvictThreads) halo_kernel(EvictArgs a) {
   for (int u = threadIdx.x; u < d * a.upr; u += blockDim.x) dst[u] = src[u];
 }
 
+// Column chains: thread (chunk cl of the workgroup, column c) moves rows
+// row0 + r <- row0 + r + d for r = 0 .. rows - 1 of column c, kEvictRowsInFlight
+// rows at a time, the next group's loads issued before this group's stores
+// (they touch disjoint rows: the stores end below row0 + r + P, the next
+// loads start at row0 + r + P + d).
+template <class U>
+__device__ inline U shift_src(const EvictArgs& a, const U* rowsp, const U* halo, int row0, int src,
+                              int c, bool next_exists) {
+  return (next_exists && src >= row0 + a.chunk_rows)
+             ? halo[int64_t(src - row0 - a.chunk_rows) * a.upr + c]
+             : rowsp[int64_t(src) * a.upr + c];
+}
+
 template <class U>
 __global__ void __launch_bounds__(kEvictThreads) shift_kernel(EvictArgs a) {
-  const int k = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
+  constexpr int P = kEvictRowsInFlight;
+  const int per_wg = kEvictThreads / a.upr;          // chunks per workgroup
+  const int cl = threadIdx.x / a.upr, c = threadIdx.x - cl * a.upr;
+  if (cl >= per_wg) return;
+  const int k = blockIdx.x * per_wg + cl, y = blockIdx.y, b = blockIdx.z;
+  if (k >= a.nchunks) return;
   int L;
   const int d = drop_of(a, b, &L);
   if (d == 0 || d > kEvictHaloMax) return;
@@ -79,23 +99,23 @@ __global__ void __launch_bounds__(kEvictThreads) shift_kernel(EvictArgs a) {
   const bool next_exists = row0 + C < keep;
   U* rowsp = cache_rows<U>(a, b, y);
   const U* halo = halo_rows<U>(a, b, y, k);
-  const int units = rows * a.upr;
-  U v[kEvictUnitsPerThread];
+  U cur[P], nxt[P];
 #pragma unroll
-  for (int n = 0; n < kEvictUnitsPerThread; ++n) {
-    const int u = threadIdx.x + n * kEvictThreads;
-    if (u < units) {
-      const int r = u / a.upr, c = u - r * a.upr;
-      const int src = row0 + r + d;
-      v[n] = (next_exists && src >= row0 + C) ? halo[int64_t(src - row0 - C) * a.upr + c]
-                                               : rowsp[int64_t(src) * a.upr + c];
+  for (int p = 0; p < P; ++p)
+    if (p < rows) cur[p] = shift_src<U>(a, rowsp, halo, row0, row0 + p + d, c, next_exists);
+  for (int r0 = 0; r0 < rows; r0 += P) {
+    const bool more = r0 + P < rows;
+    if (more) {
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (r0 + P + p < rows)
+          nxt[p] = shift_src<U>(a, rowsp, halo, row0, row0 + r0 + P + p + d, c, next_exists);
     }
-  }
-  __syncthreads();  // every source of this chunk has been read
 #pragma unroll
-  for (int n = 0; n < kEvictUnitsPerThread; ++n) {
-    const int u = threadIdx.x + n * kEvictThreads;
-    if (u < units) rowsp[int64_t(row0) * a.upr + u] = v[n];
+    for (int p = 0; p < P; ++p)
+      if (r0 + p < rows) rowsp[int64_t(row0 + r0 + p) * a.upr + c] = cur[p];
+#pragma unroll
+    for (int p = 0; p < P; ++p) cur[p] = nxt[p];
   }
 }
 
@@ -129,7 +149,8 @@ __global__ void __launch_bounds__(kEvictThreads) serial_kernel(EvictArgs a) {
 template <class U>
 hipError_t run(const EvictArgs& a, int max_drop, hipStream_t st) {
   if (max_drop <= kEvictHaloMax) {
-    const dim3 grid(a.nchunks, a.Hkv * 2, a.B);
+    const int per_wg = kEvictThreads / a.upr;
+    const dim3 grid((a.nchunks + per_wg - 1) / per_wg, a.Hkv * 2, a.B);
     if (a.nchunks > 1) {
       hipLaunchKernelGGL(halo_kernel<U>, dim3(a.nchunks - 1, a.Hkv * 2, a.B),
                          dim3(kEvictThreads), 0, st, a);

@@ -56,11 +56,20 @@ constexpr int kDecodeMaxWorkers = kDecodeMaxWorkgroups * kDecodeWaves;  // waves
 constexpr int kDecodeMaxHG = 16;         // query heads per unit (the 16 MFMA columns)
 constexpr int kDecodeArgBatch = 64;      // largest batch the fast decode plans in its arguments
 
-// Eviction: rows per workgroup chunk is chosen so a chunk is 64 KiB; halo
-// copies are used up to this many dropped rows.
-constexpr int kEvictHaloMax = 32;
+// Eviction (parallel form): chunks of kEvictChunkRows rows, one thread per
+// 16-byte column of a chunk; halo copies are used up to kEvictHaloMax
+// dropped rows, the serial form beyond.
+constexpr int kEvictHaloMax = 16;         // largest drop the parallel eviction handles
 constexpr int kEvictThreads = 256;
-constexpr int kEvictUnitsPerThread = 16;
+constexpr int kEvictUnitsPerThread = 16;  // serial eviction: units per thread per pass
+#ifndef GQA_EVICT_CHUNK_ROWS
+#define GQA_EVICT_CHUNK_ROWS 64
+#endif
+#ifndef GQA_EVICT_ROWS_IN_FLIGHT
+#define GQA_EVICT_ROWS_IN_FLIGHT 8
+#endif
+constexpr int kEvictChunkRows = GQA_EVICT_CHUNK_ROWS;       // rows per chunk of the parallel eviction
+constexpr int kEvictRowsInFlight = GQA_EVICT_ROWS_IN_FLIGHT;  // rows of one column a thread has in flight
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -72,8 +81,7 @@ struct EvictGeometry {
 inline EvictGeometry evict_geometry(int row_bytes) {
   EvictGeometry g;
   g.unit = (row_bytes % 16 == 0) ? 16 : ((row_bytes % 4 == 0) ? 4 : 2);
-  const int chunk_bytes = kEvictThreads * kEvictUnitsPerThread * g.unit;
-  g.chunk_rows = chunk_bytes / row_bytes > 0 ? chunk_bytes / row_bytes : 1;
+  g.chunk_rows = kEvictChunkRows;
   return g;
 }
 
