@@ -90,6 +90,10 @@ struct DecodeArgs {
   const float* sinv;
   float* partials;
   int* counters;
+  uint16_t* halo_k;                     // fused eviction: next-block first rows, [B, Hkv, hb, D]
+  uint16_t* halo_v;
+  int shift;                            // fused eviction on: full sequences drop their oldest row
+  int hb;                               // halo rows per unit (blocks of the buffer)
   int B, H, Hkv, G, M, W;
   int rot, rot_rows, interleaved;
   int n_hg, hg_size;
@@ -102,6 +106,7 @@ struct DecodeArgs {
 
 struct Seq {
   int L, Lp, kstart, kend, nb;          // nb: blocks per unit of this sequence
+  int d;                                // rows dropped by the fused eviction (0 or 1)
 };
 
 __device__ inline Seq seq_of(const DecodeArgs& a, int b) {
@@ -111,6 +116,7 @@ __device__ inline Seq seq_of(const DecodeArgs& a, int b) {
   s.kend = s.Lp + 1;
   s.kstart = a.W > 0 ? (s.kend - a.W > 0 ? s.kend - a.W : 0) : 0;
   s.nb = (s.kend - s.kstart + kKeys - 1) / kKeys;
+  s.d = a.shift && s.L >= a.M ? 1 : 0;
   return s;
 }
 
@@ -120,6 +126,7 @@ struct Blk {
   const uint16_t* vc;
   int kb, kend, Lp;        // first key, unit end, new-token row
   int b, g, ub, i, nb;
+  int d;                   // fused eviction: key r is read from buffer row r + d
 };
 
 __device__ inline void set_unit(Blk& k, const DecodeArgs& a) {
@@ -132,6 +139,7 @@ __device__ inline void set_unit(Blk& k, const DecodeArgs& a) {
   k.Lp = s.Lp;
   k.nb = s.nb;
   k.kb = s.kstart + kKeys * k.i;
+  k.d = s.d;
 }
 
 __device__ inline Blk locate(const DecodeArgs& a, int64_t x) {
@@ -241,10 +249,18 @@ struct Q4 {
 
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ inline KV load_kv(const Blk& k, int n, int q4) {
+__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
-  const uint16_t* kp = k.kc + int64_t(row) * kD + 8 * q4;
-  const uint16_t* vp = k.vc + int64_t(row) * kD + 8 * q4;
+  // fused eviction: key `row` is buffer row row + d. The first row of the
+  // next block's sources is overwritten by that block's shifted stores, so
+  // the last key of a block comes from the copy taken before the kernel; the
+  // new-token key has no buffer row (past the end: any valid row, replaced).
+  int src = row + k.d;
+  const bool halo = k.d && n == kKeys - 1 && k.i + 1 < k.nb;
+  src = src < a.M ? src : row;
+  const int64_t hrow = ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD + 8 * q4;
+  const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
+  const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * kD + 8 * q4;
   KV r;
   r.k0 = ld16(kp); r.k1 = ld16(kp + 32); r.k2 = ld16(kp + 64); r.k3 = ld16(kp + 96);
   r.v0 = ld16(vp); r.v1 = ld16(vp + 32); r.v2 = ld16(vp + 64); r.v3 = ld16(vp + 96);
@@ -308,6 +324,16 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
       kc[0] = r.k0; kc[4] = r.k1; kc[8] = r.k2; kc[12] = r.k3;
       vc[0] = r.v0; vc[4] = r.v1; vc[8] = r.v2; vc[12] = r.v3;
     }
+  }
+  if (k.d && k.ub % a.n_hg == 0 && k.kb + n < k.kend) {
+    // fused eviction: key kb + n now lives in buffer row kb + n (its source
+    // rows of this block are already in registers; the row this overwrites
+    // for the previous block was read from the halo copy)
+    const int64_t crow = int64_t(k.kb + n) * kD + 8 * q4;
+    uint4* kc = reinterpret_cast<uint4*>(const_cast<uint16_t*>(k.kc) + crow);
+    uint4* vc = reinterpret_cast<uint4*>(const_cast<uint16_t*>(k.vc) + crow);
+    kc[0] = r.k0; kc[4] = r.k1; kc[8] = r.k2; kc[12] = r.k3;
+    vc[0] = r.v0; vc[4] = r.v1; vc[8] = r.v2; vc[12] = r.v3;
   }
   // ---- V rows into the tile ----
   {
@@ -571,7 +597,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (S < E) {
     Blk cur = locate(a, S);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
-    KV rc = load_kv(cur, n, q4);
+    KV rc = load_kv(a, cur, n, q4);
     Acc s;
     acc_reset(s);
     bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
@@ -581,7 +607,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // next (x + 2), clamped to the slice's last block. Q rows are loaded when
     // their unit starts (a small, cache-resident read).
     Blk nxt = S + 1 < E ? next_block(a, cur) : cur;        // block x + 1
-    KV r1 = load_kv(nxt, n, q4);
+    KV r1 = load_kv(a, nxt, n, q4);
     Blk ahead = S + 2 < E ? next_block(a, nxt) : nxt;       // block x + 2
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
@@ -589,7 +615,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv(ahead, n, q4);
+      r_fill = load_kv(a, ahead, n, q4);
       compute<T>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
@@ -695,7 +721,34 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds);
 }
 
+// Fused eviction, before the decode kernel: for every full sequence, unit
+// (b, g) and block i but the last, copy buffer row 16 (i + 1) + ... the first
+// source row of block i + 1, i.e. key 16 i + 15's source, which block i + 1's
+// shifted stores overwrite. One workgroup per (b, g, K|V).
+__global__ void __launch_bounds__(256) shift_halo_kernel(DecodeArgs a) {
+  const int y = blockIdx.x, b = blockIdx.y;
+  const int g = y >> 1;
+  const Seq s = seq_of(a, b);
+  if (!s.d) return;
+  const uint16_t* src = ((y & 1) ? a.v_cache : a.k_cache) + (int64_t(b) * a.Hkv + g) * a.M * kD;
+  uint16_t* dst = ((y & 1) ? a.halo_v : a.halo_k) + (int64_t(b) * a.Hkv + g) * a.hb * kD;
+  const int n = (s.nb - 1) * (kD / 8);            // 16-byte chunks to copy
+  for (int c = threadIdx.x; c < n; c += 256) {
+    const int i = c / (kD / 8), part = c % (kD / 8);
+    const int row = s.kstart + kKeys * (i + 1) + s.d - 1;   // = key 16 i + 15 + d
+    *reinterpret_cast<uint4*>(dst + int64_t(i) * kD + 8 * part) =
+        *reinterpret_cast<const uint4*>(src + int64_t(row) * kD + 8 * part);
+  }
+}
+
 }  // namespace
+
+bool decode_fused_evict_supported(const Problem& p) {
+  // the window must cover the whole buffer (every kept row is read, so every
+  // kept row can be moved by its reader), and one unit per kv head (a single
+  // head group reads, and so may rewrite, each row)
+  return p.window >= p.M && ceil_div(p.G, kDecodeMaxHG) == 1;
+}
 
 bool decode_fast_supported(const Problem& p) {
   return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.S == 1 &&
@@ -703,7 +756,7 @@ bool decode_fast_supported(const Problem& p) {
 }
 
 hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
-                              hipStream_t st) {
+                              hipStream_t st, bool fuse_evict) {
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(p.q);
   a.k_new = static_cast<const uint16_t*>(p.k_new);
@@ -715,6 +768,10 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
   a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scratch);
   a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + lay.counters);
+  a.shift = fuse_evict ? 1 : 0;
+  a.hb = ceil_div(p.M, kKeys);
+  a.halo_k = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.decode_halo);
+  a.halo_v = a.halo_k + int64_t(p.B) * p.Hkv * a.hb * kD;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window;
   a.n_hg = ceil_div(p.G, kDecodeMaxHG);
   a.hg_size = ceil_div(p.G, a.n_hg);
@@ -743,6 +800,11 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   while (workers > 1 && max_unit * workers > int64_t(kMergeMax - 1) * total) workers /= 2;
   a.workers = int(workers);
   const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
+  if (a.shift) {
+    hipLaunchKernelGGL(shift_halo_kernel, dim3(p.Hkv * 2, p.B), dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (p.dtype == GQA_FP16)
     hipLaunchKernelGGL(decode_kernel<F16>, dim3(blocks), dim3(kThreads), 0, st, a);
   else

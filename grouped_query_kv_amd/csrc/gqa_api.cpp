@@ -151,13 +151,15 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
   if (P.B == 0) return GQA_OK;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (needs_evict) {
+  const bool fast_decode = P.S == 1 && decode_fast_supported(P);
+  const bool fuse_evict = needs_evict && fast_decode && decode_fused_evict_supported(P);
+  if (needs_evict && !fuse_evict) {
     e = launch_evict(P, P.S, max_drop, ws, lay, hs);
     if (e != hipSuccess) return hip_fail(e, "eviction");
   }
   const bool evicted_lengths = P.window > 0;
-  if (P.S == 1 && decode_fast_supported(P)) {
-    e = launch_decode_fast(P, ws, lay, hs);
+  if (fast_decode) {
+    e = launch_decode_fast(P, ws, lay, hs, fuse_evict);
     if (e != hipSuccess) return hip_fail(e, "decode");
     return GQA_OK;
   }
@@ -195,8 +197,12 @@ WorkspaceLayout workspace_layout(const gqa_shape& s) {
   const EvictGeometry eg = evict_geometry((int)row_bytes);
   const int64_t chunks = (M + eg.chunk_rows - 1) / eg.chunk_rows;
   const int64_t halo = B * Hkv * 2 * chunks * kEvictHaloMax * row_bytes;
+  // fused-eviction halo rows (decode): [2][B, Hkv, ceil(M / 16), D] in the dtype
+  int64_t dhalo = 0;
+  if (D == 128 && s.dtype != GQA_FP32) dhalo = 2 * B * Hkv * ((M + 15) / 16) * D * 2;
   l.scratch = l.counters_bytes;
-  l.scratch_bytes = align256(size_t(std::max(partial, halo)));
+  l.decode_halo = l.scratch + align256(size_t(partial));
+  l.scratch_bytes = align256(std::max(size_t(halo), align256(size_t(partial)) + size_t(dhalo)));
   l.total = l.scratch + l.scratch_bytes;
   return l;
 }

@@ -40,6 +40,7 @@ struct WorkspaceLayout {
   size_t counters_bytes;
   size_t scratch;         // shared by decode partials and eviction halos
   size_t scratch_bytes;
+  size_t decode_halo;     // fused-eviction halo rows, after the decode partials
   size_t total;
 };
 
@@ -100,8 +101,11 @@ hipError_t launch_attention_simple(const Problem& p, hipStream_t st);
 
 // Fast decode (fp16/bf16, D == 128, S == 1): fused append + split-KV + merge.
 bool decode_fast_supported(const Problem& p);
+// Eviction folded into the decode (the window covers the buffer, one head
+// group per kv head): each kept row is moved by the wave that reads it.
+bool decode_fused_evict_supported(const Problem& p);
 hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
-                              hipStream_t st);
+                              hipStream_t st, bool fuse_evict);
 
 // Fast prefill (fp16/bf16, D == 128): MFMA flash attention over the cache.
 bool prefill_fast_supported(const Problem& p);
