@@ -66,6 +66,90 @@ __global__ void __launch_bounds__(256) rotary_rows_kernel(
   }
 }
 
+// Vector form for 2-byte types with D % 16 == 0: one thread per 8 rotary
+// pairs of one row (rotate-half: 16 bytes from each half of the row;
+// interleaved: two 16-byte runs of 4 pairs each), 16-byte loads and stores,
+// index arithmetic once per thread.
+template <class T>
+__device__ inline void rot8(uint4& x, uint4& y, const float* c8, const float* s8) {
+  using Bits = typename T::bits;
+  uint32_t* xw = &x.x;
+  uint32_t* yw = &y.x;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    Bits x0 = Bits(xw[w] & 0xFFFFu), x1 = Bits(xw[w] >> 16);
+    Bits y0 = Bits(yw[w] & 0xFFFFu), y1 = Bits(yw[w] >> 16);
+    rotate_pair<T>(x0, y0, c8[2 * w], s8[2 * w]);
+    rotate_pair<T>(x1, y1, c8[2 * w + 1], s8[2 * w + 1]);
+    xw[w] = uint32_t(x0) | (uint32_t(x1) << 16);
+    yw[w] = uint32_t(y0) | (uint32_t(y1) << 16);
+  }
+}
+
+template <class T>
+__device__ inline void rot_inter8(uint4& x, const float* c4, const float* s4) {
+  using Bits = typename T::bits;
+  uint32_t* xw = &x.x;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    Bits a = Bits(xw[w] & 0xFFFFu), b = Bits(xw[w] >> 16);
+    rotate_pair<T>(a, b, c4[w], s4[w]);
+    xw[w] = uint32_t(a) | (uint32_t(b) << 16);
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) rotary_rows_vec_kernel(
+    const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, const int32_t* __restrict__ lens,
+    int B, int S, int Hkv, int D, int M, const float* __restrict__ cosv,
+    const float* __restrict__ sinv, int rot_rows, int interleaved, int evicted) {
+  const int half = D / 2;
+  const int cpr = half / 8;                       // threads per row: 8 pairs each
+  const int64_t total = int64_t(B) * S * Hkv * cpr;
+  for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < total;
+       idx += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = idx / cpr;                  // source row (b, i, g)
+    const int ch = int(idx - r * cpr);
+    const int g = int(r % Hkv);
+    const int64_t bi = r / Hkv;
+    const int i = int(bi % S), b = int(bi / S);
+    const int pos = clamp_len(clamp_len(lens[b], 0, M) + i, 0, rot_rows - 1);
+    const float* cr = cosv + int64_t(pos) * half;
+    const float* sr = sinv + int64_t(pos) * half;
+    const uint16_t* srow = src + r * D;
+    const int row = dest_base(lens, b, S, M, evicted != 0) + i;
+    uint16_t* drow = dst + ((int64_t(b) * Hkv + g) * M + row) * D;
+    if (!interleaved) {
+      const int j0 = 8 * ch;                      // pairs (j, j + D/2), j = j0 .. j0 + 7
+      uint4 x = *reinterpret_cast<const uint4*>(srow + j0);
+      uint4 y = *reinterpret_cast<const uint4*>(srow + j0 + half);
+      const float4 c0 = *reinterpret_cast<const float4*>(cr + j0);
+      const float4 c1 = *reinterpret_cast<const float4*>(cr + j0 + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sr + j0);
+      const float4 s1 = *reinterpret_cast<const float4*>(sr + j0 + 4);
+      const float c8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float s8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      rot8<T>(x, y, c8, s8);
+      *reinterpret_cast<uint4*>(drow + j0) = x;
+      *reinterpret_cast<uint4*>(drow + j0 + half) = y;
+    } else {
+      const int e0 = 16 * ch;                     // elements e0 .. e0 + 15 = pairs 8 ch .. + 7
+      uint4 x = *reinterpret_cast<const uint4*>(srow + e0);
+      uint4 y = *reinterpret_cast<const uint4*>(srow + e0 + 8);
+      const float4 c0 = *reinterpret_cast<const float4*>(cr + 8 * ch);
+      const float4 c1 = *reinterpret_cast<const float4*>(cr + 8 * ch + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sr + 8 * ch);
+      const float4 s1 = *reinterpret_cast<const float4*>(sr + 8 * ch + 4);
+      const float ca[4] = {c0.x, c0.y, c0.z, c0.w}, sa[4] = {s0.x, s0.y, s0.z, s0.w};
+      const float cb[4] = {c1.x, c1.y, c1.z, c1.w}, sb[4] = {s1.x, s1.y, s1.z, s1.w};
+      rot_inter8<T>(x, ca, sa);
+      rot_inter8<T>(y, cb, sb);
+      *reinterpret_cast<uint4*>(drow + e0) = x;
+      *reinterpret_cast<uint4*>(drow + e0 + 8) = y;
+    }
+  }
+}
+
 int grid_for(int64_t total) {
   int64_t blocks = (total + 255) / 256;
   const int64_t cap = 256 * 64;  // enough workgroups to fill the chip many times
@@ -97,8 +181,18 @@ hipError_t copy_rows(const void* src, void* dst, const Problem& p, bool evicted,
 
 template <class T>
 hipError_t rotary_rows(const Problem& p, bool evicted, hipStream_t st) {
-  const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 2);
   using Bits = typename T::bits;
+  if constexpr (sizeof(Bits) == 2) {
+    if (p.D % 16 == 0) {
+    const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 16);
+    hipLaunchKernelGGL(rotary_rows_vec_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(p.k_new), static_cast<uint16_t*>(p.k_cache),
+                       p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,
+                       p.interleaved, int(evicted));
+      return hipGetLastError();
+    }
+  }
+  const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 2);
   hipLaunchKernelGGL(rotary_rows_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
                      static_cast<const Bits*>(p.k_new), static_cast<Bits*>(p.k_cache),
                      p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,

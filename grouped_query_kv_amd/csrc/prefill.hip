@@ -1,26 +1,28 @@
 // Flash-style attention for S >= 1 new tokens, fp16/bf16, head_size 128.
 //
-// One workgroup (4 waves) takes one (b, kv head) and 128 query rows, where
+// One workgroup (8 waves) takes one (b, kv head) and 256 query rows, where
 // the rows of a kv head are its (position i, local head j) pairs flattened as
 // r = i * G + j: the G query heads that share the kv head share every K/V
-// tile the workgroup stages in LDS, whatever G is. Each wave owns 32 rows.
+// tile the workgroup holds in LDS, whatever G is. Each wave owns 32 rows.
 //
 // Per 64-key tile (the gemm0 -> softmax -> gemm1 chain of the "KV Cache"
 // discussion's worked example, on gfx950 MFMA 32x32x16):
 //   S^T = K Q^T   A = K rows from LDS, B = Q^T held in registers (rotated
 //                 on load under the fp64 rule when rotary is on);
-//                 lane (row, half) gets 16 keys of its row;
+//                 lane (row, half) gets 32 keys of its row;
 //   online softmax per row, in registers (one cross-lane step);
-//   O^T += V^T P^T  A = V^T from LDS (staged transposed, keys permuted so one
-//                 16-byte read gives the 8 keys the lane's P slice holds),
-//                 B = P^T straight from the S^T registers.
+//   O^T += V^T P^T  A = V^T through transposing LDS reads, B = P^T straight
+//                 from the S^T registers.
+// The eight waves form two groups that alternate between the matrix
+// products and the softmax (see prefill_kernel), so the two waves sharing a
+// SIMD keep its matrix core and its vector unit busy at the same time.
 // Keys run from the workgroup's window start to its last row's own position:
 // the tile loop ends at the sequence's length (the early exit on the key-block
 // loop from the discussion's notes), each wave skips the tiles no row of its
 // own can see, and the causal/window mask is applied only on tiles that are
 // not fully visible to all of the wave's rows. K/V rows past the valid length
-// are never read from memory (zeros are staged instead), so P and V entries of
-// masked keys are exact zeros.
+// are never read from memory (the tile loads return zeros there), so P and V
+// entries of masked keys are exact zeros.
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
@@ -68,7 +70,12 @@ template <> struct Mma32<BF16> {
 
 constexpr int kD = 128;
 constexpr int kBK = 64;                       // keys per tile
-constexpr int kThreads = 256;
+#ifndef GQA_PREFILL_READ_AHEAD
+#define GQA_PREFILL_READ_AHEAD 8              // LDS operand reads issued ahead of their product
+#endif
+constexpr int kWaves = 8;                     // two groups of four (one wave of each per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWgRows = 32 * kWaves;          // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 // The running maximum used in the exponent is refreshed only when a score
 // exceeds it by more than this many binary orders, so weights stay <= 2^8:
@@ -152,28 +159,28 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Per-lane byte offsets of the tile loads, relative to the tile's first key.
-// Wave w moves rows 16 w + 4 q + lane / 16 (q = 0..3); the swizzle depends on
-// the row only through key & 15 = (4 q + lane / 16) & 15 (tiles start at
-// multiples of 64), so four offsets per lane cover every tile.
+// Wave w moves rows 8 w + 4 q + lane / 16 (q = 0, 1); the K swizzle depends
+// on the row only through key & 15 = (8 w + 4 q + lane / 16) & 15 (tiles
+// start at multiples of 64), the V swizzle only through lane / 16.
 struct LoadOffsets {
-  int k[4];
-  int v;         // V: swizzle independent of q; quad q adds 1024 q
+  int k[2];
+  int v;         // V: one pattern; quad q adds 1024 q
 };
 
 __device__ inline LoadOffsets load_offsets(int wave, int lane) {
   LoadOffsets lo;
   const int lr = lane >> 4, slot = lane & 15;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rrow = 16 * wave + 4 * q + lr;
+  for (int q = 0; q < 2; ++q) {
+    const int rrow = 8 * wave + 4 * q + lr;
     lo.k[q] = rrow * 256 + 16 * (slot ^ swz_k(rrow));
   }
-  lo.v = (16 * wave + lr) * 256 + 16 * (slot ^ swz_v(lr));
+  lo.v = (8 * wave + lr) * 256 + 16 * (slot ^ swz_v(lr));
   return lo;
 }
 
-// Issue this wave's share (16 rows) of one tile: quad q covers rows
-// 16 w + 4 q .. + 3. The instruction's immediate offset moves both the
+// Issue this wave's share (8 rows) of one tile: quad q covers rows
+// 8 w + 4 q .. + 3. The instruction's immediate offset moves both the
 // memory address and the LDS destination, so V (one offset pattern) steps
 // through its quads with it from one LDS base; K (a different swizzle per
 // quad) uses per-quad lane offsets and LDS bases. Each tile gets its own
@@ -184,10 +191,10 @@ template <bool kIsV, int Q>
 __device__ inline void quad_load(__amdgpu_buffer_rsrc_t rsrc, unsigned char* tile,
                                  const LoadOffsets& lo, int wave) {
   if (kIsV)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 16 * wave * 256), 16, lo.v, 0,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 8 * wave * 256), 16, lo.v, 0,
                                              1024 * Q, 0);
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (16 * wave + 4 * Q) * 256),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (8 * wave + 4 * Q) * 256),
                                              16, lo.k[Q], 0, 0, 0);
 }
 
@@ -200,8 +207,6 @@ __device__ inline void tile_load(const uint16_t* base, int kvalid, unsigned char
       const_cast<uint16_t*>(base + int64_t(t0) * kD), 0, rows * kD * 2, 0x00020000);
   quad_load<kIsV, 0>(rsrc, tile, lo, wave);
   quad_load<kIsV, 1>(rsrc, tile, lo, wave);
-  quad_load<kIsV, 2>(rsrc, tile, lo, wave);
-  quad_load<kIsV, 3>(rsrc, tile, lo, wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -270,15 +275,24 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
 template <class T>
 __device__ inline void scores_tile(const unsigned char* kt, const uint4 (&qv)[8], f32x16 (&s)[2],
                                    int col, int c) {
+  // the two 32-key halves are independent accumulation chains: alternate
+  // them so that consecutive products never wait on each other
+  const unsigned char* k0 = kt + col * 256;
+  const unsigned char* k1 = kt + (32 + col) * 256;
+  const int sw = swz_k(col);
+  s[0] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k0 + 16 * (c ^ sw)), qv[0], f32x16{});
+  s[1] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k1 + 16 * (c ^ sw)), qv[0], f32x16{});
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const unsigned char* krow = kt + (32 * h + col) * 256;
-    const int sw = swz_k(col);
-    s[h] = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * (c ^ sw)), qv[0], f32x16{});
+  for (int kk = 1; kk < 8; ++kk) {
+    s[0] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k0 + 16 * ((2 * kk + c) ^ sw)), qv[kk], s[0]);
+    s[1] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k1 + 16 * ((2 * kk + c) ^ sw)), qv[kk], s[1]);
+  }
+  // operand reads kPrefetch products ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, GQA_PREFILL_READ_AHEAD, 0);
 #pragma unroll
-    for (int kk = 1; kk < 8; ++kk)
-      s[h] = Mma32<T>::run(*reinterpret_cast<const uint4*>(krow + 16 * ((2 * kk + c) ^ sw)),
-                           qv[kk], s[h]);
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
 
@@ -309,31 +323,80 @@ __device__ inline void pv_tile(const unsigned char* vt, const uint4 (&pk)[4], f3
       o[dt] = Mma32<T>::run(make_uint4(w[0], w[1], w[2], w[3]), pk[u], o[dt]);
     }
   }
+  // operand reads kPrefetch products ahead of the products that use them
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * GQA_PREFILL_READ_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
 }
 
-// One workgroup = 4 waves x 32 query rows of one (b, kv head). Software
-// pipeline per iteration t (one barrier): loads of K(t+2) and V(t+1) are in
-// flight while S(t+1) = K(t+1) Q^T runs on the matrix cores under the softmax
-// of tile t, then O += V(t) P(t).
+// One workgroup = 8 waves x 32 query rows of one (b, kv head): group 0
+// (waves 0-3) and group 1 (waves 4-7), one wave of each on every SIMD.
+// Every 64-key tile t takes two phases, separated by workgroup barriers:
+//   phase 2t:     group 0: O += V(t-1) P(t-1), S(t) = K(t) Q^T   (matrix cores)
+//                 group 1: softmax of S(t-1) -> P(t-1)            (vector units)
+//   phase 2t + 1: group 0: softmax of S(t) -> P(t)
+//                 group 1: O += V(t-1) P(t-1), S(t) = K(t) Q^T
+// so the two waves sharing a SIMD always work on different units. K(t+1)
+// and V(t) go to the free LDS buffers at the start of phase 2t (the tiles
+// they replace were last read in phase 2t - 1) and are waited for at the
+// end of phase 2t + 1.
 template <class T>
-__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
+__device__ inline void products(int t, int wt0, int wt1, const unsigned char* kt,
+                                const unsigned char* vt, const uint4 (&qv)[8], const uint4 (&pk)[4],
+                                f32x16 (&o)[4], f32x16 (&sc)[2], int col, int c, int lane) {
+  if (t - 1 >= wt0 && t - 1 < wt1) pv_tile<T>(vt, pk, o, lane);
+  if (t >= wt0 && t < wt1) scores_tile<T>(kt, qv, sc, col, c);
+}
+
+template <class T>
+__device__ inline void softmax_step(int t, int wt0, int wt1, f32x16 (&sc)[2], RowState& rs,
+                                    f32x16 (&o)[4], uint4 (&pk)[4], float cs, int my_p, int span,
+                                    int w_full_lo, int w_full_hi, int c) {
+  if (t < wt0 || t >= wt1) return;
+  const int tb = t * kBK;
+  const bool full = tb + kBK - 1 <= w_full_hi && tb >= w_full_lo;
+  const int lim_hi = my_p - (tb + 4 * c);
+  if (full)
+    softmax_tile<T, false>(sc, rs, o, pk, cs, lim_hi, span);
+  else
+    softmax_tile<T, true>(sc, rs, o, pk, cs, lim_hi, span);
+}
+
+template <class T>
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
+  // four separately declared tiles, each used at fixed places of the
+  // two-iteration loop body: the compiler can then tell the tiles being read
+  // from the tiles being filled by direct-to-LDS loads and does not wait for
+  // those loads before every read
+  __shared__ __attribute__((aligned(1024))) unsigned char k_even[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_odd[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_even[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_odd[kTileBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+#ifndef GQA_PREFILL_GROUP_ODD
+  const int grp = wave >> 2;
+#else
+  const int grp = wave & 1;
+#endif
   const int col = lane & 31, c = lane >> 5;     // S^T column (= the lane's row), k half
   const int units = a.B * a.Hkv;
-  const int rb = a.n_rb - 1 - int(blockIdx.x) / units;    // longest row blocks first
   const int bg = int(blockIdx.x) % units;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.G, S = a.S;
+
+  // one row block: the whole tile loop for 256 query rows
+  auto row_block = [&](const int rb) {
   const int nrows = S * G;
   // lengths are read through a vector load: mark them wave-uniform
   const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.lens[b], 0, a.M - S));
   const int kvalid = L + S;
 
-  const int r0 = rb * 128;
+  const int r0 = rb * kWgRows;
   const int wr0 = r0 + 32 * wave;
   const bool wave_has_rows = wr0 < nrows;
   const int r = wr0 + col;
@@ -344,7 +407,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const int my_ws = a.W > 0 ? max(0, my_p - a.W + 1) : 0;   // window start
 
   // workgroup and wave key ranges (tiles)
-  const int wg_ilo = r0 / G, wg_ihi = min(S - 1, (r0 + 127) / G);
+  const int wg_ilo = r0 / G, wg_ihi = min(S - 1, (r0 + kWgRows - 1) / G);
   const int w_ilo = min(S - 1, wr0 / G), w_ihi = min(S - 1, (wr0 + 31) / G);
   const int wg_kstart = a.W > 0 ? max(0, L + wg_ilo - a.W + 1) : 0;
   const int wg_kend = L + wg_ihi + 1;
@@ -361,11 +424,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const uint16_t* kc = a.k_cache + kvbase;
   const uint16_t* vc = a.v_cache + kvbase;
 
-  // prologue loads: K(t_begin), V(t_begin), K(t_begin + 1)
   const LoadOffsets lo = load_offsets(wave, lane);
-  tile_load<false>(kc, kvalid, lds_k[0], t_begin * kBK, lo, wave);
-  tile_load<true>(vc, kvalid, lds_v[0], t_begin * kBK, lo, wave);
-  if (t_begin + 1 < t_end) tile_load<false>(kc, kvalid, lds_k[1], (t_begin + 1) * kBK, lo, wave);
+  tile_load<false>(kc, kvalid, k_even, t_begin * kBK, lo, wave);
 
   // ---- Q^T (B operand): lane holds Q[row][16 ks + 8 c + e] ----
   uint4 qv[8];
@@ -393,40 +453,60 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   RowState rs{-INFINITY, 0.f, 0.f};
   const float cs = a.scale_log2;
   const int span = my_p - my_ws;
+  f32x16 sc[2];
+  uint4 pk[4];
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // one pipeline step; `cur` holds S(t), `next` receives S(t + 1)
-  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&next)[2]) {
-    const int buf = (t - t_begin) & 1;
-    // K(t) and V(t - 1) are no longer read by anyone: refill their buffers
-    if (t + 2 < t_end) tile_load<false>(kc, kvalid, lds_k[buf], (t + 2) * kBK, lo, wave);
-    if (t + 1 < t_end) tile_load<true>(vc, kvalid, lds_v[buf ^ 1], (t + 1) * kBK, lo, wave);
-    if (t + 1 >= wt0 && t + 1 < wt1) scores_tile<T>(lds_k[buf ^ 1], qv, next, col, c);
-    if (t >= wt0 && t < wt1) {
-      const int tb = t * kBK;
-      const bool full = tb + kBK - 1 <= w_full_hi && tb >= w_full_lo;
-      const int lim_hi = my_p - (tb + 4 * c);
-      uint4 pk[4];
-      if (full)
-        softmax_tile<T, false>(cur, rs, o, pk, cs, lim_hi, span);
-      else
-        softmax_tile<T, true>(cur, rs, o, pk, cs, lim_hi, span);
-      pv_tile<T>(lds_v[buf], pk, o, lane);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // Tile t (j = t - t_begin) uses K buffer j % 2 and V(t - 1) in buffer
+  // (j + 1) % 2, and fills K(t + 1) into buffer (j + 1) % 2 and V(t) into
+  // buffer j % 2. The two groups run separate loops with the same barriers
+  // (s_barrier counts arrivals, not program locations).
+  // Phase barriers order execution only: every LDS read of a tile is
+  // consumed by a product before its wave reaches the barrier, so a bare
+  // s_barrier (no memory fence, which would wait for the direct-to-LDS loads
+  // still in flight) suffices in the middle of a tile. At the end of a tile
+  // each wave first waits for its own loads, so the next tiles are complete
+  // in LDS once everyone has passed.
+  auto phase_barrier = []() { __builtin_amdgcn_s_barrier(); };
+  auto tiles_landed_barrier = []() {
+    // vmcnt(0), expcnt and lgkmcnt left alone; as a builtin the compiler
+    // sees that the direct-to-LDS loads have completed
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_barrier();
   };
-
-  f32x16 sa[2], sb[2];
-  if (t_begin >= wt0 && t_begin < wt1) scores_tile<T>(lds_k[0], qv, sa, col, c);
-  int t = t_begin;
-  for (; t + 1 < t_end; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  auto loads = [&](int t, unsigned char* kn, unsigned char* vn) {
+    if (t + 1 < t_end) tile_load<false>(kc, kvalid, kn, (t + 1) * kBK, lo, wave);
+    if (t < t_end) tile_load<true>(vc, kvalid, vn, t * kBK, lo, wave);
+  };
+  auto step0 = [&](int t, const unsigned char* kt, const unsigned char* vt, unsigned char* kn,
+                   unsigned char* vn) {
+    loads(t, kn, vn);
+    products<T>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
+    phase_barrier();
+    softmax_step<T>(t, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c);
+    tiles_landed_barrier();
+  };
+  auto step1 = [&](int t, const unsigned char* kt, const unsigned char* vt, unsigned char* kn,
+                   unsigned char* vn) {
+    loads(t, kn, vn);
+    softmax_step<T>(t - 1, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c);
+    phase_barrier();
+    products<T>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
+    tiles_landed_barrier();
+  };
+  if (grp == 0) {
+    for (int t = t_begin; t <= t_end; t += 2) {
+      step0(t, k_even, v_odd, k_odd, v_even);
+      if (t + 1 <= t_end) step0(t + 1, k_odd, v_even, k_even, v_odd);
+    }
+  } else {
+    for (int t = t_begin; t <= t_end; t += 2) {
+      step1(t, k_even, v_odd, k_odd, v_even);
+      if (t + 1 <= t_end) step1(t + 1, k_odd, v_even, k_even, v_odd);
+    }
   }
-  if (t < t_end) step(t, sa, sb);
 
   if (!row_ok) return;
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs.l), __float_as_uint(rs.l),
@@ -443,6 +523,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       w.y = Mma32<T>::pack2(o[dt][4 * v4 + 2] * inv, o[dt][4 * v4 + 3] * inv);
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
+  };
+
+  row_block(a.n_rb - 1 - int(blockIdx.x) / units);      // longest row blocks first
 }
 
 }  // namespace
@@ -462,7 +545,7 @@ hipError_t launch_prefill_fast(const Problem& p, hipStream_t st) {
   a.cosv = p.cos; a.sinv = p.sin;
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window;
   a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
-  a.n_rb = ceil_div(p.S * p.G, 128);
+  a.n_rb = ceil_div(p.S * p.G, kWgRows);
   a.scale_log2 = fabsf(p.scale) * kLog2e;
   a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
   const int blocks = a.n_rb * p.B * p.Hkv;
