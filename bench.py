@@ -37,6 +37,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, 2.5 PFLOP/s
 METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GPU"
+# HBM traffic of the decode kernel on the headline workload, per dispatch, from
+# two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+# each scaled by what the same counter reads for a plain 512 MiB device-to-device
+# copy: FETCH_SIZE reads 262157 KiB for 524288 KiB moved (x2.0), WRITE_SIZE reads
+# 524288 KiB (x1.0). Valid only for the kernel sources the counters were taken
+# on; any change to them makes the figure null until the passes are repeated.
+DECODE_TRAFFIC = {
+    "sources": {"grouped_query_kv_amd/csrc/decode.hip":
+                "54caa92e97d1223b04fed4cf4c977fb27a29f2d47581aabfe7ee69e529ec1555",
+                "grouped_query_kv_amd/csrc/gqa_internal.h":
+                "f440e922da4e765bb388c50656d56351503e0ec2972d424801302fc7eea3dba4"},
+    "fetch_kib": 74183.28, "write_kib": 1050.29,
+    "fetch_scale": 524288.0 / 262157.15, "write_scale": 1.0,
+}
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
 
@@ -134,7 +148,10 @@ def time_calls(torch, sets, call, steps, warmup):
     Pass 1 (the timed region): barrier + synchronize, the calls back to back,
     synchronize; returns wall ms per step. Pass 2: the same calls, each
     bracketed by HIP events recorded on the launch stream; returns the list
-    of per-call device times in ms (the kernel time the roofline uses).
+    of per-call device times in ms (the kernel time the roofline uses). Pass 2
+    is queued behind a spin kernel that outlasts the host's enqueue time, so
+    the device runs the calls back to back and the events see device time
+    only, not host launch latency.
     """
     stream = torch.cuda.current_stream()
     for i in range(warmup):
@@ -143,10 +160,12 @@ def time_calls(torch, sets, call, steps, warmup):
     t0 = time.perf_counter()
     for i in range(steps):
         call(sets[(warmup + i) % len(sets)])
+    enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    torch.cuda._sleep(spin_cycles(torch, 2.0 * enq + 2e-3))
     for i in range(steps):
         ev[i][0].record(stream)
         call(sets[(warmup + i) % len(sets)])
@@ -154,6 +173,34 @@ def time_calls(torch, sets, call, steps, warmup):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     return wall, per
+
+
+_SPIN_RATE = []
+
+
+def spin_cycles(torch, seconds):
+    """Argument for torch.cuda._sleep that spins about `seconds` (rate measured once)."""
+    if not _SPIN_RATE:
+        n = 1 << 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(n)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_RATE.append(n / max(a.elapsed_time(b) * 1e-3, 1e-6))
+    return int(min(seconds, 1.0) * _SPIN_RATE[0]) + 1
+
+
+def decode_traffic_bytes():
+    """Counter-derived HBM bytes per decode dispatch, or None if the kernel changed."""
+    import hashlib
+    for rel, digest in DECODE_TRAFFIC["sources"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    t = DECODE_TRAFFIC
+    return int(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
 
 
 def stats(per):
@@ -221,6 +268,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default="c2,c3,c4,c5", help="workloads to run (c2 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device-to-device copies of MIB MiB (the reference "
+                         "for scaling memory-traffic counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; the op is not sharded across "
@@ -228,6 +278,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_copy": n, "copies": 5}), flush=True)
+        return
     import gqa_inputs as gi
     import grouped_query_kv_amd as gqa
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -311,7 +370,7 @@ def main():
                    "global_batch": 16, "seq_len": 4096, "parallelism": "none (1 GPU)",
                    "seqlens_k": c2.seqlens_k.tolist()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(),
                      "kernel": "decode call (all launches of gqa_attention_decode)",
                      "bytes_per_call": c2_bytes, **st2},
         "cpu_baseline": cpu,
