@@ -22,6 +22,7 @@ the decode workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -157,12 +158,17 @@ def time_calls(torch, sets, call, steps, warmup):
     for i in range(warmup):
         call(sets[i % len(sets)])
     torch.cuda.synchronize()
+    gc_was = gc.isenabled()
+    gc.disable()                 # no collector pause inside the timed region
     t0 = time.perf_counter()
     for i in range(steps):
         call(sets[(warmup + i) % len(sets)])
     enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    if gc_was:
+        gc.enable()
+    log(f"[bench]   wall {wall:.4f} ms/step, host enqueue {enq * 1e3 / steps:.4f} ms/step")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda._sleep(spin_cycles(torch, 2.0 * enq + 2e-3))

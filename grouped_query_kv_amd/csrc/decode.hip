@@ -726,19 +726,17 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 // source row of block i + 1, i.e. key 16 i + 15's source, which block i + 1's
 // shifted stores overwrite. One workgroup per (b, g, K|V).
 __global__ void __launch_bounds__(256) shift_halo_kernel(DecodeArgs a) {
-  const int y = blockIdx.x, b = blockIdx.y;
+  // one 16-byte chunk per thread: 16 halo rows per block, every copy in flight at once
+  const int y = blockIdx.y, b = blockIdx.z;
   const int g = y >> 1;
   const Seq s = seq_of(a, b);
-  if (!s.d) return;
+  const int i = blockIdx.x * 16 + (threadIdx.x >> 4), part = threadIdx.x & 15;
+  if (!s.d || i >= s.nb - 1) return;
   const uint16_t* src = ((y & 1) ? a.v_cache : a.k_cache) + (int64_t(b) * a.Hkv + g) * a.M * kD;
   uint16_t* dst = ((y & 1) ? a.halo_v : a.halo_k) + (int64_t(b) * a.Hkv + g) * a.hb * kD;
-  const int n = (s.nb - 1) * (kD / 8);            // 16-byte chunks to copy
-  for (int c = threadIdx.x; c < n; c += 256) {
-    const int i = c / (kD / 8), part = c % (kD / 8);
-    const int row = s.kstart + kKeys * (i + 1) + s.d - 1;   // = key 16 i + 15 + d
-    *reinterpret_cast<uint4*>(dst + int64_t(i) * kD + 8 * part) =
-        *reinterpret_cast<const uint4*>(src + int64_t(row) * kD + 8 * part);
-  }
+  const int row = s.kstart + kKeys * (i + 1) + s.d - 1;     // = key 16 i + 15 + d
+  *reinterpret_cast<uint4*>(dst + int64_t(i) * kD + 8 * part) =
+      *reinterpret_cast<const uint4*>(src + int64_t(row) * kD + 8 * part);
 }
 
 }  // namespace
@@ -801,7 +799,7 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.workers = int(workers);
   const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
   if (a.shift) {
-    hipLaunchKernelGGL(shift_halo_kernel, dim3(p.Hkv * 2, p.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(shift_halo_kernel, dim3(ceil_div(a.hb, 16), p.Hkv * 2, p.B), dim3(256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -69,6 +69,7 @@ template <> struct Mma32<BF16> {
 };
 
 constexpr int kD = 128;
+constexpr int kPrefillArgBatch = 64;          // batches whose lengths travel in the arguments
 constexpr int kBK = 64;                       // keys per tile
 #ifndef GQA_PREFILL_READ_AHEAD
 #define GQA_PREFILL_READ_AHEAD 8              // LDS operand reads issued ahead of their product
@@ -95,14 +96,48 @@ struct PrefillArgs {
   int n_rb;           // row blocks per (b, kv head)
   float scale_log2;   // |scale| * log2(e)
   uint32_t q_sign;    // 0x80008000 when the scale is negative: Q is negated (exact)
+  int hl_ok;          // past lengths below are valid (B <= kPrefillArgBatch)
+  int hl[kPrefillArgBatch];   // past lengths from the host (the same values as lens)
 };
 
-// Rotate one row's 8 B-operand chunks in place. Chunk ks holds dims
-// 16 ks + 8 c + e: rotate-half pairs (d, d + 64) are chunks (ks, ks + 4) of the
-// same lane, interleaved pairs are neighbours inside a chunk.
+// The cos/sin values one lane needs for its row's 8 B-operand chunks; chunk
+// ks holds dims 16 ks + 8 c + e. Rotate-half pairs (d, d + 64) are chunks
+// (ks, ks + 4) of the same lane and use entry 8 ks + e (table index
+// 16 ks + 8 c + e); interleaved pairs are neighbours inside a chunk and use
+// entry 4 ks + e / 2 (table index 8 ks + 4 c + e / 2). All sixteen 16-byte
+// loads are issued together, before any of them is used.
+struct RotVals {
+  float4 c0, c1, c2, c3, c4, c5, c6, c7;
+  float4 s0, s1, s2, s3, s4, s5, s6, s7;
+};
+
+__device__ __forceinline__ void load_rot(RotVals& r, const float* cosr, const float* sinr, int c,
+                                         int interleaved) {
+  const float4* cv = reinterpret_cast<const float4*>(cosr);
+  const float4* sv = reinterpret_cast<const float4*>(sinr);
+  // float4 index of entry 4 m: rotate-half 4 (m / 2) + 2 c + m % 2, interleaved 2 m + c
+  const int o0 = interleaved ? c : 2 * c;
+  const int st = interleaved ? 2 : 1;
+  auto idx = [&](int m) { return interleaved ? o0 + st * m : 4 * (m >> 1) + o0 + (m & 1); };
+  r.c0 = cv[idx(0)]; r.c1 = cv[idx(1)]; r.c2 = cv[idx(2)]; r.c3 = cv[idx(3)];
+  r.c4 = cv[idx(4)]; r.c5 = cv[idx(5)]; r.c6 = cv[idx(6)]; r.c7 = cv[idx(7)];
+  r.s0 = sv[idx(0)]; r.s1 = sv[idx(1)]; r.s2 = sv[idx(2)]; r.s3 = sv[idx(3)];
+  r.s4 = sv[idx(4)]; r.s5 = sv[idx(5)]; r.s6 = sv[idx(6)]; r.s7 = sv[idx(7)];
+}
+
+__device__ __forceinline__ float rot_entry(const RotVals& r, int i, bool sine) {
+  // i is a compile-time constant after unrolling: picks one register
+  const float4 v = sine ? (i < 4 ? r.s0 : i < 8 ? r.s1 : i < 12 ? r.s2 : i < 16 ? r.s3 :
+                           i < 20 ? r.s4 : i < 24 ? r.s5 : i < 28 ? r.s6 : r.s7)
+                        : (i < 4 ? r.c0 : i < 8 ? r.c1 : i < 12 ? r.c2 : i < 16 ? r.c3 :
+                           i < 20 ? r.c4 : i < 24 ? r.c5 : i < 28 ? r.c6 : r.c7);
+  const int k = i & 3;
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Rotate one row's 8 B-operand chunks in place with the loaded values.
 template <class T>
-__device__ inline void rotate_q(uint4 (&qv)[8], int c, const float* cosr, const float* sinr,
-                                int interleaved) {
+__device__ __forceinline__ void apply_rot(uint4 (&qv)[8], const RotVals& r, int interleaved) {
   using Bits = typename T::bits;
   auto get = [&](int ks, int e) -> Bits {
     const uint32_t w = (&qv[ks].x)[e >> 1];
@@ -118,9 +153,8 @@ __device__ inline void rotate_q(uint4 (&qv)[8], int c, const float* cosr, const 
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = 16 * ks + 8 * c + e;
         Bits x = get(ks, e), y = get(ks + 4, e);
-        rotate_pair<T>(x, y, cosr[j], sinr[j]);
+        rotate_pair<T>(x, y, rot_entry(r, 8 * ks + e, false), rot_entry(r, 8 * ks + e, true));
         put(ks, e, x);
         put(ks + 4, e, y);
       }
@@ -129,9 +163,8 @@ __device__ inline void rotate_q(uint4 (&qv)[8], int c, const float* cosr, const 
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const int j = (16 * ks + 8 * c + e) >> 1;
         Bits x = get(ks, e), y = get(ks, e + 1);
-        rotate_pair<T>(x, y, cosr[j], sinr[j]);
+        rotate_pair<T>(x, y, rot_entry(r, 4 * ks + e / 2, false), rot_entry(r, 4 * ks + e / 2, true));
         put(ks, e, x);
         put(ks, e + 1, y);
       }
@@ -233,13 +266,16 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
         s[h][v] = uint32_t(lim_hi - off) <= uint32_t(span) ? s[h][v] : -INFINITY;
       }
   }
-  float tmax = fmaxf(s[0][0], s[1][0]);
+  // NaN-propagating maximum: unlike fmaxf it needs no quieting of each
+  // operand, so the chain folds into one three-input max per two scores
+  float tmax = __builtin_elementwise_maximum(s[0][0], s[1][0]);
 #pragma unroll
-  for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, fmaxf(s[0][v], s[1][v]));
+  for (int v = 1; v < 16; ++v)
+    tmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(tmax, s[0][v]), s[1][v]);
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
                                                      false, false);
-    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    tmax = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   }
   const float tm = tmax * cs;
   if (__any(tm > rs.m_run + kRescaleSlack)) {
@@ -392,8 +428,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   // one row block: the whole tile loop for 256 query rows
   auto row_block = [&](const int rb) {
   const int nrows = S * G;
-  // lengths are read through a vector load: mark them wave-uniform
-  const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.lens[b], 0, a.M - S));
+  // past lengths come from the arguments when the host could pass them
+  // (no dependent load before the first tile and the rotary tables); a
+  // device read is marked wave-uniform
+  int len_raw;
+  if (a.hl_ok) {
+    len_raw = a.hl[b];                 // a scalar read of the argument block
+    asm volatile("" : "+s"(len_raw));  // keeps it apart from the device read below
+  } else {
+    len_raw = __builtin_amdgcn_readfirstlane(a.lens[b]);
+  }
+  const int L = clamp_len(len_raw, 0, a.M - S);
   const int kvalid = L + S;
 
   const int r0 = rb * kWgRows;
@@ -431,13 +476,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   uint4 qv[8];
   {
     const uint16_t* qrow = a.q + ((int64_t(b) * S + my_i) * a.H + my_h) * kD + 8 * c;
+    // lanes past the last row read a valid row (my_i = S - 1): rows never
+    // mix, and those lanes store nothing, so no load waits on a branch
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qv[ks] = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : make_uint4(0, 0, 0, 0);
-    if (a.rot && row_ok) {
-      const int pos = clamp_len(a.lens[b] + my_i, 0, a.rot_rows - 1);
-      rotate_q<T>(qv, c, a.cosv + int64_t(pos) * (kD / 2), a.sinv + int64_t(pos) * (kD / 2),
-                  a.interleaved);
+    for (int ks = 0; ks < 8; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
+    if (a.rot) {
+      const int pos = clamp_len(len_raw + my_i, 0, a.rot_rows - 1);
+      RotVals rv;
+      load_rot(rv, a.cosv + int64_t(pos) * (kD / 2), a.sinv + int64_t(pos) * (kD / 2), c,
+               a.interleaved);
+      apply_rot<T>(qv, rv, a.interleaved);
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -548,6 +596,9 @@ hipError_t launch_prefill_fast(const Problem& p, hipStream_t st) {
   a.n_rb = ceil_div(p.S * p.G, kWgRows);
   a.scale_log2 = fabsf(p.scale) * kLog2e;
   a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
+  a.hl_ok = p.lens_host != nullptr && p.B <= kPrefillArgBatch;
+  if (a.hl_ok)
+    for (int b = 0; b < p.B; ++b) a.hl[b] = p.lens_host[b];
   const int blocks = a.n_rb * p.B * p.Hkv;
   if (blocks == 0) return hipSuccess;
   if (p.dtype == GQA_FP16)

@@ -95,6 +95,9 @@ SMALL = [
     ("fp32", 2, 9, 4, 2, 8, 40, [0, 31], 7, False, 0, "prefill"),
     ("bf16", 2, 3, 2, 1, 256, 40, [10, 0], -1, True, 0, "prefill"),
     ("fp16", 1, 1, 1, 1, 8, 1, [0], -1, False, 0, "prefill"),               # M = 1
+    # more sequences than travel in the kernel arguments: lengths read on the device
+    ("bf16", 66, 3, 4, 2, 128, 64, [(7 * i) % 62 for i in range(66)], -1, True, 0, "prefill"),
+    ("fp16", 66, 1, 4, 2, 128, 64, [(5 * i) % 64 for i in range(66)], -1, False, 0, "decode"),
 ]
 
 
