@@ -13,8 +13,9 @@ Timing: inputs are resident in HBM before the timed region; each step rotates
 over enough independent input sets (>= 1 GiB) that the 256 MB Infinity Cache
 cannot serve repeated reads. Wall time over K back-to-back steps
 (synchronised on both sides) gives ms_per_step and `value`; a second pass of
-the same K steps with HIP events recorded on the launch stream around each
-call gives the per-call device time used for the roofline fraction.
+the same K steps between one pair of HIP events on the launch stream, queued
+behind a spin kernel so that the device runs the calls back to back, gives
+the device time per call used for the roofline fraction.
 
 The CPU baseline times the fp64 oracle (as it stands) on a bounded sample of
 the decode workload on this host's cores.
@@ -46,11 +47,11 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "54caa92e97d1223b04fed4cf4c977fb27a29f2d47581aabfe7ee69e529ec1555",
+                "809c230f7b77ff499a1f73aed7e30251d640745dba44976a3cd08a7004d7bd71",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
                 "f440e922da4e765bb388c50656d56351503e0ec2972d424801302fc7eea3dba4"},
-    "fetch_kib": 74183.28, "write_kib": 1050.29,
-    "fetch_scale": 524288.0 / 262157.15, "write_scale": 1.0,
+    "fetch_kib": 74198.50, "write_kib": 1050.29,
+    "fetch_scale": 524288.0 / 262157.11, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
@@ -144,15 +145,17 @@ def prefill_flops(case):
 # ----------------------------------------------------------------------------
 
 def time_calls(torch, sets, call, steps, warmup):
-    """Warmup, then two passes of `steps` calls rotating over the input sets.
+    """Warmup, then three passes of `steps` calls rotating over the input sets.
 
     Pass 1 (the timed region): barrier + synchronize, the calls back to back,
-    synchronize; returns wall ms per step. Pass 2: the same calls, each
-    bracketed by HIP events recorded on the launch stream; returns the list
-    of per-call device times in ms (the kernel time the roofline uses). Pass 2
-    is queued behind a spin kernel that outlasts the host's enqueue time, so
-    the device runs the calls back to back and the events see device time
-    only, not host launch latency.
+    synchronize; gives the wall ms per step. Pass 2: one pair of HIP events
+    on the launch stream around the same calls back to back, queued behind a
+    spin kernel that outlasts the host's enqueue time, so the device runs
+    them without gaps from the host; gives the device ms per call the
+    roofline uses (the figure a kernel trace reports, plus the few hundred
+    ns between dispatches). Pass 3: an event pair around each call, for the
+    spread (each pair adds its own dispatch overhead).
+    Returns (wall ms per step, device ms per call, per-call event ms list).
     """
     stream = torch.cuda.current_stream()
     for i in range(warmup):
@@ -166,9 +169,15 @@ def time_calls(torch, sets, call, steps, warmup):
     enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    if gc_was:
-        gc.enable()
     log(f"[bench]   wall {wall:.4f} ms/step, host enqueue {enq * 1e3 / steps:.4f} ms/step")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(spin_cycles(torch, 2.0 * enq + 2e-3))
+    e0.record(stream)
+    for i in range(steps):
+        call(sets[(warmup + i) % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dev = e0.elapsed_time(e1) / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda._sleep(spin_cycles(torch, 2.0 * enq + 2e-3))
@@ -177,8 +186,10 @@ def time_calls(torch, sets, call, steps, warmup):
         call(sets[(warmup + i) % len(sets)])
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return wall, per
+    if gc_was:
+        gc.enable()
+    per = [x.elapsed_time(y) for x, y in ev]
+    return wall, dev, per
 
 
 _SPIN_RATE = []
@@ -209,10 +220,11 @@ def decode_traffic_bytes():
     return int(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
 
 
-def stats(per):
+def stats(dev, per):
     a = np.sort(np.asarray(per))
-    return {"mean_ms": float(a.mean()), "median_ms": float(np.median(a)),
-            "p10_ms": float(a[int(0.1 * (len(a) - 1))]), "p90_ms": float(a[int(0.9 * (len(a) - 1))])}
+    return {"mean_ms": float(dev), "per_call_event_median_ms": float(np.median(a)),
+            "per_call_event_p10_ms": float(a[int(0.1 * (len(a) - 1))]),
+            "per_call_event_p90_ms": float(a[int(0.9 * (len(a) - 1))])}
 
 
 def decode_call(gqa):
@@ -306,9 +318,9 @@ def main():
     log(f"[bench] C2 decode sets: building (lens={c2.seqlens_k.tolist()})")
     sets = make_sets(c2, torch, 2)
     log(f"[bench] C2 decode: {len(sets)} input sets, timing {args.steps} steps")
-    wall, per = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
+    wall, dev, per = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
     c2_bytes = decode_bytes(c2, [int(x) for x in c2.seqlens_k])
-    st2 = stats(per)
+    st2 = stats(dev, per)
     achieved = c2_bytes / (st2["mean_ms"] * 1e-3) / 1e9
     value = c2_bytes / (wall * 1e-3) / 1e9
     del sets
@@ -321,9 +333,9 @@ def main():
         sets = make_sets(c3, torch, 3)
         steps = max(5, args.steps // 2)
         log(f"[bench] C3 prefill: {len(sets)} input sets, timing {steps} steps")
-        w3, per3 = time_calls(torch, sets, prefill_call(gqa), steps, max(2, args.warmup // 2))
+        w3, dev3, per3 = time_calls(torch, sets, prefill_call(gqa), steps, max(2, args.warmup // 2))
         fl = prefill_flops(c3)
-        s3 = stats(per3)
+        s3 = stats(dev3, per3)
         tf = fl / (s3["mean_ms"] * 1e-3) / 1e12
         extra["prefill_c3"] = {"workload": "bf16 causal prefill B=4 H=32 Hkv=8 D=128 S=2048 rotary",
                                "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
@@ -335,9 +347,9 @@ def main():
         log("[bench] C4 continuation sets: building")
         sets = make_sets(c4, torch, 4)
         log(f"[bench] C4 continuation: {len(sets)} input sets")
-        w4, per4 = time_calls(torch, sets, prefill_call(gqa), args.steps, args.warmup)
+        w4, dev4, per4 = time_calls(torch, sets, prefill_call(gqa), args.steps, args.warmup)
         fl = prefill_flops(c4)
-        s4 = stats(per4)
+        s4 = stats(dev4, per4)
         tf = fl / (s4["mean_ms"] * 1e-3) / 1e12
         extra["continuation_c4"] = {"workload": "fp16 ragged continuation B=8 H=28 Hkv=4 D=128 S=128",
                                     "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
@@ -350,8 +362,8 @@ def main():
         log("[bench] C5 window decode sets: building")
         sets = make_sets(c5, torch, 5)
         log(f"[bench] C5 window decode: {len(sets)} input sets")
-        w5, per5 = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
-        s5 = stats(per5)
+        w5, dev5, per5 = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
+        s5 = stats(dev5, per5)
         att = decode_bytes(c5, [4095] * 8, window=4096)
         shift = 8 * 8 * 4095 * 128 * 2 * 2 * 2      # read + write of every kept row, K and V
         extra["window_decode_c5"] = {
