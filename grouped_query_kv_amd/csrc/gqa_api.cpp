@@ -166,7 +166,7 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
   e = launch_append(P, evicted_lengths, hs);
   if (e != hipSuccess) return hip_fail(e, "append");
   if (prefill_fast_supported(P)) {
-    e = launch_prefill_fast(P, hs);
+    e = launch_prefill_fast(P, ws, lay, hs);
     if (e != hipSuccess) return hip_fail(e, "prefill");
   } else {
     e = launch_attention_simple(P, hs);
@@ -200,10 +200,24 @@ WorkspaceLayout workspace_layout(const gqa_shape& s) {
   // fused-eviction halo rows (decode): [2][B, Hkv, ceil(M / 16), D] in the dtype
   int64_t dhalo = 0;
   if (D == 128 && s.dtype != GQA_FP32) dhalo = 2 * B * Hkv * ((M + 15) / 16) * D * 2;
+  // prefill split partials: [row blocks, splits] slots (only when splitting)
+  int64_t pf_items = 0, pf_partial = 0;
+  if (D == 128 && s.dtype != GQA_FP32 && s.new_tokens > 0) {
+    const int ns = prefill_split_count(B, s.new_tokens, G, Hkv, M);
+    if (ns > 1) {
+      pf_items = ((s.new_tokens * G + kPrefillWgRows - 1) / kPrefillWgRows) * B * Hkv;
+      pf_partial = pf_items * ns * int64_t(kPrefillSlotFloats) * 4;
+    }
+  }
   l.scratch = l.counters_bytes;
   l.decode_halo = l.scratch + align256(size_t(partial));
-  l.scratch_bytes = align256(std::max(size_t(halo), align256(size_t(partial)) + size_t(dhalo)));
-  l.total = l.scratch + l.scratch_bytes;
+  // the scratch area is reused: an eviction before the prefill kernel has
+  // finished with it (stream order), and decode runs in calls of its own
+  l.prefill_partials = l.scratch;
+  l.scratch_bytes = align256(std::max({size_t(halo), align256(size_t(partial)) + size_t(dhalo),
+                                       size_t(pf_partial)}));
+  l.prefill_counters = l.scratch + l.scratch_bytes;
+  l.total = l.prefill_counters + align256(size_t(pf_items) * sizeof(int32_t));
   return l;
 }
 

@@ -41,8 +41,33 @@ struct WorkspaceLayout {
   size_t scratch;         // shared by decode partials and eviction halos
   size_t scratch_bytes;
   size_t decode_halo;     // fused-eviction halo rows, after the decode partials
+  size_t prefill_counters;  // int32 [prefill row blocks] split counters (kept zero)
+  size_t prefill_partials;  // split partials of the prefill kernel (in the scratch area)
   size_t total;
 };
+
+// Prefill: 256 query rows per workgroup. When a call has too few row blocks
+// to fill the chip, each row block's key tiles are cut into `splits` ranges
+// taken by separate workgroups, merged by the last one to finish. A split
+// partial holds, for each of the 512 lanes, its 64 unnormalised output
+// values, the row's exponent base and the row's weight sum (fp32).
+constexpr int kPrefillWgRows = 256;
+constexpr int kPrefillTargetWorkgroups = 256;   // one per CU
+constexpr int kPrefillMaxSplits = 4;
+constexpr size_t kPrefillSlotFloats = 512 * 64 + 2 * 512;
+
+// A function of the shape only (the workspace is sized from it): split when
+// the row blocks fill less than three quarters of the chip and the buffer
+// holds at least 8 tiles of 64 keys per split.
+inline int prefill_split_count(int64_t B, int64_t S, int64_t G, int64_t Hkv, int64_t M) {
+  const int64_t items = ((S * G + kPrefillWgRows - 1) / kPrefillWgRows) * B * Hkv;
+  if (items <= 0 || 4 * items >= 3 * kPrefillTargetWorkgroups) return 1;
+  int64_t ns = (kPrefillTargetWorkgroups + items - 1) / items;
+  ns = ns < kPrefillMaxSplits ? ns : kPrefillMaxSplits;
+  const int64_t by_len = ((M + 63) / 64) / 8;
+  ns = ns < by_len ? ns : by_len;
+  return ns < 1 ? 1 : int(ns);
+}
 
 // Decode: fast split-KV kernel limits.
 #ifndef GQA_DECODE_WG_WAVES
@@ -109,6 +134,7 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
 
 // Fast prefill (fp16/bf16, D == 128): MFMA flash attention over the cache.
 bool prefill_fast_supported(const Problem& p);
-hipError_t launch_prefill_fast(const Problem& p, hipStream_t st);
+hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
+                               hipStream_t st);
 
 }  // namespace gqa

@@ -77,6 +77,7 @@ constexpr int kBK = 64;                       // keys per tile
 constexpr int kWaves = 8;                     // two groups of four (one wave of each per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWgRows = 32 * kWaves;          // query rows per workgroup
+static_assert(kWgRows == kPrefillWgRows && kThreads == 512, "split slots assume 512 lanes x 256 rows");
 constexpr float kLog2e = 1.4426950408889634f;
 // The running maximum used in the exponent is refreshed only when a score
 // exceeds it by more than this many binary orders, so weights stay <= 2^8:
@@ -96,6 +97,10 @@ struct PrefillArgs {
   int n_rb;           // row blocks per (b, kv head)
   float scale_log2;   // |scale| * log2(e)
   uint32_t q_sign;    // 0x80008000 when the scale is negative: Q is negated (exact)
+  int n_items0;       // n_rb * B * Hkv row blocks
+  int splits;         // key ranges per row block (1: no split)
+  float* partials;    // splits > 1: [row block][split] slots of kPrefillSlotFloats
+  int* counters;      // splits > 1: per row block, finished splits (kept zero)
   int hl_ok;          // past lengths below are valid (B <= kPrefillArgBatch)
   int hl[kPrefillArgBatch];   // past lengths from the host (the same values as lens)
 };
@@ -411,6 +416,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_odd[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_even[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_odd[kTileBytes];
+  __shared__ int sh_last;                       // split merge: this workgroup finished last
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -421,7 +427,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
 #endif
   const int col = lane & 31, c = lane >> 5;     // S^T column (= the lane's row), k half
   const int units = a.B * a.Hkv;
-  const int bg = int(blockIdx.x) % units;
+  // workgroup -> (split, row block): all first splits, longest row blocks
+  // first, then all second splits, ...
+  const int split = int(blockIdx.x) / a.n_items0;
+  const int item = int(blockIdx.x) % a.n_items0;
+  const int bg = item % units;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.G, S = a.S;
 
@@ -460,10 +470,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int w_kend = L + w_ihi + 1;
   const int w_full_lo = a.W > 0 ? L + w_ihi - a.W + 1 : 0;  // keys >= this: no window cut
   const int w_full_hi = L + w_ilo;                          // keys <= this: no causal cut
-  const int t_begin = __builtin_amdgcn_readfirstlane(wg_kstart / kBK);
-  const int t_end = __builtin_amdgcn_readfirstlane((wg_kend + kBK - 1) / kBK);
-  const int wt0 = wave_has_rows ? w_kstart / kBK : t_end;
-  const int wt1 = wave_has_rows ? (w_kend + kBK - 1) / kBK : t_end;
+  // this split's share of the row block's tiles (all of them without a split)
+  const int rb_t0 = wg_kstart / kBK, rb_t1 = (wg_kend + kBK - 1) / kBK;
+  const int t_begin = __builtin_amdgcn_readfirstlane(rb_t0 + (rb_t1 - rb_t0) * split / a.splits);
+  const int t_end = __builtin_amdgcn_readfirstlane(rb_t0 + (rb_t1 - rb_t0) * (split + 1) / a.splits);
+  const int wt0 = wave_has_rows ? max(w_kstart / kBK, t_begin) : t_end;
+  const int wt1 = wave_has_rows ? min((w_kend + kBK - 1) / kBK, t_end) : t_end;
 
   const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
   const uint16_t* kc = a.k_cache + kvbase;
@@ -556,10 +568,67 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     }
   }
 
-  if (!row_ok) return;
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs.l), __float_as_uint(rs.l),
                                                     false, false);
-  const float inv = 1.f / (__uint_as_float(lsw[0]) + __uint_as_float(lsw[1]));
+  float l_row = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // the row's weight sum
+  if (a.splits > 1) {
+    // publish this split's partial, count it in; the last split to finish
+    // merges all of them in split order (the same sum whoever is last)
+    float* slots = a.partials + int64_t(item) * a.splits * int64_t(kPrefillSlotFloats);
+    float* mine = slots + int64_t(split) * kPrefillSlotFloats;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        __hip_atomic_store(mine + (wave * 64 + dt * 16 + v) * 64 + lane, o[dt][v],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + 512 * 64 + tid, rs.m_use, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + 512 * 65 + tid, l_row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial has landed
+    __syncthreads();
+    if (tid == 0) {
+      const int prev = __hip_atomic_fetch_add(a.counters + item, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      sh_last = prev == a.splits - 1;
+      if (sh_last) __hip_atomic_store(a.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!sh_last) return;
+    float mj[kPrefillMaxSplits], lj[kPrefillMaxSplits];
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kPrefillMaxSplits; ++j) {
+      mj[j] = -INFINITY;
+      lj[j] = 0.f;
+      if (j < a.splits) {
+        const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
+        mj[j] = __hip_atomic_load(sj + 512 * 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lj[j] = __hip_atomic_load(sj + 512 * 65 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lj[j] > 0.f) M = fmaxf(M, mj[j]);   // a split that saw no key of the row adds nothing
+      }
+    }
+    l_row = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPrefillMaxSplits; ++j) {
+      if (j >= a.splits) break;
+      const float wj = lj[j] > 0.f ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
+      l_row = fmaf(lj[j], wj, l_row);
+      const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          o[dt][v] = fmaf(__hip_atomic_load(sj + (wave * 64 + dt * 16 + v) * 64 + lane,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                          wj, o[dt][v]);
+    }
+  }
+  if (!row_ok) return;
+  const float inv = 1.f / l_row;
   uint16_t* orow = a.out + ((int64_t(b) * S + my_i) * a.H + my_h) * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -573,17 +642,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     }
   };
 
-  row_block(a.n_rb - 1 - int(blockIdx.x) / units);      // longest row blocks first
+  row_block(a.n_rb - 1 - item / units);      // longest row blocks first
 }
 
 }  // namespace
 
 bool prefill_fast_supported(const Problem& p) {
-  // buffer ranges are 32-bit byte counts
-  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.M <= (1 << 23);
+  // buffer ranges are 32-bit byte counts; cos/sin rows are read as float4
+  const bool rot_aligned = !p.rot || ((reinterpret_cast<uintptr_t>(p.cos) |
+                                       reinterpret_cast<uintptr_t>(p.sin)) & 15) == 0;
+  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.M <= (1 << 23) &&
+         rot_aligned;
 }
 
-hipError_t launch_prefill_fast(const Problem& p, hipStream_t st) {
+hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
+                               hipStream_t st) {
   PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(p.q);
   a.k_cache = static_cast<const uint16_t*>(p.k_cache);
@@ -599,8 +672,14 @@ hipError_t launch_prefill_fast(const Problem& p, hipStream_t st) {
   a.hl_ok = p.lens_host != nullptr && p.B <= kPrefillArgBatch;
   if (a.hl_ok)
     for (int b = 0; b < p.B; ++b) a.hl[b] = p.lens_host[b];
-  const int blocks = a.n_rb * p.B * p.Hkv;
-  if (blocks == 0) return hipSuccess;
+  a.n_items0 = a.n_rb * p.B * p.Hkv;
+  if (a.n_items0 == 0) return hipSuccess;
+  a.splits = prefill_split_count(p.B, p.S, p.G, p.Hkv, p.M);
+  if (a.splits > 1) {
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.prefill_partials);
+    a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + lay.prefill_counters);
+  }
+  const int blocks = a.n_items0 * a.splits;
   if (p.dtype == GQA_FP16)
     hipLaunchKernelGGL(prefill_kernel<F16>, dim3(blocks), dim3(kThreads), 0, st, a);
   else

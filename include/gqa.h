@@ -130,7 +130,9 @@ gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts,
 /*
  * The whole op for S >= 1 new tokens per sequence (steps 1-4): fused
  * flash-style attention on MFMA for fp16/bf16 with D = 128, a plain
- * kernel otherwise. With a window, S > 1 and an eviction needed by some
+ * kernel otherwise. When the shape has too few 256-row blocks to fill the
+ * GPU, each block's key range is split over several workgroups whose
+ * partials (kept in the workspace) the last one merges by log-sum-exp. With a window, S > 1 and an eviction needed by some
  * sequence, returns GQA_ERR_UNSUPPORTED (attention would need the
  * pre-eviction keys). Source: all three pages as summarised above; the
  * key-tile loop ends at each sequence's length ("KV Cache", notes and

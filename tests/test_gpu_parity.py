@@ -95,6 +95,11 @@ SMALL = [
     ("fp32", 2, 9, 4, 2, 8, 40, [0, 31], 7, False, 0, "prefill"),
     ("bf16", 2, 3, 2, 1, 256, 40, [10, 0], -1, True, 0, "prefill"),
     ("fp16", 1, 1, 1, 1, 8, 1, [0], -1, False, 0, "prefill"),               # M = 1
+    # few row blocks and a long buffer: key ranges split over 4 workgroups,
+    # including splits that see no key at all (a sequence with L = 0)
+    ("fp16", 3, 40, 8, 2, 128, 2048, [0, 700, 1999], -1, True, 0, "prefill"),
+    ("bf16", 2, 33, 16, 2, 128, 2048, [1500, 0], 100, False, 0, "prefill"),
+    ("bf16", 2, 7, 8, 8, 128, 1024, [1017, 300], -1, False, 0, "prefill"),
     # more sequences than travel in the kernel arguments: lengths read on the device
     ("bf16", 66, 3, 4, 2, 128, 64, [(7 * i) % 62 for i in range(66)], -1, True, 0, "prefill"),
     ("fp16", 66, 1, 4, 2, 128, 64, [(5 * i) % 64 for i in range(66)], -1, False, 0, "decode"),
