@@ -98,13 +98,20 @@ __device__ inline void rot_inter8(uint4& x, const float* c4, const float* s4) {
   }
 }
 
+// Fused append for 2-byte types with D % 16 == 0: K and V in one launch. A
+// thread owns 16 elements of one source row, split over two 16-byte runs
+// (rotate-half: the same 8 offsets in each half, so a run pairs with the
+// other; interleaved: two adjacent runs of 4 pairs each). K is rotated when
+// tables are given, V is copied; index arithmetic once per thread.
 template <class T>
-__global__ void __launch_bounds__(256) rotary_rows_vec_kernel(
-    const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, const int32_t* __restrict__ lens,
-    int B, int S, int Hkv, int D, int M, const float* __restrict__ cosv,
-    const float* __restrict__ sinv, int rot_rows, int interleaved, int evicted) {
+__global__ void __launch_bounds__(256) append_rows_vec_kernel(
+    const uint16_t* __restrict__ k_src, uint16_t* __restrict__ k_dst,
+    const uint16_t* __restrict__ v_src, uint16_t* __restrict__ v_dst,
+    const int32_t* __restrict__ lens, int B, int S, int Hkv, int D, int M,
+    const float* __restrict__ cosv, const float* __restrict__ sinv, int rot, int rot_rows,
+    int interleaved, int evicted) {
   const int half = D / 2;
-  const int cpr = half / 8;                       // threads per row: 8 pairs each
+  const int cpr = D / 16;                         // threads per row: 16 elements each
   const int64_t total = int64_t(B) * S * Hkv * cpr;
   for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < total;
        idx += int64_t(gridDim.x) * blockDim.x) {
@@ -113,40 +120,40 @@ __global__ void __launch_bounds__(256) rotary_rows_vec_kernel(
     const int g = int(r % Hkv);
     const int64_t bi = r / Hkv;
     const int i = int(bi % S), b = int(bi / S);
-    const int pos = clamp_len(clamp_len(lens[b], 0, M) + i, 0, rot_rows - 1);
-    const float* cr = cosv + int64_t(pos) * half;
-    const float* sr = sinv + int64_t(pos) * half;
-    const uint16_t* srow = src + r * D;
     const int row = dest_base(lens, b, S, M, evicted != 0) + i;
-    uint16_t* drow = dst + ((int64_t(b) * Hkv + g) * M + row) * D;
-    if (!interleaved) {
-      const int j0 = 8 * ch;                      // pairs (j, j + D/2), j = j0 .. j0 + 7
-      uint4 x = *reinterpret_cast<const uint4*>(srow + j0);
-      uint4 y = *reinterpret_cast<const uint4*>(srow + j0 + half);
-      const float4 c0 = *reinterpret_cast<const float4*>(cr + j0);
-      const float4 c1 = *reinterpret_cast<const float4*>(cr + j0 + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(sr + j0);
-      const float4 s1 = *reinterpret_cast<const float4*>(sr + j0 + 4);
-      const float c8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float s8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      rot8<T>(x, y, c8, s8);
-      *reinterpret_cast<uint4*>(drow + j0) = x;
-      *reinterpret_cast<uint4*>(drow + j0 + half) = y;
-    } else {
-      const int e0 = 16 * ch;                     // elements e0 .. e0 + 15 = pairs 8 ch .. + 7
-      uint4 x = *reinterpret_cast<const uint4*>(srow + e0);
-      uint4 y = *reinterpret_cast<const uint4*>(srow + e0 + 8);
-      const float4 c0 = *reinterpret_cast<const float4*>(cr + 8 * ch);
-      const float4 c1 = *reinterpret_cast<const float4*>(cr + 8 * ch + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(sr + 8 * ch);
-      const float4 s1 = *reinterpret_cast<const float4*>(sr + 8 * ch + 4);
-      const float ca[4] = {c0.x, c0.y, c0.z, c0.w}, sa[4] = {s0.x, s0.y, s0.z, s0.w};
-      const float cb[4] = {c1.x, c1.y, c1.z, c1.w}, sb[4] = {s1.x, s1.y, s1.z, s1.w};
-      rot_inter8<T>(x, ca, sa);
-      rot_inter8<T>(y, cb, sb);
-      *reinterpret_cast<uint4*>(drow + e0) = x;
-      *reinterpret_cast<uint4*>(drow + e0 + 8) = y;
+    const int64_t doff = ((int64_t(b) * Hkv + g) * M + row) * D;
+    // the two 16-byte runs of this thread (element offsets within the row)
+    const int o1 = interleaved ? 16 * ch : 8 * ch;
+    const int o2 = interleaved ? 16 * ch + 8 : 8 * ch + half;
+    const uint16_t* ks = k_src + r * D;
+    const uint16_t* vs = v_src + r * D;
+    uint4 x = *reinterpret_cast<const uint4*>(ks + o1);
+    uint4 y = *reinterpret_cast<const uint4*>(ks + o2);
+    const uint4 vx = *reinterpret_cast<const uint4*>(vs + o1);
+    const uint4 vy = *reinterpret_cast<const uint4*>(vs + o2);
+    if (rot) {
+      const int pos = clamp_len(clamp_len(lens[b], 0, M) + i, 0, rot_rows - 1);
+      const float* cr = cosv + int64_t(pos) * half + 8 * ch;   // pairs 8 ch .. 8 ch + 7
+      const float* sr = sinv + int64_t(pos) * half + 8 * ch;
+      const float4 c0 = *reinterpret_cast<const float4*>(cr);
+      const float4 c1 = *reinterpret_cast<const float4*>(cr + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sr);
+      const float4 s1 = *reinterpret_cast<const float4*>(sr + 4);
+      if (!interleaved) {
+        const float c8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float s8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        rot8<T>(x, y, c8, s8);
+      } else {
+        const float ca[4] = {c0.x, c0.y, c0.z, c0.w}, sa[4] = {s0.x, s0.y, s0.z, s0.w};
+        const float cb[4] = {c1.x, c1.y, c1.z, c1.w}, sb[4] = {s1.x, s1.y, s1.z, s1.w};
+        rot_inter8<T>(x, ca, sa);
+        rot_inter8<T>(y, cb, sb);
+      }
     }
+    *reinterpret_cast<uint4*>(k_dst + doff + o1) = x;
+    *reinterpret_cast<uint4*>(k_dst + doff + o2) = y;
+    *reinterpret_cast<uint4*>(v_dst + doff + o1) = vx;
+    *reinterpret_cast<uint4*>(v_dst + doff + o2) = vy;
   }
 }
 
@@ -182,16 +189,6 @@ hipError_t copy_rows(const void* src, void* dst, const Problem& p, bool evicted,
 template <class T>
 hipError_t rotary_rows(const Problem& p, bool evicted, hipStream_t st) {
   using Bits = typename T::bits;
-  if constexpr (sizeof(Bits) == 2) {
-    if (p.D % 16 == 0) {
-    const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 16);
-    hipLaunchKernelGGL(rotary_rows_vec_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(p.k_new), static_cast<uint16_t*>(p.k_cache),
-                       p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,
-                       p.interleaved, int(evicted));
-      return hipGetLastError();
-    }
-  }
   const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 2);
   hipLaunchKernelGGL(rotary_rows_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
                      static_cast<const Bits*>(p.k_new), static_cast<Bits*>(p.k_cache),
@@ -200,10 +197,28 @@ hipError_t rotary_rows(const Problem& p, bool evicted, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <class T>
+hipError_t append_rows_vec(const Problem& p, bool evicted, hipStream_t st) {
+  const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 16);
+  hipLaunchKernelGGL(append_rows_vec_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(p.k_new), static_cast<uint16_t*>(p.k_cache),
+                     static_cast<const uint16_t*>(p.v_new), static_cast<uint16_t*>(p.v_cache),
+                     p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot, p.rot_rows,
+                     p.interleaved, int(evicted));
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_append(const Problem& p, bool evicted, hipStream_t st) {
   if (p.B == 0 || p.S == 0) return hipSuccess;
+  // fp16/bf16 rows of 16-element runs: K and V in one launch (float4 rotary
+  // reads need 16-byte aligned tables)
+  const bool tables_aligned = !p.rot || ((reinterpret_cast<uintptr_t>(p.cos) |
+                                          reinterpret_cast<uintptr_t>(p.sin)) & 15) == 0;
+  if (p.dtype != GQA_FP32 && p.D % 16 == 0 && tables_aligned)
+    return p.dtype == GQA_FP16 ? append_rows_vec<F16>(p, evicted, st)
+                               : append_rows_vec<BF16>(p, evicted, st);
   hipError_t e;
   if (p.rot) {
     if (p.dtype == GQA_FP32) e = rotary_rows<F32>(p, evicted, st);

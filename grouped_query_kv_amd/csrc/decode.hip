@@ -99,6 +99,7 @@ struct DecodeArgs {
   int n_hg, hg_size;
   int workers;                          // waves in the launch that take a slice
   int64_t total;                        // T: blocks over all units
+  int fits32;                           // (T + 1) * workers < 2^32: slice bounds in 32 bits
   float scale_log2;
   int32_t hl[kDecodeArgBatch];          // past lengths
   int32_t pb[kDecodeArgBatch + 1];      // first global block of sequence b (all its units)
@@ -394,6 +395,8 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
 // The worker (wave of the launch) that owns global block x: worker w takes
 // the slice [w T / N, (w + 1) T / N).
 __device__ inline int owner_worker(const DecodeArgs& a, int64_t x) {
+  if (a.fits32)   // the usual case: a 32-bit division (the 64-bit one is a long sequence)
+    return int((uint32_t(x + 1) * uint32_t(a.workers) - 1u) / uint32_t(a.total));
   return int(((x + 1) * a.workers - 1) / a.total);
 }
 
@@ -592,8 +595,16 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   unsigned char* vt = lds + wv * kWaveLds + kSlotBytes;     // the V tile while streaming
   if (lane < 4) sh_tab[wv][lane >> 1][lane & 1] = -1;
 
-  const int64_t S = worker < a.workers ? (int64_t(worker) * a.total) / a.workers : 0;
-  const int64_t E = worker < a.workers ? (int64_t(worker + 1) * a.total) / a.workers : 0;
+  int64_t S = 0, E = 0;
+  if (worker < a.workers) {
+    if (a.fits32) {
+      S = uint32_t(worker) * uint32_t(a.total) / uint32_t(a.workers);
+      E = uint32_t(worker + 1) * uint32_t(a.total) / uint32_t(a.workers);
+    } else {
+      S = (int64_t(worker) * a.total) / a.workers;
+      E = (int64_t(worker + 1) * a.total) / a.workers;
+    }
+  }
   if (S < E) {
     Blk cur = locate(a, S);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
@@ -651,13 +662,17 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   // ---- combine the partials of each cut unit in slice order. The table
   // is read once (one LDS round trip); entries of a unit are consecutive in
   // slice order (empty entries between them are skipped). ----
+  // every lane reads the same entries: mark them wave-uniform, so that the
+  // per-sequence arguments they index are scalar reads, not vector loads
+  // from the argument block that wait a full memory round trip
   int tb[2 * kDecodeWaves], tu[2 * kDecodeWaves];
 #pragma unroll
   for (int f = 0; f < 2 * kDecodeWaves; ++f) {
-    tb[f] = sh_tab[f >> 1][f & 1][0];
-    tu[f] = sh_tab[f >> 1][f & 1][1];
+    tb[f] = __builtin_amdgcn_readfirstlane(sh_tab[f >> 1][f & 1][0]);
+    tu[f] = __builtin_amdgcn_readfirstlane(sh_tab[f >> 1][f & 1][1]);
   }
   int nglob = 0, gb0 = 0, gub0 = 0, gb1 = 0, gub1 = 0;
+  int gunit0 = 0, gunit1 = 0, gneed0 = 0, gneed1 = 0;   // counter index, earlier arrivals
   int prev_b = -1, prev_ub = -1;
 #pragma unroll
   for (int e = 0; e < 2 * kDecodeWaves; ++e) {
@@ -701,7 +716,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       }
     }
     if (!inside) {
-      if (nglob == 0) { gb0 = b; gub0 = ub; } else { gb1 = b; gub1 = ub; }
+      const int need = u.w_last / kDecodeWaves - u.w_first / kDecodeWaves;
+      if (nglob == 0) { gb0 = b; gub0 = ub; gunit0 = u.unit; gneed0 = need; }
+      else { gb1 = b; gub1 = ub; gunit1 = u.unit; gneed1 = need; }
       ++nglob;
     }
   }
@@ -709,11 +726,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial stores have landed
   __syncthreads();
   if (tid < nglob) {
-    const int b = tid ? gb1 : gb0, ub = tid ? gub1 : gub0;
-    const UnitInfo u = unit_info(a, b, ub);
-    const int prev = __hip_atomic_fetch_add(a.counters + u.unit, 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    sh_flag[tid] = prev == u.w_last / kDecodeWaves - u.w_first / kDecodeWaves;
+    // counted in; the workgroup that completes the count merges
+    const int prev = __hip_atomic_fetch_add(a.counters + (tid ? gunit1 : gunit0), 1,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_flag[tid] = prev == (tid ? gneed1 : gneed0);
   }
   __syncthreads();
   float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
@@ -797,6 +813,7 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   }
   while (workers > 1 && max_unit * workers > int64_t(kMergeMax - 1) * total) workers /= 2;
   a.workers = int(workers);
+  a.fits32 = (total + 1) * workers < (int64_t(1) << 32) ? 1 : 0;
   const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
   if (a.shift) {
     hipLaunchKernelGGL(shift_halo_kernel, dim3(ceil_div(a.hb, 16), p.Hkv * 2, p.B), dim3(256), 0, st, a);
