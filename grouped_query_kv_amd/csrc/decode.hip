@@ -250,14 +250,16 @@ struct Q4 {
 
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4) {
+__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
   // fused eviction: key `row` is buffer row row + d. The first row of the
-  // next block's sources is overwritten by that block's shifted stores, so
-  // the last key of a block comes from the copy taken before the kernel; the
-  // new-token key has no buffer row (past the end: any valid row, replaced).
+  // next block's sources is overwritten by that block's shifted stores. When
+  // this wave also takes the next block, it loads this block well before it
+  // stores the next one; when the next block starts another wave's slice,
+  // the last key comes from the copy taken before the kernel. The new-token
+  // key has no buffer row (past the end: any valid row, replaced).
   int src = row + k.d;
-  const bool halo = k.d && n == kKeys - 1 && k.i + 1 < k.nb;
+  const bool halo = k.d && slice_end && n == kKeys - 1 && k.i + 1 < k.nb;
   src = src < a.M ? src : row;
   const int64_t hrow = ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD + 8 * q4;
   const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
@@ -608,7 +610,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (S < E) {
     Blk cur = locate(a, S);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
-    KV rc = load_kv(a, cur, n, q4);
+    KV rc = load_kv(a, cur, n, q4, S + 1 >= E);
     Acc s;
     acc_reset(s);
     bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
@@ -618,7 +620,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // next (x + 2), clamped to the slice's last block. Q rows are loaded when
     // their unit starts (a small, cache-resident read).
     Blk nxt = S + 1 < E ? next_block(a, cur) : cur;        // block x + 1
-    KV r1 = load_kv(a, nxt, n, q4);
+    KV r1 = load_kv(a, nxt, n, q4, S + 2 >= E);
     Blk ahead = S + 2 < E ? next_block(a, nxt) : nxt;       // block x + 2
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
@@ -626,7 +628,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv(a, ahead, n, q4);
+      r_fill = load_kv(a, ahead, n, q4, x + 3 >= E);   // ahead = min(x + 2, E - 1)
       compute<T>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
@@ -737,22 +739,32 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds);
 }
 
-// Fused eviction, before the decode kernel: for every full sequence, unit
-// (b, g) and block i but the last, copy buffer row 16 (i + 1) + ... the first
-// source row of block i + 1, i.e. key 16 i + 15's source, which block i + 1's
-// shifted stores overwrite. One workgroup per (b, g, K|V).
+// Fused eviction, before the decode kernel: for the last block i of every
+// worker's slice whose unit goes on into the next worker's slice, copy the
+// first source row of block i + 1 (key 16 i + 15's source), which block
+// i + 1's shifted stores, made by another wave, may overwrite first.
 __global__ void __launch_bounds__(256) shift_halo_kernel(DecodeArgs a) {
-  // one 16-byte chunk per thread: 16 halo rows per block, every copy in flight at once
-  const int y = blockIdx.y, b = blockIdx.z;
-  const int g = y >> 1;
-  const Seq s = seq_of(a, b);
-  const int i = blockIdx.x * 16 + (threadIdx.x >> 4), part = threadIdx.x & 15;
-  if (!s.d || i >= s.nb - 1) return;
-  const uint16_t* src = ((y & 1) ? a.v_cache : a.k_cache) + (int64_t(b) * a.Hkv + g) * a.M * kD;
-  uint16_t* dst = ((y & 1) ? a.halo_v : a.halo_k) + (int64_t(b) * a.Hkv + g) * a.hb * kD;
-  const int row = s.kstart + kKeys * (i + 1) + s.d - 1;     // = key 16 i + 15 + d
-  *reinterpret_cast<uint4*>(dst + int64_t(i) * kD + 8 * part) =
-      *reinterpret_cast<const uint4*>(src + int64_t(row) * kD + 8 * part);
+  // 16 workers per block, one 16-byte chunk of one row per thread: for the
+  // last block of each worker's slice, when its unit continues into the
+  // next worker's slice, save the next block's first source row
+  const int w = blockIdx.x * 16 + (threadIdx.x >> 4), part = threadIdx.x & 15;
+  if (w >= a.workers) return;
+  int64_t S, E;
+  if (a.fits32) {
+    S = uint32_t(w) * uint32_t(a.total) / uint32_t(a.workers);
+    E = uint32_t(w + 1) * uint32_t(a.total) / uint32_t(a.workers);
+  } else {
+    S = (int64_t(w) * a.total) / a.workers;
+    E = (int64_t(w + 1) * a.total) / a.workers;
+  }
+  if (S >= E) return;
+  const Blk k = locate(a, E - 1);
+  if (!k.d || k.i + 1 >= k.nb) return;
+  const bool vside = blockIdx.y != 0;
+  const uint16_t* src = (vside ? k.vc : k.kc) + int64_t(k.kb + kKeys - 1 + k.d) * kD;
+  uint16_t* dst = (vside ? a.halo_v : a.halo_k) +
+                  ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD;
+  *reinterpret_cast<uint4*>(dst + 8 * part) = *reinterpret_cast<const uint4*>(src + 8 * part);
 }
 
 }  // namespace
@@ -816,7 +828,7 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.fits32 = (total + 1) * workers < (int64_t(1) << 32) ? 1 : 0;
   const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
   if (a.shift) {
-    hipLaunchKernelGGL(shift_halo_kernel, dim3(ceil_div(a.hb, 16), p.Hkv * 2, p.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(shift_halo_kernel, dim3(ceil_div(a.workers, 16), 2), dim3(256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
