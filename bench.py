@@ -47,10 +47,10 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "809c230f7b77ff499a1f73aed7e30251d640745dba44976a3cd08a7004d7bd71",
+                "adbc056a5dfe72c3514c02ff1176820930be48382309fcbb5c4b5f035619dac2",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "f440e922da4e765bb388c50656d56351503e0ec2972d424801302fc7eea3dba4"},
-    "fetch_kib": 74198.50, "write_kib": 1050.29,
+                "d027341bb70095180b1770782f0b845e62eb2f2be5daa28a5e726f7d822827ff"},
+    "fetch_kib": 74158.08, "write_kib": 1050.28,
     "fetch_scale": 524288.0 / 262157.11, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}

@@ -743,12 +743,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 // worker's slice whose unit goes on into the next worker's slice, copy the
 // first source row of block i + 1 (key 16 i + 15's source), which block
 // i + 1's shifted stores, made by another wave, may overwrite first.
-__global__ void __launch_bounds__(256) shift_halo_kernel(DecodeArgs a) {
-  // 16 workers per block, one 16-byte chunk of one row per thread: for the
-  // last block of each worker's slice, when its unit continues into the
-  // next worker's slice, save the next block's first source row
-  const int w = blockIdx.x * 16 + (threadIdx.x >> 4), part = threadIdx.x & 15;
-  if (w >= a.workers) return;
+__global__ void __launch_bounds__(64) shift_halo_kernel(DecodeArgs a) {
+  // one wave per worker (its plan values stay scalar): lanes 0-15 copy the K
+  // row, lanes 16-31 the V row, 16 bytes each
+  const int w = blockIdx.x, lane = threadIdx.x;
   int64_t S, E;
   if (a.fits32) {
     S = uint32_t(w) * uint32_t(a.total) / uint32_t(a.workers);
@@ -757,10 +755,11 @@ __global__ void __launch_bounds__(256) shift_halo_kernel(DecodeArgs a) {
     S = (int64_t(w) * a.total) / a.workers;
     E = (int64_t(w + 1) * a.total) / a.workers;
   }
-  if (S >= E) return;
+  if (S >= E || lane >= 32) return;
   const Blk k = locate(a, E - 1);
   if (!k.d || k.i + 1 >= k.nb) return;
-  const bool vside = blockIdx.y != 0;
+  const bool vside = lane >= 16;
+  const int part = lane & 15;
   const uint16_t* src = (vside ? k.vc : k.kc) + int64_t(k.kb + kKeys - 1 + k.d) * kD;
   uint16_t* dst = (vside ? a.halo_v : a.halo_k) +
                   ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD;
@@ -828,7 +827,7 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.fits32 = (total + 1) * workers < (int64_t(1) << 32) ? 1 : 0;
   const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
   if (a.shift) {
-    hipLaunchKernelGGL(shift_halo_kernel, dim3(ceil_div(a.workers, 16), 2), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(shift_halo_kernel, dim3(a.workers), dim3(64), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
