@@ -100,6 +100,12 @@ SMALL = [
     ("fp16", 3, 40, 8, 2, 128, 2048, [0, 700, 1999], -1, True, 0, "prefill"),
     ("bf16", 2, 33, 16, 2, 128, 2048, [1500, 0], 100, False, 0, "prefill"),
     ("bf16", 2, 7, 8, 8, 128, 1024, [1017, 300], -1, False, 0, "prefill"),
+    # more than 16 query heads per kv head: several head groups per kv head
+    # in the decode (G = 32: two groups of 16; G = 20: two groups of 10)
+    ("fp16", 3, 1, 32, 1, 128, 700, [699, 5, 300], -1, False, 0, "decode"),
+    ("bf16", 2, 1, 40, 2, 128, 520, [100, 518], -1, True, 0, "decode"),
+    ("bf16", 2, 1, 40, 2, 128, 520, [519, 519], 64, False, 0, "decode"),
+    ("fp16", 2, 9, 32, 1, 128, 300, [0, 250], -1, True, 0, "prefill"),
     # more sequences than travel in the kernel arguments: lengths read on the device
     ("bf16", 66, 3, 4, 2, 128, 64, [(7 * i) % 62 for i in range(66)], -1, True, 0, "prefill"),
     ("fp16", 66, 1, 4, 2, 128, 64, [(5 * i) % 64 for i in range(66)], -1, False, 0, "decode"),
