@@ -690,15 +690,20 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       float m[2 * kDecodeWaves], l[2 * kDecodeWaves], o[2 * kDecodeWaves];
 #pragma unroll
       for (int f = 0; f < 2 * kDecodeWaves; ++f) {
+        // loaded unconditionally (every slot lies inside the workgroup's LDS)
+        // and selected after: no branch per entry, all reads in flight at once
         const bool mine = f >= e && tb[f] == b && tu[f] == ub;
         const float* sl = reinterpret_cast<const float*>(lds + (f >> 1) * kWaveLds + (f & 1) * kSlotBytes);
-        m[f] = mine ? sl[kDecodeMaxHG * kD + h] : -INFINITY;
-        l[f] = mine ? sl[kDecodeMaxHG * kD + kDecodeMaxHG + h] : 0.f;
-        o[f] = mine ? sl[h * kD + d] : 0.f;
+        const float mv = sl[kDecodeMaxHG * kD + h];
+        const float lv = sl[kDecodeMaxHG * kD + kDecodeMaxHG + h];
+        const float ov = sl[h * kD + d];
+        m[f] = mine ? mv : -INFINITY;
+        l[f] = mine ? lv : 0.f;
+        o[f] = mine ? ov : 0.f;
       }
       float M = -INFINITY;
 #pragma unroll
-      for (int f = 0; f < 2 * kDecodeWaves; ++f) M = fmaxf(M, m[f]);
+      for (int f = 0; f < 2 * kDecodeWaves; ++f) M = __builtin_elementwise_maximum(M, m[f]);
       float L = 0.f, O = 0.f;
 #pragma unroll
       for (int f = 0; f < 2 * kDecodeWaves; ++f) {
