@@ -259,3 +259,32 @@ def test_prefill_then_decodes_match_one_shot(dt, D):
         out = dev.run("decode")
         assert_close(out_f64(out, dt)[:, 0], ref[:, n + s], dt, f"decode {s}")
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# split prefill: the workspace counters return to zero, repeated calls agree
+# --------------------------------------------------------------------------
+
+def test_split_prefill_repeated_calls_share_workspace(gpu):
+    torch = gpu
+    import grouped_query_kv_amd as gqa
+    case = gi.make_case("split-repeat", "fp16", 3, 40, 8, 2, 128, 2048, [0, 700, 1999], seed=11,
+                        rotary=True, rotary_rows=2048 + 40)
+    st, want, kc, vc, _ = O.gqa_attention(case, "prefill")
+    assert st == O.OK
+    dev = DevCase(case)
+    n = gqa.gqa_workspace_bytes(3, 40, 8, 2, 128, 2048, gqa.GQA_FP16)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    outs = []
+    for i in range(3):
+        say(f"[gpu] split prefill, call {i} on one workspace of {n} bytes")
+        outs.append(out_f64(dev.run("prefill", workspace=ws), case.dtype))
+        torch.cuda.synchronize()
+        # the per-row-block split counters sit at the end of the workspace
+        assert int(ws[-256:].count_nonzero()) == 0, "split counters not back to zero"
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "k_cache")
+    assert_bits_equal(gv, vc, "v_cache")
+    for o in outs:
+        assert_close(o, want, case.dtype, "split prefill")
+        assert np.array_equal(o, outs[0]), "the merge order depends on arrival"
