@@ -47,11 +47,11 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "adbc056a5dfe72c3514c02ff1176820930be48382309fcbb5c4b5f035619dac2",
+                "54b02924ca1b01c9bd0eded68248a412fae317c817a3568a7b2b676c880486af",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
                 "d027341bb70095180b1770782f0b845e62eb2f2be5daa28a5e726f7d822827ff"},
-    "fetch_kib": 74158.08, "write_kib": 1050.28,
-    "fetch_scale": 524288.0 / 262157.11, "write_scale": 1.0,
+    "fetch_kib": 74189.48, "write_kib": 1050.28,
+    "fetch_scale": 524288.0 / 262156.81, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
@@ -284,7 +284,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="c2,c3,c4,c5", help="workloads to run (c2 is the headline)")
+    ap.add_argument("--only", default="decode,prefill,continuation,window",
+                    help="workloads to run, comma-separated; the split-KV decode (the headline) "
+                         "always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (the reference "
@@ -311,73 +313,76 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     which = set(args.only.split(","))
+    unknown = which - {"decode", "prefill", "continuation", "window"}
+    if unknown:
+        sys.exit(f"--only: unknown workloads {sorted(unknown)}")
     result = {}
 
     # --- headline: fp16 split-KV decode -------------------------------------
-    c2 = gi.config(2)
-    log(f"[bench] C2 decode sets: building (lens={c2.seqlens_k.tolist()})")
-    sets = make_sets(c2, torch, 2)
-    log(f"[bench] C2 decode: {len(sets)} input sets, timing {args.steps} steps")
+    dec = gi.workload("split-kv-decode-fp16")
+    log(f"[bench] split-KV decode sets: building (lens={dec.seqlens_k.tolist()})")
+    sets = make_sets(dec, torch, gi.WORKLOAD_SEEDS[dec.name])
+    log(f"[bench] split-KV decode: {len(sets)} input sets, timing {args.steps} steps")
     wall, dev, per = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
-    c2_bytes = decode_bytes(c2, [int(x) for x in c2.seqlens_k])
-    st2 = stats(dev, per)
-    achieved = c2_bytes / (st2["mean_ms"] * 1e-3) / 1e9
-    value = c2_bytes / (wall * 1e-3) / 1e9
+    dec_bytes = decode_bytes(dec, [int(x) for x in dec.seqlens_k])
+    st_dec = stats(dev, per)
+    achieved = dec_bytes / (st_dec["mean_ms"] * 1e-3) / 1e9
+    value = dec_bytes / (wall * 1e-3) / 1e9
     del sets
     torch.cuda.empty_cache()
 
     extra = {}
-    if "c3" in which:
-        c3 = gi.config(3)
-        log("[bench] C3 prefill sets: building")
-        sets = make_sets(c3, torch, 3)
+    if "prefill" in which:
+        pre = gi.workload("causal-prefill-bf16")
+        log("[bench] causal prefill sets: building")
+        sets = make_sets(pre, torch, gi.WORKLOAD_SEEDS[pre.name])
         steps = max(5, args.steps // 2)
-        log(f"[bench] C3 prefill: {len(sets)} input sets, timing {steps} steps")
-        w3, dev3, per3 = time_calls(torch, sets, prefill_call(gqa), steps, max(2, args.warmup // 2))
-        fl = prefill_flops(c3)
-        s3 = stats(dev3, per3)
-        tf = fl / (s3["mean_ms"] * 1e-3) / 1e12
-        extra["prefill_c3"] = {"workload": "bf16 causal prefill B=4 H=32 Hkv=8 D=128 S=2048 rotary",
-                               "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
-                               "ms_per_call_wall": w3, "flops": fl, **s3}
+        log(f"[bench] causal prefill: {len(sets)} input sets, timing {steps} steps")
+        w, d, p_ = time_calls(torch, sets, prefill_call(gqa), steps, max(2, args.warmup // 2))
+        fl = prefill_flops(pre)
+        st = stats(d, p_)
+        tf = fl / (st["mean_ms"] * 1e-3) / 1e12
+        extra["causal_prefill"] = {"workload": "bf16 causal prefill B=4 H=32 Hkv=8 D=128 S=2048 rotary",
+                                   "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
+                                   "ms_per_call_wall": w, "flops": fl, **st}
         del sets
         torch.cuda.empty_cache()
-    if "c4" in which:
-        c4 = gi.config(4)
-        log("[bench] C4 continuation sets: building")
-        sets = make_sets(c4, torch, 4)
-        log(f"[bench] C4 continuation: {len(sets)} input sets")
-        w4, dev4, per4 = time_calls(torch, sets, prefill_call(gqa), args.steps, args.warmup)
-        fl = prefill_flops(c4)
-        s4 = stats(dev4, per4)
-        tf = fl / (s4["mean_ms"] * 1e-3) / 1e12
-        extra["continuation_c4"] = {"workload": "fp16 ragged continuation B=8 H=28 Hkv=4 D=128 S=128",
-                                    "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
-                                    "ms_per_call_wall": w4, "flops": fl,
-                                    "lens": c4.seqlens_k.tolist(), **s4}
+    if "continuation" in which:
+        cont = gi.workload("ragged-continuation-fp16")
+        log("[bench] ragged continuation sets: building")
+        sets = make_sets(cont, torch, gi.WORKLOAD_SEEDS[cont.name])
+        log(f"[bench] ragged continuation: {len(sets)} input sets")
+        w, d, p_ = time_calls(torch, sets, prefill_call(gqa), args.steps, args.warmup)
+        fl = prefill_flops(cont)
+        st = stats(d, p_)
+        tf = fl / (st["mean_ms"] * 1e-3) / 1e12
+        extra["ragged_continuation"] = {"workload": "fp16 ragged continuation B=8 H=28 Hkv=4 D=128 S=128",
+                                        "tflops": tf, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS,
+                                        "ms_per_call_wall": w, "flops": fl,
+                                        "lens": cont.seqlens_k.tolist(), **st}
         del sets
         torch.cuda.empty_cache()
-    if "c5" in which:
-        c5 = gi.config(5)
-        log("[bench] C5 window decode sets: building")
-        sets = make_sets(c5, torch, 5)
-        log(f"[bench] C5 window decode: {len(sets)} input sets")
-        w5, dev5, per5 = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
-        s5 = stats(dev5, per5)
-        att = decode_bytes(c5, [4095] * 8, window=4096)
+    if "window" in which:
+        win = gi.workload("window-decode-bf16")
+        log("[bench] window decode sets: building")
+        sets = make_sets(win, torch, gi.WORKLOAD_SEEDS[win.name])
+        log(f"[bench] window decode: {len(sets)} input sets")
+        w, d, p_ = time_calls(torch, sets, decode_call(gqa), args.steps, args.warmup)
+        st = stats(d, p_)
+        att = decode_bytes(win, [4095] * 8, window=4096)
         shift = 8 * 8 * 4095 * 128 * 2 * 2 * 2      # read + write of every kept row, K and V
-        extra["window_decode_c5"] = {
+        extra["window_decode"] = {
             "workload": "bf16 sliding-window decode B=8 H=32 Hkv=8 D=128 M=W=4096, full cache",
-            "step_gbs_vs_fused_minimum": (att + shift // 2) / (s5["mean_ms"] * 1e-3) / 1e9,
+            "step_gbs_vs_fused_minimum": (att + shift // 2) / (st["mean_ms"] * 1e-3) / 1e9,
             "step_bytes_unfused": att + shift, "attention_bytes": att,
-            "ms_per_call_wall": w5, **s5}
+            "ms_per_call_wall": w, **st}
         del sets
         torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
-        cpu = cpu_baseline(c2)
+        cpu = cpu_baseline(dec)
 
     line = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -386,11 +391,11 @@ def main():
         "config": {"workload": "fp16 decode, B=16 H=32 Hkv=8 D=128 M=4096, past lengths U{512..4095} "
                                "(seed 2), 1 new token per sequence",
                    "global_batch": 16, "seq_len": 4096, "parallelism": "none (1 GPU)",
-                   "seqlens_k": c2.seqlens_k.tolist()},
+                   "seqlens_k": dec.seqlens_k.tolist()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(),
                      "kernel": "decode call (all launches of gqa_attention_decode)",
-                     "bytes_per_call": c2_bytes, **st2},
+                     "bytes_per_call": dec_bytes, **st_dec},
         "cpu_baseline": cpu,
         **extra,
     }

@@ -8,14 +8,16 @@ Everything is returned as raw bit patterns in numpy arrays (uint32 for fp32,
 uint16 for fp16 and bf16) so that cache contents, including NaN poison with a
 payload, survive round trips bit for bit.
 
-Workloads follow the five shapes of the hot path:
-  C1  fp32 prefill-then-decode example (prompt 32, head size 8, buffer 64);
-      the prefill/decode GEMM shapes come from the worked example of the
-      rocMLIR "KV Cache" discussion.
-  C2  fp16 decode, B=16, H=32, Hkv=8, D=128, M=4096, past lengths U{512..4095}.
-  C3  bf16 causal prefill, B=4, H=32, Hkv=8, D=128, S=2048, rotary theta=1e4.
-  C4  fp16 ragged continuation, B=8, H=28, Hkv=4, D=128, S=128, past U{0..3072}.
-  C5  bf16 sliding-window decode, B=8, H=32, Hkv=8, D=128, M=W=4096, full cache.
+Workloads (by name; the seed of each is fixed):
+  worked-example            fp32 prefill-then-decode example (prompt 32, head
+                            size 8, buffer 64); the prefill/decode GEMM shapes
+                            come from the worked example of the rocMLIR
+                            "KV Cache" discussion.
+  split-kv-decode-fp16      B=16, H=32, Hkv=8, D=128, M=4096, past lengths
+                            U{512..4095}.
+  causal-prefill-bf16       B=4, H=32, Hkv=8, D=128, S=2048, rotary theta=1e4.
+  ragged-continuation-fp16  B=8, H=28, Hkv=4, D=128, S=128, past U{0..3072}.
+  window-decode-bf16        B=8, H=32, Hkv=8, D=128, M=W=4096, full cache.
 """
 from __future__ import annotations
 
@@ -134,36 +136,45 @@ def _uniform_int(rng, lo, hi, n):
     return rng.integers(lo, hi + 1, size=n).astype(np.int32)
 
 
-def config(idx: int, step: int = 1, seed: Optional[int] = None) -> Case:
-    """The five workloads. seed defaults to the config index.
+WORKLOAD_SEEDS = {
+    "worked-example": 1,
+    "split-kv-decode-fp16": 2,
+    "causal-prefill-bf16": 3,
+    "ragged-continuation-fp16": 4,
+    "window-decode-bf16": 5,
+}
 
-    C1 has two steps: step 1 is the 32-token prefill from an empty cache and
-    step 2 the one-token decode at past length 32 (use `c1_decode_after`
-    to chain step 2 onto the cache a real step 1 produced)."""
-    seed = idx if seed is None else seed
+
+def workload(name: str, step: int = 1, seed: Optional[int] = None) -> Case:
+    """One of the named workloads; seed defaults to the workload's own.
+
+    The worked example has two steps: step 1 is the 32-token prefill from an
+    empty cache and step 2 the one-token decode at past length 32 (to chain
+    step 2 onto the cache a real step 1 produced, replace its caches)."""
+    if name not in WORKLOAD_SEEDS:
+        raise ValueError(f"unknown workload {name!r}; known: {sorted(WORKLOAD_SEEDS)}")
+    seed = WORKLOAD_SEEDS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
-    if idx == 1:
+    if name == "worked-example":
         if step == 1:
-            return make_case("C1-prefill", "fp32", 1, 32, 4, 2, 8, 64, [0], seed,
+            return make_case("worked-example-prefill", "fp32", 1, 32, 4, 2, 8, 64, [0], seed,
                              scale=1.0 / math.sqrt(8.0), rng=rng)
-        return make_case("C1-decode", "fp32", 1, 1, 4, 2, 8, 64, [32], seed,
+        return make_case("worked-example-decode", "fp32", 1, 1, 4, 2, 8, 64, [32], seed,
                          scale=1.0 / math.sqrt(8.0), rng=rng)
-    if idx == 2:
+    if name == "split-kv-decode-fp16":
         lens = _uniform_int(rng, 512, 4095, 16)
-        return make_case("C2-decode", "fp16", 16, 1, 32, 8, 128, 4096, lens, seed, rng=rng)
-    if idx == 3:
+        return make_case(name, "fp16", 16, 1, 32, 8, 128, 4096, lens, seed, rng=rng)
+    if name == "causal-prefill-bf16":
         lens = np.zeros(4, np.int32)
-        return make_case("C3-prefill", "bf16", 4, 2048, 32, 8, 128, 4096, lens, seed,
+        return make_case(name, "bf16", 4, 2048, 32, 8, 128, 4096, lens, seed,
                          rotary=True, theta=10000.0, rotary_rows=4096, rng=rng)
-    if idx == 4:
+    if name == "ragged-continuation-fp16":
         lens = _uniform_int(rng, 0, 3072, 8)
-        return make_case("C4-continuation", "fp16", 8, 128, 28, 4, 128, 4096, lens, seed, rng=rng)
-    if idx == 5:
-        totals = _uniform_int(rng, 4096, 16384, 8)
-        lens = np.full(8, 4096, np.int32)
-        return make_case("C5-window-decode", "bf16", 8, 1, 32, 8, 128, 4096, lens, seed,
-                         window=4096, rng=rng, extra={"total_lengths": totals})
-    raise ValueError(idx)
+        return make_case(name, "fp16", 8, 128, 28, 4, 128, 4096, lens, seed, rng=rng)
+    totals = _uniform_int(rng, 4096, 16384, 8)
+    lens = np.full(8, 4096, np.int32)
+    return make_case(name, "bf16", 8, 1, 32, 8, 128, 4096, lens, seed,
+                     window=4096, rng=rng, extra={"total_lengths": totals})
 
 
 def next_decode_tokens(case: Case, rng) -> Case:

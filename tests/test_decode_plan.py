@@ -161,7 +161,7 @@ def test_plan_fixed(case):
 
 def test_plan_decode_workload():
     import gqa_inputs as gi
-    c = gi.config(2)
+    c = gi.workload("split-kv-decode-fp16")
     run_plan(plan_launch([int(x) for x in c.seqlens_k], 16, 32, 8, 4096, -1))
 
 

@@ -52,13 +52,13 @@ def check_full(case, entry="prefill", what=""):
 
 
 # --------------------------------------------------------------------------
-# C1: the worked example (prefill 32, then decode to 33)
+# the worked example (prefill 32, then decode to 33)
 # --------------------------------------------------------------------------
 
-def test_c1_prefill_then_decode():
-    c1 = gi.config(1, step=1)
-    dev, kc, vc, lens, _ = check_full(c1, "prefill", "C1 step 1")
-    c2 = gi.config(1, step=2)
+def test_worked_example_prefill_then_decode():
+    c1 = gi.workload("worked-example", step=1)
+    dev, kc, vc, lens, _ = check_full(c1, "prefill", "worked example step 1")
+    c2 = gi.workload("worked-example", step=2)
     c2.k_cache, c2.v_cache = kc, vc                 # continue from step 1's cache
     st, want, kc2, vc2, _ = O.gqa_attention(c2, "decode")
     d2 = DevCase(c2)
@@ -67,9 +67,9 @@ def test_c1_prefill_then_decode():
     out = d2.run("decode")
     assert dev.k_cache.data_ptr() == ptr
     gk, gv = d2.caches()
-    assert_bits_equal(gk, kc2, "C1 step 2 k_cache")
-    assert_bits_equal(gv, vc2, "C1 step 2 v_cache")
-    assert_close(out_f64(out, "fp32"), want, "fp32", "C1 step 2")
+    assert_bits_equal(gk, kc2, "worked example step 2 k_cache")
+    assert_bits_equal(gv, vc2, "worked example step 2 v_cache")
+    assert_close(out_f64(out, "fp32"), want, "fp32", "worked example step 2")
 
 
 # --------------------------------------------------------------------------
@@ -167,25 +167,25 @@ def test_evict_window_half(dt, D, M, lens, incoming):
 # the five workloads at full size
 # --------------------------------------------------------------------------
 
-def test_c2_decode_full():
-    check_full(gi.config(2), "decode", "C2")
+def test_split_kv_decode_full_size():
+    check_full(gi.workload("split-kv-decode-fp16"), "decode", "split-KV decode")
 
 
-def test_c5_window_decode_rolling_steps():
+def test_window_decode_rolling_steps():
     import grouped_query_kv_amd as gqa
-    case = gi.config(5)
+    case = gi.workload("window-decode-bf16")
     rng = np.random.default_rng(55)
     dev = DevCase(case)
     ptr = dev.k_cache.data_ptr()
     for step in range(4):
-        say(f"[gpu] C5 rolling step {step}")
+        say(f"[gpu] window decode rolling step {step}")
         st, want, kc, vc, lens = O.gqa_attention(case, "decode")
         assert st == O.OK and lens.tolist() == [4096] * 8
         out = dev.run("decode")
         gk, gv = dev.caches()
-        assert_bits_equal(gk, kc, f"C5 step {step} k_cache")
-        assert_bits_equal(gv, vc, f"C5 step {step} v_cache")
-        assert_close(out_f64(out, "bf16"), want, "bf16", f"C5 step {step}")
+        assert_bits_equal(gk, kc, f"window decode step {step} k_cache")
+        assert_bits_equal(gv, vc, f"window decode step {step} v_cache")
+        assert_close(out_f64(out, "bf16"), want, "bf16", f"window decode step {step}")
         assert dev.k_cache.data_ptr() == ptr
         nxt = gi.next_decode_tokens(case, rng)
         nxt.k_cache, nxt.v_cache = kc, vc
@@ -201,34 +201,34 @@ def test_c5_window_decode_rolling_steps():
     assert e.value.status == gqa.GQA_ERR_NO_ROOM
 
 
-def test_c3_prefill_full_sampled():
-    case = gi.config(3)
+def test_causal_prefill_full_size_sampled():
+    case = gi.workload("causal-prefill-bf16")
     rows = {0: [0, 1, 2, 63, 64, 127, 128, 1000, 2047], 1: [5, 511, 512, 2046],
             2: [0, 2047], 3: [1023, 1024, 1025]}
-    say("[gpu] C3 prefill (sampled rows vs oracle, full caches)")
+    say("[gpu] causal prefill (sampled rows vs oracle, full caches)")
     want, kc, vc = oracle_sampled(case, rows)
     dev = DevCase(case)
     out = dev.run("prefill")
     gk, gv = dev.caches()
-    assert_bits_equal(gk, kc, "C3 k_cache")
-    assert_bits_equal(gv, vc, "C3 v_cache")
+    assert_bits_equal(gk, kc, "causal prefill k_cache")
+    assert_bits_equal(gv, vc, "causal prefill v_cache")
     got = out_f64(out, "bf16")
-    worst = max(assert_close(got[b, r], want[b], "bf16", f"C3 b={b}") for b, r in rows.items())
+    worst = max(assert_close(got[b, r], want[b], "bf16", f"causal prefill b={b}") for b, r in rows.items())
     say(f"[gpu]   max abs error {worst:.3e}")
 
 
-def test_c4_continuation_full_sampled():
-    case = gi.config(4)
+def test_ragged_continuation_full_size_sampled():
+    case = gi.workload("ragged-continuation-fp16")
     rows = {b: [0, 1, 63, 64, 126, 127] for b in range(case.batch)}
-    say(f"[gpu] C4 continuation lens={case.seqlens_k.tolist()}")
+    say(f"[gpu] ragged continuation lens={case.seqlens_k.tolist()}")
     want, kc, vc = oracle_sampled(case, rows)
     dev = DevCase(case)
     out = dev.run("prefill")
     gk, gv = dev.caches()
-    assert_bits_equal(gk, kc, "C4 k_cache")
-    assert_bits_equal(gv, vc, "C4 v_cache")
+    assert_bits_equal(gk, kc, "ragged continuation k_cache")
+    assert_bits_equal(gv, vc, "ragged continuation v_cache")
     got = out_f64(out, "fp16")
-    worst = max(assert_close(got[b, r], want[b], "fp16", f"C4 b={b}") for b, r in rows.items())
+    worst = max(assert_close(got[b, r], want[b], "fp16", f"ragged continuation b={b}") for b, r in rows.items())
     say(f"[gpu]   max abs error {worst:.3e}")
 
 

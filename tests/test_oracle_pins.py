@@ -61,8 +61,8 @@ def test_brute_force_matches_oracle(kw):
 
 
 @pytest.mark.parametrize("step", [1, 2])
-def test_brute_force_matches_oracle_on_c1(step):
-    case = gi.config(1, step=step)
+def test_brute_force_matches_oracle_on_worked_example(step):
+    case = gi.workload("worked-example", step=step)
     st, out, kc, vc, _ = O.gqa_attention(case)
     assert st == O.OK
     bout, bkc, bvc = brute.brute_attention(case)
