@@ -203,10 +203,10 @@ WorkspaceLayout workspace_layout(const gqa_shape& s) {
   // prefill split partials: [row blocks, splits] slots (only when splitting)
   int64_t pf_items = 0, pf_partial = 0;
   if (D == 128 && s.dtype != GQA_FP32 && s.new_tokens > 0) {
-    const int ns = prefill_split_count(B, s.new_tokens, G, Hkv, M);
-    if (ns > 1) {
+    if (prefill_may_split(B, s.new_tokens, G, Hkv, M)) {
       pf_items = ((s.new_tokens * G + kPrefillWgRows - 1) / kPrefillWgRows) * B * Hkv;
-      pf_partial = pf_items * ns * int64_t(kPrefillSlotFloats) * 4;
+      // the plan may give one row block up to kPrefillMaxSplits ranges
+      pf_partial = pf_items * kPrefillMaxSplits * int64_t(kPrefillSlotFloats) * 4;
     }
   }
   l.scratch = l.counters_bytes;

@@ -47,26 +47,25 @@ struct WorkspaceLayout {
 };
 
 // Prefill: 256 query rows per workgroup. When a call has too few row blocks
-// to fill the chip, each row block's key tiles are cut into `splits` ranges
-// taken by separate workgroups, merged by the last one to finish. A split
-// partial holds, for each of the 512 lanes, its 64 unnormalised output
-// values, the row's exponent base and the row's weight sum (fp32).
+// to fill the chip, each row block's key tiles are cut into up to
+// kPrefillMaxSplits ranges taken by separate workgroups and merged by the
+// last one to finish; the host sizes the ranges to the lengths (the plan in
+// the launch). A range's partial holds, for each of the 512 lanes, its 64
+// unnormalised output values, the row's exponent base and its weight sum
+// (fp32).
 constexpr int kPrefillWgRows = 256;
 constexpr int kPrefillTargetWorkgroups = 256;   // one per CU
-constexpr int kPrefillMaxSplits = 4;
+constexpr int kPrefillMaxSplits = 4;            // slots per row block in the workspace
+constexpr int kPrefillPlanMax = 512;            // workgroups a split plan can list
 constexpr size_t kPrefillSlotFloats = 512 * 64 + 2 * 512;
 
-// A function of the shape only (the workspace is sized from it): split when
-// the row blocks fill less than three quarters of the chip and the buffer
-// holds at least 8 tiles of 64 keys per split.
-inline int prefill_split_count(int64_t B, int64_t S, int64_t G, int64_t Hkv, int64_t M) {
+// A function of the shape only (the workspace is sized from it): whether the
+// row blocks may be split, i.e. they fill less than three quarters of the
+// chip and the buffer holds at least 8 tiles of 64 keys per extra range.
+inline bool prefill_may_split(int64_t B, int64_t S, int64_t G, int64_t Hkv, int64_t M) {
   const int64_t items = ((S * G + kPrefillWgRows - 1) / kPrefillWgRows) * B * Hkv;
-  if (items <= 0 || 4 * items >= 3 * kPrefillTargetWorkgroups) return 1;
-  int64_t ns = (kPrefillTargetWorkgroups + items - 1) / items;
-  ns = ns < kPrefillMaxSplits ? ns : kPrefillMaxSplits;
-  const int64_t by_len = ((M + 63) / 64) / 8;
-  ns = ns < by_len ? ns : by_len;
-  return ns < 1 ? 1 : int(ns);
+  if (items <= 0 || 4 * items >= 3 * kPrefillTargetWorkgroups) return false;
+  return ((M + 63) / 64) / 8 >= 2;
 }
 
 // Decode: fast split-KV kernel limits.

@@ -23,6 +23,10 @@
 // not fully visible to all of the wave's rows. K/V rows past the valid length
 // are never read from memory (the tile loads return zeros there), so P and V
 // entries of masked keys are exact zeros.
+#include <algorithm>
+#include <atomic>
+#include <vector>
+
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
@@ -71,6 +75,9 @@ template <> struct Mma32<BF16> {
 constexpr int kD = 128;
 constexpr int kPrefillArgBatch = 64;          // batches whose lengths travel in the arguments
 constexpr int kBK = 64;                       // keys per tile
+#ifndef GQA_PREFILL_PLAN_PCT
+#define GQA_PREFILL_PLAN_PCT 100              // split plan: workgroups per 100 CUs
+#endif
 #ifndef GQA_PREFILL_READ_AHEAD
 #define GQA_PREFILL_READ_AHEAD 8              // LDS operand reads issued ahead of their product
 #endif
@@ -98,9 +105,10 @@ struct PrefillArgs {
   float scale_log2;   // |scale| * log2(e)
   uint32_t q_sign;    // 0x80008000 when the scale is negative: Q is negated (exact)
   int n_items0;       // n_rb * B * Hkv row blocks
-  int splits;         // key ranges per row block (1: no split)
-  float* partials;    // splits > 1: [row block][split] slots of kPrefillSlotFloats
-  int* counters;      // splits > 1: per row block, finished splits (kept zero)
+  float* partials;    // splitting: [row block][kPrefillMaxSplits] slots of kPrefillSlotFloats
+  int* counters;      // splitting: per row block, finished ranges (kept zero)
+  int plan_n;         // > 0: workgroup w takes plan[w] = row block | range << 16 | ranges << 24
+  uint32_t plan[kPrefillPlanMax];
   int hl_ok;          // past lengths below are valid (B <= kPrefillArgBatch)
   int hl[kPrefillArgBatch];   // past lengths from the host (the same values as lens)
 };
@@ -427,10 +435,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
 #endif
   const int col = lane & 31, c = lane >> 5;     // S^T column (= the lane's row), k half
   const int units = a.B * a.Hkv;
-  // workgroup -> (split, row block): all first splits, longest row blocks
-  // first, then all second splits, ...
-  const int split = int(blockIdx.x) / a.n_items0;
-  const int item = int(blockIdx.x) % a.n_items0;
+  // workgroup -> (row block, key range, ranges of that row block): from the
+  // host's plan (sized to the lengths) when splitting, else one row block
+  // each, longest first
+  int item = int(blockIdx.x), split = 0, nsplit = 1;
+  if (a.plan_n > 0) {
+    const uint32_t e = a.plan[blockIdx.x];
+    item = int(e & 0xFFFFu);
+    split = int((e >> 16) & 0xFFu);
+    nsplit = int(e >> 24);
+  }
   const int bg = item % units;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.G, S = a.S;
@@ -472,8 +486,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int w_full_hi = L + w_ilo;                          // keys <= this: no causal cut
   // this split's share of the row block's tiles (all of them without a split)
   const int rb_t0 = wg_kstart / kBK, rb_t1 = (wg_kend + kBK - 1) / kBK;
-  const int t_begin = __builtin_amdgcn_readfirstlane(rb_t0 + (rb_t1 - rb_t0) * split / a.splits);
-  const int t_end = __builtin_amdgcn_readfirstlane(rb_t0 + (rb_t1 - rb_t0) * (split + 1) / a.splits);
+  const int t_begin = __builtin_amdgcn_readfirstlane(rb_t0 + (rb_t1 - rb_t0) * split / nsplit);
+  const int t_end = __builtin_amdgcn_readfirstlane(rb_t0 + (rb_t1 - rb_t0) * (split + 1) / nsplit);
   const int wt0 = wave_has_rows ? max(w_kstart / kBK, t_begin) : t_end;
   const int wt1 = wave_has_rows ? min((w_kend + kBK - 1) / kBK, t_end) : t_end;
 
@@ -571,10 +585,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs.l), __float_as_uint(rs.l),
                                                     false, false);
   float l_row = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // the row's weight sum
-  if (a.splits > 1) {
+  if (nsplit > 1) {
     // publish this split's partial, count it in; the last split to finish
     // merges all of them in split order (the same sum whoever is last)
-    float* slots = a.partials + int64_t(item) * a.splits * int64_t(kPrefillSlotFloats);
+    float* slots = a.partials + int64_t(item) * kPrefillMaxSplits * int64_t(kPrefillSlotFloats);
     float* mine = slots + int64_t(split) * kPrefillSlotFloats;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -589,7 +603,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     if (tid == 0) {
       const int prev = __hip_atomic_fetch_add(a.counters + item, 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
-      sh_last = prev == a.splits - 1;
+      sh_last = prev == nsplit - 1;
       if (sh_last) __hip_atomic_store(a.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -600,7 +614,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < kPrefillMaxSplits; ++j) {
       mj[j] = -INFINITY;
       lj[j] = 0.f;
-      if (j < a.splits) {
+      if (j < nsplit) {
         const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
         mj[j] = __hip_atomic_load(sj + 512 * 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lj[j] = __hip_atomic_load(sj + 512 * 65 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -614,7 +628,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
 #pragma unroll
     for (int j = 0; j < kPrefillMaxSplits; ++j) {
-      if (j >= a.splits) break;
+      if (j >= nsplit) break;
       const float wj = lj[j] > 0.f ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
       l_row = fmaf(lj[j], wj, l_row);
       const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
@@ -655,6 +669,21 @@ bool prefill_fast_supported(const Problem& p) {
          rot_aligned;
 }
 
+namespace {
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = kPrefillTargetWorkgroups;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+}  // namespace
+
 hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
                                hipStream_t st) {
   PrefillArgs a{};
@@ -674,12 +703,52 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
     for (int b = 0; b < p.B; ++b) a.hl[b] = p.lens_host[b];
   a.n_items0 = a.n_rb * p.B * p.Hkv;
   if (a.n_items0 == 0) return hipSuccess;
-  a.splits = prefill_split_count(p.B, p.S, p.G, p.Hkv, p.M);
-  if (a.splits > 1) {
+  int blocks = a.n_items0;
+  if (prefill_may_split(p.B, p.S, p.G, p.Hkv, p.M) && p.lens_host != nullptr) {
     a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.prefill_partials);
     a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + lay.prefill_counters);
+    // Key ranges sized to the lengths: the fewest ranges per row block (at
+    // most kPrefillMaxSplits) that keep every range within T tiles, for the
+    // smallest T whose total fits one workgroup per CU; longest ranges first.
+    const int budget = std::min(kPrefillPlanMax,
+                                std::max(device_cu_count() * GQA_PREFILL_PLAN_PCT / 100, a.n_items0));
+    std::vector<int> tiles(a.n_items0);
+    const int units = p.B * p.Hkv;
+    int tmax = 1;
+    for (int k = 0; k < a.n_items0; ++k) {
+      const int rb = a.n_rb - 1 - k / units, b = (k % units) / p.Hkv;
+      const int L = std::max(0, std::min(p.lens_host[b], p.M - p.S));
+      const int r0 = rb * kWgRows;
+      const int ilo = r0 / p.G, ihi = std::min(p.S - 1, (r0 + kWgRows - 1) / p.G);
+      const int kstart = p.window > 0 ? std::max(0, L + ilo - p.window + 1) : 0;
+      const int kend = L + ihi + 1;
+      tiles[k] = std::max(1, (kend + kBK - 1) / kBK - kstart / kBK);
+      tmax = std::max(tmax, tiles[k]);
+    }
+    auto ranges = [&](int k, int T) { return std::min(kPrefillMaxSplits, (tiles[k] + T - 1) / T); };
+    auto total = [&](int T) {
+      int n = 0;
+      for (int k = 0; k < a.n_items0; ++k) n += ranges(k, T);
+      return n;
+    };
+    int lo = 1, hi = tmax;                 // total(hi) == n_items0 <= budget
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (total(mid) <= budget) hi = mid; else lo = mid + 1;
+    }
+    std::vector<int> order(a.n_items0);
+    for (int k = 0; k < a.n_items0; ++k) order[k] = k;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+      return int64_t(tiles[x]) * ranges(y, lo) > int64_t(tiles[y]) * ranges(x, lo);
+    });
+    a.plan_n = 0;
+    for (int k : order) {
+      const int n = ranges(k, lo);
+      for (int j = 0; j < n; ++j)
+        a.plan[a.plan_n++] = uint32_t(k) | (uint32_t(j) << 16) | (uint32_t(n) << 24);
+    }
+    blocks = a.plan_n;
   }
-  const int blocks = a.n_items0 * a.splits;
   if (p.dtype == GQA_FP16)
     hipLaunchKernelGGL(prefill_kernel<F16>, dim3(blocks), dim3(kThreads), 0, st, a);
   else

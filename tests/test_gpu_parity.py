@@ -95,8 +95,9 @@ SMALL = [
     ("fp32", 2, 9, 4, 2, 8, 40, [0, 31], 7, False, 0, "prefill"),
     ("bf16", 2, 3, 2, 1, 256, 40, [10, 0], -1, True, 0, "prefill"),
     ("fp16", 1, 1, 1, 1, 8, 1, [0], -1, False, 0, "prefill"),               # M = 1
-    # few row blocks and a long buffer: key ranges split over 4 workgroups,
-    # including splits that see no key at all (a sequence with L = 0)
+    # few row blocks and a long buffer: key ranges sized to the lengths and
+    # split over up to 4 workgroups, including ranges in which some rows see
+    # no key (their causal limit lies before the range) and an unsplit L = 0
     ("fp16", 3, 40, 8, 2, 128, 2048, [0, 700, 1999], -1, True, 0, "prefill"),
     ("bf16", 2, 33, 16, 2, 128, 2048, [1500, 0], 100, False, 0, "prefill"),
     ("bf16", 2, 7, 8, 8, 128, 1024, [1017, 300], -1, False, 0, "prefill"),
