@@ -75,6 +75,9 @@ template <> struct Mma32<BF16> {
 constexpr int kD = 128;
 constexpr int kPrefillArgBatch = 64;          // batches whose lengths travel in the arguments
 constexpr int kBK = 64;                       // keys per tile
+#ifndef GQA_PREFILL_SETPRIO
+#define GQA_PREFILL_SETPRIO 2                 // wave priority while issuing matrix products
+#endif
 #ifndef GQA_PREFILL_PLAN_PCT
 #define GQA_PREFILL_PLAN_PCT 100              // split plan: workgroups per 100 CUs
 #endif
@@ -396,8 +399,14 @@ template <class T>
 __device__ inline void products(int t, int wt0, int wt1, const unsigned char* kt,
                                 const unsigned char* vt, const uint4 (&qv)[8], const uint4 (&pk)[4],
                                 f32x16 (&o)[4], f32x16 (&sc)[2], int col, int c, int lane) {
+#if GQA_PREFILL_SETPRIO
+  __builtin_amdgcn_s_setprio(GQA_PREFILL_SETPRIO);
+#endif
   if (t - 1 >= wt0 && t - 1 < wt1) pv_tile<T>(vt, pk, o, lane);
   if (t >= wt0 && t < wt1) scores_tile<T>(kt, qv, sc, col, c);
+#if GQA_PREFILL_SETPRIO
+  __builtin_amdgcn_s_setprio(0);
+#endif
 }
 
 template <class T>
