@@ -119,6 +119,13 @@ __global__ void __launch_bounds__(kEvictThreads) shift_kernel(EvictArgs a) {
   }
 }
 
+// A copy unit as a built-in vector (or scalar) type of the same size.
+template <class U> struct RawOf { using type = U; };
+template <> struct RawOf<uint4> {
+  typedef uint32_t type __attribute__((ext_vector_type(4)));
+};
+template <class U> using Raw = typename RawOf<U>::type;
+
 template <class U>
 __global__ void __launch_bounds__(kEvictThreads) serial_kernel(EvictArgs a) {
   const int y = blockIdx.x, b = blockIdx.y;
@@ -131,17 +138,21 @@ __global__ void __launch_bounds__(kEvictThreads) serial_kernel(EvictArgs a) {
   const int64_t total = int64_t(keep) * a.upr;
   const int64_t shift = int64_t(d) * a.upr;
   for (int64_t base = 0; base < total; base += per_block) {
-    U v[kEvictUnitsPerThread];
+    // every lane loads (past the end it rereads the last unit, which stays
+    // in bounds) so the values live in registers; only the stores are guarded
+    // (held as plain vector-of-int values: an array of the HIP vector
+    // class is kept in scratch memory)
+    Raw<U> v[kEvictUnitsPerThread];
 #pragma unroll
     for (int n = 0; n < kEvictUnitsPerThread; ++n) {
       const int64_t u = base + threadIdx.x + n * kEvictThreads;
-      if (u < total) v[n] = rowsp[u + shift];
+      v[n] = __builtin_bit_cast(Raw<U>, rowsp[(u < total ? u : total - 1) + shift]);
     }
     __syncthreads();  // this pass's sources are all read before any store
 #pragma unroll
     for (int n = 0; n < kEvictUnitsPerThread; ++n) {
       const int64_t u = base + threadIdx.x + n * kEvictThreads;
-      if (u < total) rowsp[u] = v[n];
+      if (u < total) rowsp[u] = __builtin_bit_cast(U, v[n]);
     }
   }
 }
