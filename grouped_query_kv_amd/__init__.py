@@ -53,7 +53,7 @@ class Options(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m grouped_query_kv_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py build` "
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32P, VP = ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
