@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32P, VP = ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
-    lib.gqa_workspace_bytes.argtypes = [P]
+    lib.gqa_workspace_bytes.argtypes = [P, ctypes.POINTER(Options)]
     lib.gqa_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_append_kv.argtypes = [P, ctypes.POINTER(Options), VP, VP, VP, VP, I32P, VP, VP]
     lib.gqa_append_kv.restype = ctypes.c_int
@@ -150,16 +150,19 @@ def make_options(scale=0.0, local_window_size=-1, cos_cache=None, sin_cache=None
 _workspaces = {}
 
 
-def gqa_workspace_bytes(B, S, H, Hkv, D, M, dtype: int) -> int:
-    return int(lib.gqa_workspace_bytes(ctypes.byref(make_shape(B, S, H, Hkv, D, M, dtype))))
+def gqa_workspace_bytes(B, S, H, Hkv, D, M, dtype: int, local_window_size: int = -1) -> int:
+    opts = make_options(0.0, local_window_size)
+    return int(lib.gqa_workspace_bytes(ctypes.byref(make_shape(B, S, H, Hkv, D, M, dtype)),
+                                       ctypes.byref(opts)))
 
 
-def workspace_for(shape: Shape, device):
-    """A zero-filled workspace for this shape, cached per device and size.
+def workspace_for(shape: Shape, device, opts: Optional[Options] = None):
+    """A zero-filled workspace for this shape and options, cached per device
+    and size.
 
     Calls that share a cached workspace must not overlap in time (same stream
     or synchronised streams)."""
-    n = int(lib.gqa_workspace_bytes(ctypes.byref(shape)))
+    n = int(lib.gqa_workspace_bytes(ctypes.byref(shape), ctypes.byref(opts) if opts else None))
     if n == 0:
         return None, 0
     key = (str(device), n)
@@ -218,7 +221,7 @@ def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_
     opts = make_options(scale, local_window_size, cos_cache, sin_cache, rotary_interleaved)
     hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
     if workspace is None:
-        ws, nbytes = workspace_for(shape, q.device)
+        ws, nbytes = workspace_for(shape, q.device, opts)
     else:
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     _check(fn(ctypes.byref(shape), ctypes.byref(opts), _ptr(q), _ptr(k_new), _ptr(v_new),

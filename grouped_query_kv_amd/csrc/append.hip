@@ -2,6 +2,8 @@
 // BNSH buffer at row L'_b + i. Source rows [B, S, Hkv*D] are read in their
 // own order (fully coalesced); each destination row is one contiguous run.
 // Rotary (on K only) uses the fp64 rounding rule of rotate_pair.
+#include <algorithm>
+
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
@@ -208,6 +210,30 @@ hipError_t append_rows_vec(const Problem& p, bool evicted, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+// Prefix copy between two BNSH buffers of different row counts: y = (kv head,
+// K|V), z = b; the x workgroups stride over the rows [lo_b, L_b) of that
+// (b, kv head) in `U`-sized units, one unit per thread per pass.
+template <class U>
+__global__ void __launch_bounds__(256) copy_prefix_kernel(
+    const U* __restrict__ src_k, const U* __restrict__ src_v, int src_rows, U* __restrict__ dst_k,
+    U* __restrict__ dst_v, int dst_rows, const int32_t* __restrict__ lens, int Hkv, int upr,
+    int window) {
+  const int y = blockIdx.y, b = blockIdx.z, g = y >> 1;
+  const int L = clamp_len(lens[b], 0, src_rows < dst_rows ? src_rows : dst_rows);
+  int lo = 0;
+  if (window > 0) {
+    lo = L - window + 1 > 0 ? L - window + 1 : 0;
+    lo -= lo % kStageAlignRows;
+  }
+  const U* src = ((y & 1) ? src_v : src_k) + (int64_t(b) * Hkv + g) * src_rows * int64_t(upr);
+  U* dst = ((y & 1) ? dst_v : dst_k) + (int64_t(b) * Hkv + g) * dst_rows * int64_t(upr);
+  const int64_t end = int64_t(L) * upr;
+  for (int64_t u = int64_t(lo) * upr + blockIdx.x * int64_t(blockDim.x) + threadIdx.x; u < end;
+       u += int64_t(gridDim.x) * blockDim.x)
+    dst[u] = src[u];
+}
+
 }  // namespace
 
 hipError_t launch_append(const Problem& p, bool evicted, hipStream_t st) {
@@ -229,6 +255,35 @@ hipError_t launch_append(const Problem& p, bool evicted, hipStream_t st) {
   }
   if (e != hipSuccess) return e;
   return copy_rows(p.v_new, p.v_cache, p, evicted, st);
+}
+
+hipError_t launch_copy_prefix(const void* src_k, const void* src_v, int src_rows, void* dst_k,
+                              void* dst_v, int dst_rows, const int32_t* lens_dev, int B, int Hkv,
+                              int row_bytes, int window, int max_len, hipStream_t st) {
+  if (B == 0 || max_len <= 0) return hipSuccess;
+  const int unit = row_bytes % 16 == 0 ? 16 : (row_bytes % 4 == 0 ? 4 : 2);
+  const int upr = row_bytes / unit;
+  // enough workgroups per (b, kv head, K|V) that one pass covers the longest
+  // prefix at 16 units per thread; the kernel strides over the rest
+  const int64_t units = int64_t(std::min(max_len, std::min(src_rows, dst_rows))) * upr;
+  const int gx = int(std::max<int64_t>(1, std::min<int64_t>(64, (units + 4095) / 4096)));
+  const dim3 grid(gx, Hkv * 2, B);
+  if (unit == 16)
+    hipLaunchKernelGGL(copy_prefix_kernel<uint4>, grid, dim3(256), 0, st,
+                       static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v), src_rows,
+                       static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), dst_rows, lens_dev,
+                       Hkv, upr, window);
+  else if (unit == 4)
+    hipLaunchKernelGGL(copy_prefix_kernel<uint32_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint32_t*>(src_k), static_cast<const uint32_t*>(src_v),
+                       src_rows, static_cast<uint32_t*>(dst_k), static_cast<uint32_t*>(dst_v),
+                       dst_rows, lens_dev, Hkv, upr, window);
+  else
+    hipLaunchKernelGGL(copy_prefix_kernel<uint16_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(src_k), static_cast<const uint16_t*>(src_v),
+                       src_rows, static_cast<uint16_t*>(dst_k), static_cast<uint16_t*>(dst_v),
+                       dst_rows, lens_dev, Hkv, upr, window);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

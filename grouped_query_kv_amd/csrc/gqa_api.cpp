@@ -108,9 +108,6 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
         return fail(GQA_ERR_NO_ROOM, "sequence %d: %d past + %d new > max_seq_len %d", b,
                     lens_host[b], S, M);
   }
-  if (*needs_evict && S > 1)
-    return fail(GQA_ERR_UNSUPPORTED,
-                "window eviction with more than one new token is not implemented");
   Problem& P = *p;
   P.B = B; P.S = S; P.H = s->num_heads; P.Hkv = s->kv_num_heads; P.G = P.H / P.Hkv;
   P.D = D; P.M = M; P.dtype = s->dtype; P.window = W;
@@ -122,8 +119,9 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
   return GQA_OK;
 }
 
-gqa_status check_workspace(const gqa_shape* s, void* ws, size_t bytes, WorkspaceLayout* lay) {
-  *lay = workspace_layout(*s);
+gqa_status check_workspace(const gqa_shape* s, int window, void* ws, size_t bytes,
+                           WorkspaceLayout* lay) {
+  *lay = workspace_layout(*s, window);
   if (lay->total == 0) return GQA_OK;
   if (!ws) return fail(GQA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", lay->total);
   if (bytes < lay->total)
@@ -132,6 +130,45 @@ gqa_status check_workspace(const gqa_shape* s, void* ws, size_t bytes, Workspace
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Attention over one call's rows on the buffers the Problem names (the new
+// rows already appended there).
+hipError_t attend(const Problem& P, void* ws, const WorkspaceLayout& lay, hipStream_t hs) {
+  return prefill_fast_supported(P) ? launch_prefill_fast(P, ws, lay, hs)
+                                   : launch_attention_simple(P, hs);
+}
+
+// S > 1 with a window where some sequence must evict. Queries early in the
+// chunk see keys the eviction drops, so attention runs first over each
+// sequence as it stands before the eviction (past ++ new): in staging frames
+// of M + S rows per (b, kv head) in the workspace, where buffer row = position
+// in the sequence, so rotary positions stay L_b + i. Only the past rows the
+// window can reach are copied in (from the tile holding L_b - W + 1 on). The
+// cache itself then takes the ordinary eviction and the append at the
+// compacted lengths, exactly as a one-token step does.
+gqa_status windowed_chunk(const Problem& P, int max_drop, void* ws, const WorkspaceLayout& lay,
+                          hipStream_t hs) {
+  char* base = static_cast<char*>(ws);
+  Problem F = P;
+  F.M = lay.stage_rows;
+  F.k_cache = base + lay.stage_k;
+  F.v_cache = base + lay.stage_v;
+  const int row_bytes = P.D * elem_bytes(P.dtype);
+  int max_len = 0;
+  for (int b = 0; b < P.B; ++b) max_len = std::max(max_len, P.lens_host[b]);
+  hipError_t e = launch_copy_prefix(P.k_cache, P.v_cache, P.M, F.k_cache, F.v_cache, F.M,
+                                    P.lens_dev, P.B, P.Hkv, row_bytes, P.window, max_len, hs);
+  if (e != hipSuccess) return hip_fail(e, "staging copy");
+  e = launch_append(F, false, hs);
+  if (e != hipSuccess) return hip_fail(e, "staging append");
+  e = attend(F, ws, lay, hs);
+  if (e != hipSuccess) return hip_fail(e, "attention");
+  e = launch_evict(P, P.S, max_drop, ws, lay, hs);
+  if (e != hipSuccess) return hip_fail(e, "eviction");
+  e = launch_append(P, true, hs);
+  if (e != hipSuccess) return hip_fail(e, "append");
+  return GQA_OK;
+}
 
 // The whole op for one call. S == 1 takes the split-KV decode route.
 gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options* opts,
@@ -146,11 +183,12 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
                            lens_dev, out, &P, &needs_evict, &max_drop);
   if (st != GQA_OK) return st;
   WorkspaceLayout lay;
-  st = check_workspace(shape, ws, ws_bytes, &lay);
+  st = check_workspace(shape, P.window, ws, ws_bytes, &lay);
   if (st != GQA_OK) return st;
   if (P.B == 0) return GQA_OK;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
+  if (needs_evict && P.S > 1) return windowed_chunk(P, max_drop, ws, lay, hs);
   const bool fast_decode = P.S == 1 && decode_fast_supported(P);
   const bool fuse_evict = needs_evict && fast_decode && decode_fused_evict_supported(P);
   if (needs_evict && !fuse_evict) {
@@ -165,22 +203,20 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
   }
   e = launch_append(P, evicted_lengths, hs);
   if (e != hipSuccess) return hip_fail(e, "append");
-  if (prefill_fast_supported(P)) {
-    e = launch_prefill_fast(P, ws, lay, hs);
-    if (e != hipSuccess) return hip_fail(e, "prefill");
-  } else {
-    e = launch_attention_simple(P, hs);
-    if (e != hipSuccess) return hip_fail(e, "attention");
-  }
+  e = attend(P, ws, lay, hs);
+  if (e != hipSuccess) return hip_fail(e, "attention");
   return GQA_OK;
 }
 
 }  // namespace
 
-WorkspaceLayout workspace_layout(const gqa_shape& s) {
+WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   WorkspaceLayout l{};
   const int64_t B = s.batch, H = s.num_heads, Hkv = s.kv_num_heads, D = s.head_size;
-  const int64_t M = s.max_seq_len;
+  const bool staged = window > 0 && s.new_tokens > 1;
+  // the windowed chunk path runs the attention kernels on staging frames of
+  // M + S rows, so the partials and halos below are sized for that many
+  const int64_t M = s.max_seq_len + (staged ? s.new_tokens : 0);
   if (B <= 0 || Hkv <= 0 || D <= 0 || M <= 0) return l;
   const int64_t G = H > 0 && H % Hkv == 0 ? H / Hkv : 1;
   // decode merge counters, one per (b, kv head, head group)
@@ -218,6 +254,13 @@ WorkspaceLayout workspace_layout(const gqa_shape& s) {
                                        size_t(pf_partial)}));
   l.prefill_counters = l.scratch + l.scratch_bytes;
   l.total = l.prefill_counters + align256(size_t(pf_items) * sizeof(int32_t));
+  if (staged) {
+    l.stage_rows = int(M);
+    l.stage_bytes = align256(size_t(B * Hkv * M * row_bytes));
+    l.stage_k = l.total;
+    l.stage_v = l.stage_k + l.stage_bytes;
+    l.total = l.stage_v + l.stage_bytes;
+  }
   return l;
 }
 
@@ -227,9 +270,9 @@ using namespace gqa;
 
 extern "C" {
 
-size_t gqa_workspace_bytes(const gqa_shape* shape) {
+size_t gqa_workspace_bytes(const gqa_shape* shape, const gqa_options* opts) {
   if (!shape) return 0;
-  return workspace_layout(*shape).total;
+  return workspace_layout(*shape, opts ? opts->local_window_size : -1).total;
 }
 
 gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts, const void* k_new,
@@ -284,7 +327,7 @@ gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming, void* k_ca
   for (int b = 0; b < B; ++b) max_drop = std::max(max_drop, seqlens_k_host[b] + incoming - M);
   if (max_drop > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "cache is NULL");
   WorkspaceLayout lay;
-  st = check_workspace(shape, workspace, workspace_bytes, &lay);
+  st = check_workspace(shape, -1, workspace, workspace_bytes, &lay);
   if (st != GQA_OK) return st;
   if (max_drop > 0) {
     Problem P{};

@@ -43,6 +43,11 @@ struct WorkspaceLayout {
   size_t decode_halo;     // fused-eviction halo rows, after the decode partials
   size_t prefill_counters;  // int32 [prefill row blocks] split counters (kept zero)
   size_t prefill_partials;  // split partials of the prefill kernel (in the scratch area)
+  // windowed chunk (S > 1, a window, some sequence evicting): K and V staging
+  // frames [B, Hkv, stage_rows, D], stage_rows = M + S, in which attention
+  // sees each sequence before its eviction (0 bytes when not needed)
+  size_t stage_k, stage_v, stage_bytes;
+  int stage_rows;
   size_t total;
 };
 
@@ -110,7 +115,23 @@ inline EvictGeometry evict_geometry(int row_bytes) {
   return g;
 }
 
-WorkspaceLayout workspace_layout(const gqa_shape& s);
+// `window` is the call's local_window_size (-1 when off); with a window and
+// S > 1 the layout includes the staging frames.
+WorkspaceLayout workspace_layout(const gqa_shape& s, int window);
+
+// Rows of the staging frame the windowed chunk path fills before attention:
+// key tiles of the attention kernels start at multiples of this, so every
+// row of a visited tile holds a real key.
+constexpr int kStageAlignRows = 64;
+
+// Copy rows [lo_b, min(L_b, src_rows)) of every (b, kv head) of K and V
+// from buffers of src_rows rows per head to buffers of dst_rows rows per
+// head, at the same row numbers; lo_b = 0 with window <= 0, else
+// max(0, L_b - window + 1) rounded down to kStageAlignRows. max_len is the
+// largest L_b (host copy), which sizes the grid.
+hipError_t launch_copy_prefix(const void* src_k, const void* src_v, int src_rows, void* dst_k,
+                              void* dst_v, int dst_rows, const int32_t* lens_dev, int B, int Hkv,
+                              int row_bytes, int window, int max_len, hipStream_t st);
 
 // Launchers. They assume validated arguments and return the first HIP error.
 hipError_t launch_append(const Problem& p, bool evicted_lengths, hipStream_t st);

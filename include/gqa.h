@@ -108,11 +108,15 @@ typedef struct gqa_options {
 
 /*
  * Bytes of workspace the attention and eviction entry points need for this
- * shape, for any seqlens_k (an upper bound over all lengths 0..M). The
- * workspace must be zero-filled before its first use; each successful call
- * leaves it reusable (its counters return to zero). 0 means none is needed.
+ * shape and options (opts may be NULL: no window), for any seqlens_k (an
+ * upper bound over all lengths 0..M). With a window and S > 1 it includes
+ * two staging frames of B * Hkv * (M + S) rows (see gqa_attention_prefill).
+ * The workspace must be zero-filled before its first use; each successful
+ * call leaves it reusable (its counters return to zero). 0 means none is
+ * needed. A call whose local_window_size is -1 may use a workspace sized
+ * with any window.
  */
-size_t gqa_workspace_bytes(const gqa_shape* shape);
+size_t gqa_workspace_bytes(const gqa_shape* shape, const gqa_options* opts);
 
 /*
  * Append half (steps 1 and 3 for K/V only): rotary on k_new when tables are
@@ -132,11 +136,17 @@ gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts,
  * flash-style attention on MFMA for fp16/bf16 with D = 128, a plain
  * kernel otherwise. When the shape has too few 256-row blocks to fill the
  * GPU, each block's key range is split over several workgroups whose
- * partials (kept in the workspace) the last one merges by log-sum-exp. With a window, S > 1 and an eviction needed by some
- * sequence, returns GQA_ERR_UNSUPPORTED (attention would need the
- * pre-eviction keys). Source: all three pages as summarised above; the
- * key-tile loop ends at each sequence's length ("KV Cache", notes and
- * short-term plan).
+ * partials (kept in the workspace) the last one merges by log-sum-exp.
+ * With a window, S > 1 and an eviction needed by some sequence, queries
+ * early in the chunk see keys the eviction drops: attention then runs over
+ * each sequence before its eviction (past ++ new, positions L_b + i), in
+ * staging frames in the workspace that hold the past rows the window
+ * reaches and the new rows, and the cache then takes the eviction (keep the
+ * min(L_b + S, M) most recent tokens at rows 0..) and the append. Source:
+ * all three pages as summarised above; the key-tile loop ends at each
+ * sequence's length ("KV Cache", notes and short-term plan); the window
+ * keeps the most recent tokens contiguously (sliding-window follow-up of
+ * the GroupQueryAttention clarification).
  */
 gqa_status gqa_attention_prefill(const gqa_shape* shape, const gqa_options* opts,
                                  const void* q, const void* k_new, const void* v_new,

@@ -120,14 +120,25 @@ def test_invalid_arguments(g, entry, shape_kw, kw):
     assert g.lib.gqa_last_error()
 
 
-def test_window_with_multi_token_eviction_is_unsupported(g):
+def test_windowed_chunk_needs_the_staging_workspace(g):
+    # S > 1 with a window: the workspace holds two staging frames of
+    # B * Hkv * (M + S) rows, and a workspace sized without the window is
+    # rejected before any launch
+    shape = _shape(g, S=3, M=16)
     opts = g.Options(0.0, 16, None, None, 0, 0)
-    st = _call(g, "prefill", _shape(g, S=3, M=16), opts, lens=(15, 0))
-    assert st == g.GQA_ERR_UNSUPPORTED
+    plain = g.lib.gqa_workspace_bytes(ctypes.byref(shape), None)
+    staged = g.lib.gqa_workspace_bytes(ctypes.byref(shape), ctypes.byref(opts))
+    assert staged >= plain + 2 * 2 * 2 * (16 + 3) * 8 * 4
+    st = _call(g, "prefill", shape, opts, lens=(15, 0), ws_bytes=staged - 1)
+    assert st == g.GQA_ERR_WORKSPACE
+    # one token per sequence needs no staging
+    one = _shape(g, S=1, M=16)
+    assert (g.lib.gqa_workspace_bytes(ctypes.byref(one), ctypes.byref(opts))
+            == g.lib.gqa_workspace_bytes(ctypes.byref(one), None))
 
 
 def test_workspace_too_small(g):
-    need = g.lib.gqa_workspace_bytes(ctypes.byref(_shape(g, S=1, D=128, dtype=1)))
+    need = g.lib.gqa_workspace_bytes(ctypes.byref(_shape(g, S=1, D=128, dtype=1)), None)
     assert need > 0
     st = _call(g, "decode", _shape(g, S=1, D=128, dtype=1), lens=(3, 4), ws_bytes=need - 1)
     assert st == g.GQA_ERR_WORKSPACE

@@ -110,6 +110,18 @@ SMALL = [
     # more sequences than travel in the kernel arguments: lengths read on the device
     ("bf16", 66, 3, 4, 2, 128, 64, [(7 * i) % 62 for i in range(66)], -1, True, 0, "prefill"),
     ("fp16", 66, 1, 4, 2, 128, 64, [(5 * i) % 64 for i in range(66)], -1, False, 0, "decode"),
+    # windowed chunks that evict: attention over past ++ new in the staging
+    # frames, then eviction and append in the cache (some sequences evict,
+    # some not; the window below, at and above the chunk; S = M drops the
+    # whole past; the split plan on a long buffer; the generic kernel)
+    ("bf16", 2, 33, 16, 2, 128, 200, [190, 100], 200, False, 0, "prefill"),
+    ("fp16", 3, 64, 28, 4, 128, 300, [300, 280, 0], 128, True, 0, "prefill"),
+    ("bf16", 2, 130, 32, 8, 128, 512, [500, 512], 512, True, 0, "prefill"),
+    ("fp16", 1, 64, 8, 1, 128, 64, [64], 64, False, 0, "prefill"),
+    ("bf16", 2, 40, 8, 2, 128, 2048, [2040, 1000], 1024, False, 0, "prefill"),
+    ("fp16", 2, 70, 8, 2, 128, 256, [255, 256], 16, True, 1, "prefill"),
+    ("fp32", 2, 9, 4, 2, 8, 40, [35, 40], 40, False, 0, "prefill"),
+    ("bf16", 2, 5, 6, 3, 64, 48, [48, 44], 20, True, 0, "prefill"),
 ]
 
 
@@ -200,6 +212,42 @@ def test_window_decode_rolling_steps():
     with pytest.raises(gqa.GQAError) as e:
         dev.run("decode")
     assert e.value.status == gqa.GQA_ERR_NO_ROOM
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_windowed_chunks_rolling(dt):
+    """Chunks of S > 1 tokens into full W-slot caches, continued in place on
+    the GPU; each step against the oracle run on the previous oracle state."""
+    rng = np.random.default_rng(31)
+    B, H, Hkv, D, M = 4, 16, 4, 128, 1024
+    lens = [1024, 1000, 600, 1024]
+    case = gi.make_case("chunks", dt, B, 96, H, Hkv, D, M, lens, 12, window=M, rotary=True,
+                        rotary_rows=M + 4 * 128)
+    dev = DevCase(case)
+    ptr = dev.k_cache.data_ptr()
+    for step in range(3):
+        S = [96, 128, 40][step]
+        say(f"[gpu] windowed chunks {dt} step {step}: S={S} lens={case.seqlens_k.tolist()}")
+        st, want, kc, vc, after = O.gqa_attention(case, "prefill")
+        assert st == O.OK
+        out = dev.run("prefill")
+        gk, gv = dev.caches()
+        assert_bits_equal(gk, kc, f"chunk step {step} k_cache")
+        assert_bits_equal(gv, vc, f"chunk step {step} v_cache")
+        err = assert_close(out_f64(out, dt), want, dt, f"chunk step {step}")
+        say(f"[gpu]   max abs error {err:.3e}")
+        assert dev.k_cache.data_ptr() == ptr
+        # next chunk: fresh Q/K/V, the lengths the call left
+        nxt = case.copy()
+        nxt.new_tokens = [96, 128, 40, 1][step + 1]
+        nxt.q = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, H * D)), dt)
+        nxt.k_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        nxt.v_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        nxt.k_cache, nxt.v_cache, nxt.seqlens_k = kc, vc, after.astype(np.int32)
+        case = nxt
+        cache_k, cache_v = dev.k_cache, dev.v_cache
+        dev = DevCase(case)
+        dev.k_cache, dev.v_cache = cache_k, cache_v
 
 
 def test_causal_prefill_full_size_sampled():

@@ -404,6 +404,51 @@ def test_windowed_decode_equals_full_history_window_attention():
         big.k_cache, big.v_cache, big.seqlens_k = kc2, vc2, l2.astype(np.int32)
 
 
+def test_windowed_chunks_equal_full_history_window_attention():
+    """Chunks of S > 1 tokens into a full W-slot cache (attention before the
+    eviction drops the keys early queries still see) vs the same chunks into a
+    buffer long enough to keep the whole history, with the same window mask.
+    Rotary positions follow the total length on both sides."""
+    rng = np.random.default_rng(9)
+    W, T0, D = 8, 8, 4
+    small = tiny("fp32", B=2, S=1, H=4, Hkv=2, D=D, M=W, lens=(T0, 3), window=W, seed=2)
+    big = small.copy()
+    big.max_seq_len = 96
+    for name in ("k_cache", "v_cache"):
+        arr = np.zeros((2, 2, 96, D), np.uint32)
+        arr[:, :, :W] = getattr(small, name)
+        setattr(big, name, arr)
+    cos, sin = gi.rope_tables(96, D // 2)
+    for c in (small, big):
+        c.cos, c.sin = cos, sin
+    total = np.array([T0, 3])
+    for step in range(8):
+        S = int(rng.integers(2, W + 1))
+        q = gi.to_bits(rng.standard_normal((2, S, 4 * D)), "fp32")
+        k = gi.to_bits(rng.standard_normal((2, S, 2 * D)), "fp32")
+        v = gi.to_bits(rng.standard_normal((2, S, 2 * D)), "fp32")
+        for c in (small, big):
+            c.new_tokens, c.q, c.k_new, c.v_new = S, q, k, v
+        # the small cache's rows start at total - lens: rotary positions must
+        # be the history's, so only compare while nothing was dropped before
+        # this step, or without rotary
+        rot = bool((total == small.seqlens_k).all())
+        for c in (small, big):
+            c.cos, c.sin = (cos, sin) if rot else (None, None)
+        s1, o1, kc1, vc1, l1 = O.gqa_attention(small)
+        s2, o2, kc2, vc2, l2 = O.gqa_attention(big)
+        assert s1 == s2 == O.OK
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+        total = total + S
+        assert l1.tolist() == np.minimum(total, W).tolist()
+        for b in range(2):
+            n = int(l1[b])
+            assert np.array_equal(kc1[b, :, :n], kc2[b, :, int(l2[b]) - n:int(l2[b])])
+            assert np.array_equal(vc1[b, :, :n], vc2[b, :, int(l2[b]) - n:int(l2[b])])
+        small.k_cache, small.v_cache, small.seqlens_k = kc1, vc1, l1.astype(np.int32)
+        big.k_cache, big.v_cache, big.seqlens_k = kc2, vc2, l2.astype(np.int32)
+
+
 def test_prefill_then_decodes_equals_one_shot_prefill():
     n, k = 7, 4
     full = tiny("fp32", B=1, S=n + k, H=4, Hkv=2, D=8, M=16, lens=(0,), seed=12, rotary=True)
