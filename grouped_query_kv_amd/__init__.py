@@ -9,7 +9,10 @@ package raises.
 
 The functions carry the C entry points' names:
   gqa_append_kv, gqa_attention_prefill, gqa_attention_decode,
-  gqa_evict_window, gqa_workspace_bytes.
+  gqa_attention_present, gqa_evict_window, gqa_workspace_bytes.
+The attention functions also take separate present_key/present_value
+tensors (past and present in different buffers) and then call
+gqa_attention_present.
 """
 from __future__ import annotations
 
@@ -26,7 +29,7 @@ GQA_OK, GQA_ERR_NO_ROOM, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKS
 GQA_FP32, GQA_FP16, GQA_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "ok", 1: "no_room", 2: "invalid_arg", 3: "unsupported", 4: "workspace", 5: "hip"}
 EXPORTED = ("gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill", "gqa_attention_decode",
-            "gqa_evict_window", "gqa_status_string", "gqa_last_error")
+            "gqa_attention_present", "gqa_evict_window", "gqa_status_string", "gqa_last_error")
 
 
 class GQAError(RuntimeError):
@@ -66,6 +69,10 @@ def _load() -> ctypes.CDLL:
         f.argtypes = [P, ctypes.POINTER(Options), VP, VP, VP, VP, VP, I32P, VP, VP, VP,
                       ctypes.c_size_t, VP]
         f.restype = ctypes.c_int
+    lib.gqa_attention_present.argtypes = [P, ctypes.POINTER(Options), VP, VP, VP, VP, VP,
+                                          ctypes.c_int32, VP, VP, I32P, VP, VP, VP,
+                                          ctypes.c_size_t, VP]
+    lib.gqa_attention_present.restype = ctypes.c_int
     lib.gqa_evict_window.argtypes = [P, ctypes.c_int32, VP, VP, I32P, VP, I32P, VP, ctypes.c_size_t, VP]
     lib.gqa_evict_window.restype = ctypes.c_int
     lib.gqa_status_string.argtypes = [ctypes.c_int]
@@ -201,8 +208,20 @@ def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
 def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev, out,
                scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
                present_key, present_value, workspace, stream):
-    _same_buffer(k_cache, present_key, "key")
-    _same_buffer(v_cache, present_value, "value")
+    past_k = past_v = None
+    past_rows = 0
+    if (present_key is None) != (present_value is None):
+        raise GQAError(GQA_ERR_INVALID_ARG, "present_key and present_value go together")
+    if present_key is not None and (present_key.data_ptr() != k_cache.data_ptr()
+                                    or present_value.data_ptr() != v_cache.data_ptr()):
+        # separate buffers: k_cache / v_cache are the past, the call fills present
+        _contig(k_cache, v_cache)
+        Bp, Hp, past_rows, Dp = _cache_shape(k_cache, v_cache)
+        if ((Bp, Hp, Dp) != tuple(int(x) for x in present_key.shape[:2]) + (int(present_key.shape[3]),)
+                or present_key.dtype != k_cache.dtype):
+            raise GQAError(GQA_ERR_INVALID_ARG, "past and present must agree in B, Hkv, D and dtype")
+        past_k, past_v = k_cache, v_cache
+        k_cache, v_cache = present_key, present_value
     _contig(q, k_new, v_new, k_cache, v_cache, cos_cache, sin_cache)
     if q.dim() != 3 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.dim() != 3:
         raise GQAError(GQA_ERR_INVALID_ARG, "q must be [B, S, H*D], k_new/v_new [B, S, Hkv*D]")
@@ -224,6 +243,15 @@ def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_
         ws, nbytes = workspace_for(shape, q.device, opts)
     else:
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    if past_k is not None:
+        if fn is lib.gqa_attention_decode and S != 1:
+            raise GQAError(GQA_ERR_INVALID_ARG, "decode needs new_tokens == 1")
+        _check(lib.gqa_attention_present(ctypes.byref(shape), ctypes.byref(opts), _ptr(q),
+                                         _ptr(k_new), _ptr(v_new), _ptr(past_k), _ptr(past_v),
+                                         int(past_rows), _ptr(k_cache), _ptr(v_cache), hp,
+                                         _ptr(seqlens_k_dev), _ptr(out), _ptr(ws), nbytes,
+                                         _stream(stream)))
+        return out
     _check(fn(ctypes.byref(shape), ctypes.byref(opts), _ptr(q), _ptr(k_new), _ptr(v_new),
               _ptr(k_cache), _ptr(v_cache), hp, _ptr(seqlens_k_dev), _ptr(out), _ptr(ws),
               nbytes, _stream(stream)))
@@ -234,7 +262,11 @@ def gqa_attention_prefill(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seq
                           out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
                           sin_cache=None, rotary_interleaved=False, present_key=None,
                           present_value=None, workspace=None, stream=None):
-    """The whole op for S >= 1 new tokens; returns out [B, S, H*D]."""
+    """The whole op for S >= 1 new tokens; returns out [B, S, H*D].
+
+    With present_key/present_value in buffers other than k_cache/v_cache,
+    k_cache/v_cache are the past ([B, Hkv, past_rows, D], only read) and the
+    present buffers receive past ++ new (gqa_attention_present)."""
     return _attention(lib.gqa_attention_prefill, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
                       seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
                       rotary_interleaved, present_key, present_value, workspace, stream)

@@ -310,6 +310,50 @@ gqa_status gqa_attention_decode(const gqa_shape* shape, const gqa_options* opts,
                        seqlens_k_dev, out, workspace, workspace_bytes, stream);
 }
 
+gqa_status gqa_attention_present(const gqa_shape* shape, const gqa_options* opts, const void* q,
+                                 const void* k_new, const void* v_new, const void* past_key,
+                                 const void* past_value, int32_t past_rows, void* present_key,
+                                 void* present_value, const int32_t* seqlens_k_host,
+                                 const int32_t* seqlens_k_dev, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  // the whole op's own validation (shape, options, present lengths, room,
+  // workspace) comes first; nothing is launched before every check passed
+  Problem P;
+  bool needs_evict;
+  int max_drop;
+  gqa_status st = validate(kPrefill, shape, opts, q, k_new, v_new, present_key, present_value,
+                           seqlens_k_host, seqlens_k_dev, out, &P, &needs_evict, &max_drop);
+  if (st != GQA_OK) return st;
+  if (past_rows < 0) return fail(GQA_ERR_INVALID_ARG, "past_rows %d < 0", past_rows);
+  int max_len = 0;
+  for (int b = 0; b < P.B; ++b) {
+    if (seqlens_k_host[b] > past_rows)
+      return fail(GQA_ERR_INVALID_ARG, "seqlens_k[%d] = %d > past_rows %d", b, seqlens_k_host[b],
+                  past_rows);
+    max_len = std::max(max_len, seqlens_k_host[b]);
+  }
+  const bool same = past_key == present_key || past_value == present_value;
+  if (same && (past_key != present_key || past_value != present_value || past_rows != P.M))
+    return fail(GQA_ERR_INVALID_ARG,
+                "past and present share a buffer only as a whole (same K and V, same rows)");
+  if (!same && max_len > 0 && (!past_key || !past_value))
+    return fail(GQA_ERR_INVALID_ARG, "past_key or past_value is NULL");
+  WorkspaceLayout lay;
+  st = check_workspace(shape, P.window, workspace, workspace_bytes, &lay);
+  if (st != GQA_OK) return st;
+  if (P.B == 0) return GQA_OK;
+  if (!same) {
+    hipError_t e = launch_copy_prefix(past_key, past_value, past_rows, present_key, present_value,
+                                      P.M, seqlens_k_dev, P.B, P.Hkv,
+                                      P.D * elem_bytes(P.dtype), -1, max_len,
+                                      reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "past copy");
+  }
+  return run_attention(kPrefill, shape, opts, q, k_new, v_new, present_key, present_value,
+                       seqlens_k_host, seqlens_k_dev, out, workspace, workspace_bytes, stream);
+}
+
 gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming, void* k_cache,
                             void* v_cache, const int32_t* seqlens_k_host,
                             const int32_t* seqlens_k_dev, int32_t* seqlens_after_host,

@@ -171,6 +171,32 @@ gqa_status gqa_attention_decode(const gqa_shape* shape, const gqa_options* opts,
                                 void* stream);
 
 /*
+ * The whole op with separate past and present buffers: past_key/past_value
+ * [B, Hkv, past_rows, D] hold sequence b's first L_b rows (L_b <= past_rows)
+ * and are only read; present_key/present_value [B, Hkv, M, D] (M =
+ * shape->max_seq_len) receive past rows [0, L_b) at the same rows, then the
+ * call proceeds exactly as gqa_attention_prefill on the present buffers
+ * (any S >= 1; one token per sequence takes the split-KV decode). Present
+ * rows [L_b + S, M) are not written, past is never written; afterwards the
+ * present buffers can serve as a shared buffer for the next call.
+ * Passing the same K and V buffers as past and present (with past_rows = M)
+ * is the shared mode and copies nothing; any other overlap of past and
+ * present is undefined. L_b + S > M fails with GQA_ERR_NO_ROOM (window off),
+ * L_b > past_rows with GQA_ERR_INVALID_ARG, both before any launch.
+ * Workspace: gqa_workspace_bytes of the present shape. Source: question of
+ * the GroupQueryAttention clarification (past of length
+ * past_sequence_length unless it is the present tensor) and its summary
+ * (with different shapes, present is past + new in a different tensor).
+ */
+gqa_status gqa_attention_present(const gqa_shape* shape, const gqa_options* opts,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 const void* past_key, const void* past_value, int32_t past_rows,
+                                 void* present_key, void* present_value,
+                                 const int32_t* seqlens_k_host, const int32_t* seqlens_k_dev,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * Eviction half (step 2 alone): make room for `incoming` tokens
  * (0 <= incoming <= M) in every sequence by dropping its oldest
  * d_b = max(0, L_b + incoming - M) rows and shifting the rest to row 0, in

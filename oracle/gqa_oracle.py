@@ -52,6 +52,7 @@ Status strings: "ok", "no_room", "invalid_arg".
 """
 from __future__ import annotations
 
+import copy
 import math
 
 import numpy as np
@@ -296,6 +297,34 @@ def gqa_attention(case, entry: str = "prefill"):
             _attention(case, qr, keys, vals, L, out, b)
     out = out.transpose(0, 2, 1, 3).reshape(B, S, H * D)
     return OK, out, kc, vc, lens2 + S
+
+
+def gqa_attention_present(case, past_k: np.ndarray, past_v: np.ndarray):
+    """The whole op with separate past and present buffers ([P1] question:
+    past is of length past_sequence_length unless it is the present tensor;
+    the asker's summary: with different shapes, present is past + new in a
+    different tensor).
+
+    case.k_cache / case.v_cache are the present buffers [B, Hkv, M, D] as they
+    stand before the call; past_k / past_v [B, Hkv, past_rows, D] hold rows
+    [0, L_b) of each sequence. Present rows [0, L_b) take the past rows, then
+    the op runs on present exactly as in shared mode. Returns what
+    gqa_attention returns; past is never modified.
+    """
+    st = validate(case, "prefill")
+    lens = np.asarray(case.seqlens_k, dtype=np.int64)
+    past_rows = past_k.shape[2]
+    if st == OK and case.batch and int(lens.max()) > past_rows:
+        st = INVALID
+    if st != OK:
+        return st, None, case.k_cache.copy(), case.v_cache.copy(), np.array(case.seqlens_k, copy=True)
+    present = copy.copy(case)               # same inputs, own present arrays
+    present.k_cache, present.v_cache = case.k_cache.copy(), case.v_cache.copy()
+    for b in range(case.batch):
+        L = int(lens[b])
+        present.k_cache[b, :, :L] = past_k[b, :, :L]
+        present.v_cache[b, :, :L] = past_v[b, :, :L]
+    return gqa_attention(present, "prefill")
 
 
 def gqa_append_kv(case):

@@ -35,8 +35,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(g):
     names = declared_functions()
     assert set(names) == {"gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill",
-                          "gqa_attention_decode", "gqa_evict_window", "gqa_status_string",
-                          "gqa_last_error"}
+                          "gqa_attention_decode", "gqa_attention_present", "gqa_evict_window",
+                          "gqa_status_string", "gqa_last_error"}
+    assert set(names) == set(g.EXPORTED)
     lib = ctypes.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -176,6 +177,59 @@ def test_empty_batch_is_a_noop(g):
     assert _call(g, "prefill", _shape(g, B=0), lens=()) == g.GQA_OK
     assert _call(g, "append", _shape(g, B=0), lens=()) == g.GQA_OK
     assert _call(g, "append", _shape(g, S=0), lens=(1, 2)) == g.GQA_OK
+
+
+def _present(g, shape, lens, past_rows, past_k=FAKE + 0x1000, past_v=FAKE + 0x2000,
+             present_k=FAKE + 0x3000, present_v=FAKE + 0x4000):
+    # every case below must fail validation: the pointers are dummies
+    opts = g.Options(0.0, -1, None, None, 0, 0)
+    hl = np.asarray(lens, np.int32)
+    hp = hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return g.lib.gqa_attention_present(ctypes.byref(shape), ctypes.byref(opts), FAKE, FAKE, FAKE,
+                                       past_k, past_v, past_rows, present_k, present_v,
+                                       hp, FAKE, FAKE, FAKE, 1 << 30, None)
+
+
+def test_present_mode_validation(g):
+    sh = _shape(g, S=3, M=16)
+    # a length beyond the past's rows
+    assert _present(g, sh, (6, 2), 5) == g.GQA_ERR_INVALID_ARG
+    assert _present(g, sh, (3, 2), -1) == g.GQA_ERR_INVALID_ARG
+    # present too short for past + new: no room, as in shared mode
+    assert _present(g, sh, (14, 2), 20) == g.GQA_ERR_NO_ROOM
+    # the same buffers with another row count
+    assert _present(g, sh, (3, 2), 8, past_k=FAKE, past_v=FAKE + 8, present_k=FAKE,
+                    present_v=FAKE + 8) == g.GQA_ERR_INVALID_ARG
+    # only K shared, or only V
+    assert _present(g, sh, (3, 2), 16, past_k=FAKE, present_k=FAKE) == g.GQA_ERR_INVALID_ARG
+    assert _present(g, sh, (3, 2), 16, past_v=FAKE, present_v=FAKE) == g.GQA_ERR_INVALID_ARG
+    # a missing past
+    assert _present(g, sh, (3, 2), 8, past_k=0) == g.GQA_ERR_INVALID_ARG
+    # workspace checked before any launch
+    opts = g.Options(0.0, 16, None, None, 0, 0)
+    hl = np.asarray((3, 2), np.int32)
+    st = g.lib.gqa_attention_present(ctypes.byref(sh), ctypes.byref(opts), FAKE, FAKE, FAKE, FAKE,
+                                     FAKE + 64, 8, FAKE + 128, FAKE + 192,
+                                     hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), FAKE, FAKE,
+                                     None, 0, None)
+    assert st == g.GQA_ERR_WORKSPACE
+
+
+def test_binding_routes_separate_present_to_present_mode(g):
+    torch = pytest.importorskip("torch")
+    past_k, past_v = torch.zeros(1, 1, 4, 8), torch.zeros(1, 1, 4, 8)
+    pres_k, pres_v = torch.zeros(1, 1, 16, 8), torch.zeros(1, 1, 16, 8)
+    q, kn = torch.zeros(1, 2, 16), torch.zeros(1, 2, 8)
+    # length 5 exceeds the 4 past rows: only the present entry point checks
+    # that (validation, before any launch)
+    lens_dev = torch.zeros(1, dtype=torch.int32)   # never read: validation fails first
+    with pytest.raises(g.GQAError) as e:
+        g.gqa_attention_prefill(q, kn, kn, past_k, past_v, np.array([5], np.int32), lens_dev,
+                                present_key=pres_k, present_value=pres_v, stream=0)
+    assert e.value.status == g.GQA_ERR_INVALID_ARG and "past_rows" in str(e.value)
+    with pytest.raises(g.GQAError):
+        g.gqa_attention_prefill(q, kn, kn, past_k, past_v, np.array([1], np.int32), None,
+                                present_key=pres_k, stream=0)
 
 
 def test_binding_rejects_separate_past_and_present(g):

@@ -31,7 +31,7 @@ def gpu():
 
 
 from gpu_helpers import (DevCase, assert_bits_equal, assert_close, oracle_sampled,  # noqa: E402
-                         out_f64, to_dev)
+                         out_f64, to_bits, to_dev)
 
 
 def check_full(case, entry="prefill", what=""):
@@ -132,6 +132,64 @@ def test_small_shapes(spec):
                         window=W, rotary=rot, interleaved=inter,
                         rotary_rows=(M + S if rot else None))
     check_full(case, entry, f"small {spec}")
+
+
+# --------------------------------------------------------------------------
+# separate past and present buffers: present = past ++ new, then the op
+# --------------------------------------------------------------------------
+
+PRESENT = [
+    # dtype, B, S, H, Hkv, D, past_rows, present rows M, lens, window, rotary, entry
+    ("fp16", 3, 1, 32, 8, 128, 700, 701, [0, 350, 700], -1, False, "decode"),
+    ("bf16", 2, 64, 16, 2, 128, 300, 364, [300, 17], -1, True, "prefill"),
+    ("fp32", 2, 5, 4, 2, 8, 20, 25, [20, 3], -1, False, "prefill"),
+    ("bf16", 2, 40, 8, 2, 128, 256, 256, [256, 200], 128, False, "prefill"),   # present evicts
+    ("fp16", 2, 1, 8, 2, 128, 512, 512, [512, 100], 512, True, "decode"),     # decode evicts
+]
+
+
+@pytest.mark.parametrize("spec", PRESENT, ids=[f"{s[0]}-{s[-1]}-{i}" for i, s in enumerate(PRESENT)])
+def test_present_mode(spec):
+    import torch
+    dt, B, S, H, Hkv, D, P, M, lens, W, rot, entry = spec
+    seed = sum(map(ord, repr(spec))) % 1000
+    case = gi.make_case("present", dt, B, S, H, Hkv, D, M, [0] * B, seed, window=W, rotary=rot,
+                        rotary_rows=(M + S if rot else None))
+    case.seqlens_k = np.asarray(lens, np.int32)
+    rng = np.random.default_rng(seed + 1)
+    past_k = gi.fill_cache(rng, B, Hkv, P, D, lens, dt)
+    past_v = gi.fill_cache(rng, B, Hkv, P, D, lens, dt)
+    say(f"[gpu] present mode {spec}")
+    st, want, kc, vc, after = O.gqa_attention_present(case, past_k, past_v)
+    assert st == O.OK
+    dev = DevCase(case)                       # k_cache / v_cache: the present buffers
+    pk, pv = to_dev(past_k, dt), to_dev(past_v, dt)
+    import grouped_query_kv_amd as gqa
+    fn = gqa.gqa_attention_decode if entry == "decode" else gqa.gqa_attention_prefill
+    out = fn(dev.q, dev.k_new, dev.v_new, pk, pv, dev.lens_host, dev.lens_dev, scale=case.scale,
+             local_window_size=W, cos_cache=dev.cos, sin_cache=dev.sin,
+             present_key=dev.k_cache, present_value=dev.v_cache)
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "present k")
+    assert_bits_equal(gv, vc, "present v")
+    assert_bits_equal(to_bits(pk), past_k, "past k (never written)")
+    assert_bits_equal(to_bits(pv), past_v, "past v (never written)")
+    err = assert_close(out_f64(out, dt), want, dt, f"present {spec}")
+    say(f"[gpu]   max abs error {err:.3e}")
+    # the filled present buffer then serves as a shared buffer
+    if all(int(a) < M for a in after) or W > 0:
+        nxt = gi.next_decode_tokens(case, rng)
+        nxt.k_cache, nxt.v_cache, nxt.seqlens_k = kc, vc, after.astype(np.int32)
+        st2, want2, kc2, vc2, _ = O.gqa_attention(nxt, "decode")
+        assert st2 == O.OK
+        d2 = DevCase(nxt)
+        d2.k_cache, d2.v_cache = dev.k_cache, dev.v_cache
+        out2 = d2.run("decode")
+        gk2, gv2 = d2.caches()
+        assert_bits_equal(gk2, kc2, "present then shared k")
+        assert_bits_equal(gv2, vc2, "present then shared v")
+        assert_close(out_f64(out2, dt), want2, dt, "present then shared decode")
+    torch.cuda.synchronize()
 
 
 # --------------------------------------------------------------------------

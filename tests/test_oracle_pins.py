@@ -449,6 +449,58 @@ def test_windowed_chunks_equal_full_history_window_attention():
         big.k_cache, big.v_cache, big.seqlens_k = kc2, vc2, l2.astype(np.int32)
 
 
+def test_present_mode_by_index_code_and_equals_shared_mode():
+    """Separate past/present: present rows [0, L_b) are the past rows, then
+    the new rows at L_b.., every other present row untouched, past unchanged
+    (each row checked by decoding its index code); the outputs equal the
+    shared-mode op on a buffer that holds the same past."""
+    B, S, Hkv, D, P, M = 2, 3, 2, 4, 5, 11
+    lens = (5, 2)
+    case = tiny("fp32", B=B, S=S, H=4, Hkv=Hkv, D=D, M=M, lens=(0, 0), seed=4)
+    case.seqlens_k = np.asarray(lens, np.int32)
+
+    def code(b, g, j, d, new):
+        return 1000 * b + 100 * g + 10 * j + d + (0.5 if new else 0.0)
+
+    past = np.zeros((B, Hkv, P, D))
+    for b, g, j, d in np.ndindex(B, Hkv, P, D):
+        past[b, g, j, d] = code(b, g, j, d, False)
+    new = np.zeros((B, S, Hkv * D))
+    for b, i, g, d in np.ndindex(B, S, Hkv, D):
+        new[b, i, g * D + d] = code(b, g, i, d, True)
+    pk, pv = gi.to_bits(past, "fp32"), gi.to_bits(-past, "fp32")
+    case.k_new, case.v_new = gi.to_bits(new, "fp32"), gi.to_bits(-new, "fp32")
+    poison = case.k_cache.copy()
+    before = (pk.copy(), pv.copy())
+    st, out, kc, vc, after = O.gqa_attention_present(case, pk, pv)
+    assert st == O.OK and after.tolist() == [L + S for L in lens]
+    assert np.array_equal(pk, before[0]) and np.array_equal(pv, before[1])
+    for b, g, j, d in np.ndindex(B, Hkv, M, D):
+        L = lens[b]
+        got = kc[b, g, j, d]
+        if j < L:
+            want = O.to_f64(gi.to_bits(np.array(code(b, g, j, d, False)), "fp32"), "fp32")
+            assert O.to_f64(got, "fp32") == want
+        elif j < L + S:
+            assert O.to_f64(got, "fp32") == code(b, g, j - L, d, True)
+        else:
+            assert got == poison[b, g, j, d]
+        assert O.to_f64(vc[b, g, j, d], "fp32") == -O.to_f64(got, "fp32") or j >= L + S
+    shared = case.copy()
+    shared.k_cache[:, :, :P] = pk
+    shared.v_cache[:, :, :P] = pv
+    st2, out2, kc2, vc2, _ = O.gqa_attention(shared)
+    assert st2 == O.OK
+    np.testing.assert_array_equal(out, out2)
+    for b in range(B):
+        n = lens[b] + S
+        assert np.array_equal(kc[b, :, :n], kc2[b, :, :n])
+    # a past row count below some length is rejected, present untouched
+    short = pk[:, :, :4].copy()
+    st3, _, kc3, _, _ = O.gqa_attention_present(case, short, short)
+    assert st3 == O.INVALID and np.array_equal(kc3, case.k_cache)
+
+
 def test_prefill_then_decodes_equals_one_shot_prefill():
     n, k = 7, 4
     full = tiny("fp32", B=1, S=n + k, H=4, Hkv=2, D=8, M=16, lens=(0,), seed=12, rotary=True)
