@@ -86,6 +86,7 @@ class Case:
     cos: Optional[np.ndarray] = None      # fp32 [P, D/2] or None
     sin: Optional[np.ndarray] = None
     rotary_interleaved: int = 0
+    greedy_eviction: int = 0              # 1: evict only on overflow, keep the latest W
     seed: int = 0
     extra: dict = dataclasses.field(default_factory=dict)
 

@@ -10,11 +10,11 @@
 namespace gqa {
 namespace {
 
-// Destination row of sequence b's first new token. With a window the buffer
-// was just compacted, so the append starts at min(L, M - S).
-__device__ inline int dest_base(const int32_t* lens, int b, int S, int M, bool evicted) {
+// Destination row of sequence b's first new token. With a window (cap > 0)
+// the buffer was just compacted, so the append starts at the rows it kept.
+__device__ inline int dest_base(const int32_t* lens, int b, int S, int M, int cap) {
   int L = clamp_len(lens[b], 0, M);
-  if (evicted) L = L < M - S ? L : M - S;
+  if (cap > 0) L = kept_rows(L, S, M, cap);
   return clamp_len(L, 0, M - S);
 }
 
@@ -25,7 +25,7 @@ __global__ void __launch_bounds__(256) copy_rows_kernel(const U* __restrict__ sr
                                                         U* __restrict__ dst,
                                                         const int32_t* __restrict__ lens, int B,
                                                         int S, int Hkv, int M, int upr,
-                                                        int evicted) {
+                                                        int cap) {
   const int64_t total = int64_t(B) * S * Hkv * upr;
   for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < total;
        idx += int64_t(gridDim.x) * blockDim.x) {
@@ -34,7 +34,7 @@ __global__ void __launch_bounds__(256) copy_rows_kernel(const U* __restrict__ sr
     const int g = int(r % Hkv); r /= Hkv;
     const int i = int(r % S);
     const int b = int(r / S);
-    const int row = dest_base(lens, b, S, M, evicted != 0) + i;
+    const int row = dest_base(lens, b, S, M, cap) + i;
     dst[((int64_t(b) * Hkv + g) * M + row) * upr + u] = src[idx];
   }
 }
@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256) rotary_rows_kernel(
     const typename T::bits* __restrict__ src, typename T::bits* __restrict__ dst,
     const int32_t* __restrict__ lens, int B, int S, int Hkv, int D, int M,
     const float* __restrict__ cosv, const float* __restrict__ sinv, int rot_rows,
-    int interleaved, int evicted) {
+    int interleaved, int cap) {
   const int half = D / 2;
   const int64_t total = int64_t(B) * S * Hkv * half;
   for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < total;
@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(256) rotary_rows_kernel(
     const int64_t s0 = ((int64_t(b) * S + i) * Hkv + g) * D;
     typename T::bits a = src[s0 + e1], c = src[s0 + e2];
     rotate_pair<T>(a, c, cosv[int64_t(pos) * half + j], sinv[int64_t(pos) * half + j]);
-    const int row = dest_base(lens, b, S, M, evicted != 0) + i;
+    const int row = dest_base(lens, b, S, M, cap) + i;
     const int64_t d0 = ((int64_t(b) * Hkv + g) * M + row) * D;
     dst[d0 + e1] = a;
     dst[d0 + e2] = c;
@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(256) append_rows_vec_kernel(
     const uint16_t* __restrict__ v_src, uint16_t* __restrict__ v_dst,
     const int32_t* __restrict__ lens, int B, int S, int Hkv, int D, int M,
     const float* __restrict__ cosv, const float* __restrict__ sinv, int rot, int rot_rows,
-    int interleaved, int evicted) {
+    int interleaved, int cap) {
   const int half = D / 2;
   const int cpr = D / 16;                         // threads per row: 16 elements each
   const int64_t total = int64_t(B) * S * Hkv * cpr;
@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256) append_rows_vec_kernel(
     const int g = int(r % Hkv);
     const int64_t bi = r / Hkv;
     const int i = int(bi % S), b = int(bi / S);
-    const int row = dest_base(lens, b, S, M, evicted != 0) + i;
+    const int row = dest_base(lens, b, S, M, cap) + i;
     const int64_t doff = ((int64_t(b) * Hkv + g) * M + row) * D;
     // the two 16-byte runs of this thread (element offsets within the row)
     const int o1 = interleaved ? 16 * ch : 8 * ch;
@@ -173,17 +173,17 @@ hipError_t copy_rows(const void* src, void* dst, const Problem& p, bool evicted,
     const int upr = row_bytes / 16;
     hipLaunchKernelGGL(copy_rows_kernel<uint4>, dim3(grid_for(rows * upr)), dim3(256), 0, st,
                        static_cast<const uint4*>(src), static_cast<uint4*>(dst), p.lens_dev,
-                       p.B, p.S, p.Hkv, p.M, upr, int(evicted));
+                       p.B, p.S, p.Hkv, p.M, upr, evicted ? p.cap : 0);
   } else if (row_bytes % 4 == 0) {
     const int upr = row_bytes / 4;
     hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, dim3(grid_for(rows * upr)), dim3(256), 0,
                        st, static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst),
-                       p.lens_dev, p.B, p.S, p.Hkv, p.M, upr, int(evicted));
+                       p.lens_dev, p.B, p.S, p.Hkv, p.M, upr, evicted ? p.cap : 0);
   } else {
     const int upr = row_bytes / 2;
     hipLaunchKernelGGL(copy_rows_kernel<uint16_t>, dim3(grid_for(rows * upr)), dim3(256), 0,
                        st, static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
-                       p.lens_dev, p.B, p.S, p.Hkv, p.M, upr, int(evicted));
+                       p.lens_dev, p.B, p.S, p.Hkv, p.M, upr, evicted ? p.cap : 0);
   }
   return hipGetLastError();
 }
@@ -195,7 +195,7 @@ hipError_t rotary_rows(const Problem& p, bool evicted, hipStream_t st) {
   hipLaunchKernelGGL(rotary_rows_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
                      static_cast<const Bits*>(p.k_new), static_cast<Bits*>(p.k_cache),
                      p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,
-                     p.interleaved, int(evicted));
+                     p.interleaved, evicted ? p.cap : 0);
   return hipGetLastError();
 }
 
@@ -206,7 +206,7 @@ hipError_t append_rows_vec(const Problem& p, bool evicted, hipStream_t st) {
                      static_cast<const uint16_t*>(p.k_new), static_cast<uint16_t*>(p.k_cache),
                      static_cast<const uint16_t*>(p.v_new), static_cast<uint16_t*>(p.v_cache),
                      p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot, p.rot_rows,
-                     p.interleaved, int(evicted));
+                     p.interleaved, evicted ? p.cap : 0);
   return hipGetLastError();
 }
 

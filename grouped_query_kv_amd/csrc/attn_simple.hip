@@ -22,6 +22,7 @@ struct SimpleArgs {
   const float* cosv;
   const float* sinv;
   int B, S, H, Hkv, G, D, M, W;
+  int cap;             // rows an evicting sequence keeps: min(L, max(0, cap - S))
   int rot, rot_rows, interleaved;
   float scale_log2;
 };
@@ -37,7 +38,7 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(SimpleArgs a) {
   const int lane = threadIdx.x;
   const int D = a.D, g = h / a.G;
   const int L = clamp_len(a.lens[b], 0, a.M);
-  const int Lp = L < a.M - a.S ? L : a.M - a.S;   // after any eviction
+  const int Lp = kept_rows(L, a.S, a.M, a.cap);   // after any eviction
   const int p = Lp + i;
   const int kstart = a.W > 0 ? (p - a.W + 1 > 0 ? p - a.W + 1 : 0) : 0;
   const int kend = p + 1;
@@ -107,7 +108,7 @@ hipError_t launch_attention_simple(const Problem& p, hipStream_t st) {
   a.q = p.q; a.k_cache = p.k_cache; a.v_cache = p.v_cache; a.out = p.out;
   a.lens = p.lens_dev; a.cosv = p.cos; a.sinv = p.sin;
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.D = p.D; a.M = p.M;
-  a.W = p.window; a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
+  a.W = p.window; a.cap = p.cap; a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
   a.scale_log2 = p.scale * kLog2e;
   const dim3 grid(p.S, p.H, p.B);
   if (p.dtype == GQA_FP32) hipLaunchKernelGGL(attn_simple_kernel<F32>, grid, dim3(64), 0, st, a);

@@ -95,6 +95,7 @@ struct DecodeArgs {
   int shift;                            // fused eviction on: full sequences drop their oldest row
   int hb;                               // halo rows per unit (blocks of the buffer)
   int B, H, Hkv, G, M, W;
+  int cap;                              // rows an evicting sequence keeps: M - 1, or W - 1 (greedy)
   int rot, rot_rows, interleaved;
   int n_hg, hg_size;
   int workers;                          // waves in the launch that take a slice
@@ -113,7 +114,7 @@ struct Seq {
 __device__ inline Seq seq_of(const DecodeArgs& a, int b) {
   Seq s;
   s.L = clamp_len(a.hl[b], 0, a.M);
-  s.Lp = s.L < a.M - 1 ? s.L : a.M - 1;     // row of the new token (after any eviction)
+  s.Lp = kept_rows(s.L, 1, a.M, a.cap);     // row of the new token (after any eviction)
   s.kend = s.Lp + 1;
   s.kstart = a.W > 0 ? (s.kend - a.W > 0 ? s.kend - a.W : 0) : 0;
   s.nb = (s.kend - s.kstart + kKeys - 1) / kKeys;
@@ -802,14 +803,14 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.hb = ceil_div(p.M, kKeys);
   a.halo_k = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.decode_halo);
   a.halo_v = a.halo_k + int64_t(p.B) * p.Hkv * a.hb * kD;
-  a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window;
+  a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window; a.cap = p.cap;
   a.n_hg = ceil_div(p.G, kDecodeMaxHG);
   a.hg_size = ceil_div(p.G, a.n_hg);
   a.scale_log2 = p.scale * kLog2e;
   const int units_per_seq = p.Hkv * a.n_hg;
   int64_t total = 0;
   for (int b = 0; b < p.B; ++b) {
-    const int L = p.lens_host[b] < p.M - 1 ? p.lens_host[b] : p.M - 1;
+    const int L = kept_rows_host(p.lens_host[b], 1, p.M, p.cap);
     const int kend = L + 1;
     const int kstart = p.window > 0 ? (kend - p.window > 0 ? kend - p.window : 0) : 0;
     a.hl[b] = p.lens_host[b];

@@ -1,5 +1,6 @@
 // Window eviction: for every (b, kv head) with L_b + incoming > M, drop the
-// oldest d_b = L_b + incoming - M rows and move rows [d_b, L_b) to
+// oldest d_b = L_b + incoming - M rows (greedy eviction, cap = W < M:
+// d_b = L_b - min(L_b, max(0, W - incoming))) and move rows [d_b, L_b) to
 // [0, L_b - d_b), in place, for K and V. The buffer must stay where it is, so
 // this is a memmove towards lower rows.
 //
@@ -29,6 +30,7 @@ struct EvictArgs {
   char* halo;          // workspace scratch
   const int32_t* lens;
   int B, Hkv, M, incoming;
+  int cap;             // an evicting sequence keeps min(L, max(0, cap - incoming)) rows
   int upr;             // units per row
   int chunk_rows;      // C
   int nchunks;         // ceil(M / C): halo slot stride
@@ -51,8 +53,7 @@ __device__ inline U* halo_rows(const EvictArgs& a, int b, int y, int k) {
 __device__ inline int drop_of(const EvictArgs& a, int b, int* Lout) {
   const int L = clamp_len(a.lens[b], 0, a.M);
   *Lout = L;
-  const int d = L + a.incoming - a.M;
-  return d > 0 ? (d < L ? d : L) : 0;
+  return L - kept_rows(L, a.incoming, a.M, a.cap);
 }
 
 template <class U>
@@ -187,7 +188,7 @@ hipError_t launch_evict(const Problem& p, int incoming, int max_drop, void* ws,
   a.v_cache = static_cast<char*>(p.v_cache);
   a.halo = static_cast<char*>(ws) + lay.scratch;
   a.lens = p.lens_dev;
-  a.B = p.B; a.Hkv = p.Hkv; a.M = p.M; a.incoming = incoming;
+  a.B = p.B; a.Hkv = p.Hkv; a.M = p.M; a.incoming = incoming; a.cap = p.cap;
   a.upr = row_bytes / eg.unit;
   a.chunk_rows = eg.chunk_rows;
   a.nchunks = ceil_div(p.M, eg.chunk_rows);

@@ -96,11 +96,16 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
     if (entry != kAppend && (!q || !out)) return fail(GQA_ERR_INVALID_ARG, "q or out is NULL");
   }
   const bool windowed = W > 0 && entry != kAppend;
+  const bool greedy = o->greedy_eviction != 0 && entry != kAppend;
+  if (greedy && !windowed)
+    return fail(GQA_ERR_INVALID_ARG, "greedy_eviction needs a window (local_window_size > 0)");
+  const int cap = greedy ? W : M;
   *needs_evict = false;
   *max_drop = 0;
   if (windowed) {
     if (S > M) return fail(GQA_ERR_INVALID_ARG, "new_tokens %d > max_seq_len %d", S, M);
-    for (int b = 0; b < B; ++b) *max_drop = std::max(*max_drop, lens_host[b] + S - M);
+    for (int b = 0; b < B; ++b)
+      *max_drop = std::max(*max_drop, lens_host[b] - kept_rows_host(lens_host[b], S, M, cap));
     *needs_evict = *max_drop > 0;
   } else {
     for (int b = 0; b < B; ++b)
@@ -110,7 +115,7 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
   }
   Problem& P = *p;
   P.B = B; P.S = S; P.H = s->num_heads; P.Hkv = s->kv_num_heads; P.G = P.H / P.Hkv;
-  P.D = D; P.M = M; P.dtype = s->dtype; P.window = W;
+  P.D = D; P.M = M; P.dtype = s->dtype; P.window = W; P.cap = cap;
   P.scale = o->scale != 0.0f ? o->scale : 1.0f / sqrtf((float)D);
   P.rot = rot; P.cos = o->cos_cache; P.sin = o->sin_cache; P.rot_rows = o->rotary_rows;
   P.interleaved = o->rotary_interleaved != 0;
@@ -151,6 +156,7 @@ gqa_status windowed_chunk(const Problem& P, int max_drop, void* ws, const Worksp
   char* base = static_cast<char*>(ws);
   Problem F = P;
   F.M = lay.stage_rows;
+  F.cap = F.M;             // the frame holds past ++ new: nothing is evicted there
   F.k_cache = base + lay.stage_k;
   F.v_cache = base + lay.stage_v;
   const int row_bytes = P.D * elem_bytes(P.dtype);
@@ -376,7 +382,7 @@ gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming, void* k_ca
   if (max_drop > 0) {
     Problem P{};
     P.B = B; P.S = incoming; P.H = shape->kv_num_heads; P.Hkv = shape->kv_num_heads; P.G = 1;
-    P.D = shape->head_size; P.M = M; P.dtype = shape->dtype; P.window = M;
+    P.D = shape->head_size; P.M = M; P.dtype = shape->dtype; P.window = M; P.cap = M;
     P.k_cache = k_cache; P.v_cache = v_cache; P.lens_dev = seqlens_k_dev;
     P.lens_host = seqlens_k_host;
     hipError_t e = launch_evict(P, incoming, max_drop, workspace, lay,

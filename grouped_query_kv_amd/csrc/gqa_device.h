@@ -80,4 +80,13 @@ __device__ inline float wave_sum(float v) {
 // the buffer even if the device copy disagrees with the validated host copy.
 __device__ inline int clamp_len(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Rows a sequence of length L keeps before its S new rows (L + S <= M: all;
+// otherwise the min(L, max(0, cap - S)) most recent; cap = M, or W when
+// eviction is greedy).
+__device__ inline int kept_rows(int L, int S, int M, int cap) {
+  if (L + S <= M) return L;
+  const int k = cap - S > 0 ? cap - S : 0;
+  return L < k ? L : k;
+}
+
 }  // namespace gqa

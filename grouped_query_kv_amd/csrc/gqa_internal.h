@@ -15,6 +15,7 @@ struct Problem {
   int B, S, H, Hkv, G, D, M;
   int dtype;              // gqa_dtype
   int window;             // -1 off, else 1..M
+  int cap;                // an evicting sequence keeps min(L, max(0, cap - S)) rows: M, or W when greedy
   float scale;            // resolved (never 0)
   // rotary (rot == 0: none)
   int rot;
@@ -102,6 +103,15 @@ constexpr int kEvictChunkRows = GQA_EVICT_CHUNK_ROWS;       // rows per chunk of
 constexpr int kEvictRowsInFlight = GQA_EVICT_ROWS_IN_FLIGHT;  // rows of one column a thread has in flight
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Rows a sequence of length L keeps before its S new rows: all of them when
+// they fit, else the min(L, max(0, cap - S)) most recent (cap = M keeps the
+// min(L + S, M) most recent tokens in all; cap = W < M is greedy eviction).
+inline int kept_rows_host(int L, int S, int M, int cap) {
+  if (L + S <= M) return L;
+  const int k = cap - S > 0 ? cap - S : 0;
+  return L < k ? L : k;
+}
 
 // Eviction copy unit and rows per workgroup chunk for a row of `row_bytes`.
 struct EvictGeometry {

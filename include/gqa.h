@@ -39,7 +39,9 @@
  *      both nearest-even (exact products, so the cache is reproducible
  *      bit for bit);
  *   2. window eviction (only when local_window_size > 0 and L_b + S > M):
- *      rows [d, L_b) move to [0, L_b - d) with d = L_b + S - M;
+ *      rows [d, L_b) move to [0, L_b - d) with d = L_b + S - M, or with
+ *      greedy_eviction d = L_b - min(L_b, max(0, W - S)) (the sliding-window
+ *      follow-up's "conditional and greedy" eviction);
  *   3. append: cache[b, g, L'_b + i, :] = K/V row (b, i, g); no other byte
  *      of either cache is written;
  *   4. attention: query i of head h at position p = L'_b + i sees key j iff
@@ -104,6 +106,13 @@ typedef struct gqa_options {
   const float* sin_cache;      /* given together with cos_cache */
   int32_t rotary_rows;         /* rows in the tables; need L_b + S <= rows */
   int32_t rotary_interleaved;  /* 0: rotate-half pairs; 1: adjacent pairs */
+  int32_t greedy_eviction;     /* 0: on overflow keep the min(L_b + S, M) most
+                                  recent tokens (every step of a full cache
+                                  moves it); 1: needs a window W; on overflow
+                                  keep only min(L_b, max(0, W - S)) past rows,
+                                  so the buffer then holds the W most recent
+                                  tokens and the next M - W steps append
+                                  without moving anything */
 } gqa_options;
 
 /*

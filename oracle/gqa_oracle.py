@@ -54,6 +54,7 @@ from __future__ import annotations
 
 import copy
 import math
+from typing import Optional
 
 import numpy as np
 
@@ -125,6 +126,8 @@ def validate(case, entry: str) -> str:
         if B and S and int(lens.max()) + S > case.cos.shape[0]:
             return INVALID
     windowed = W > 0 and entry != "append"
+    if getattr(case, "greedy_eviction", 0) and entry != "append" and not windowed:
+        return INVALID                      # greedy eviction keeps the latest W: needs a window
     if windowed:
         if S > M:
             return INVALID
@@ -183,18 +186,27 @@ def rotated_bits(case, bits: np.ndarray, nh: int) -> np.ndarray:
 # cache edits: eviction ([P1] follow-up) and append ([P2] para 2)
 # ---------------------------------------------------------------------------
 
-def evict(k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray, incoming: int):
+def evict(k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray, incoming: int,
+          cap: Optional[int] = None):
     """Make room for `incoming` tokens by dropping the oldest ones.
 
-    For each sequence with L + incoming > M, d = L + incoming - M rows are
-    dropped and rows [d, L) move to [0, L - d), in place. Rows past L - d keep
-    their old bytes. Returns the new lengths.
+    Only a sequence with L + incoming > M evicts. By default ([P1] follow-up:
+    keep the min(total, capacity) most recent tokens) it drops
+    d = L + incoming - M rows. With cap = W < M (the follow-up's "conditional
+    and greedy" eviction: on overflow keep only the latest W) it keeps the
+    min(L, max(0, W - incoming)) most recent past rows, so that after the
+    append the buffer holds the W most recent tokens (all `incoming` of them
+    when incoming > W). Rows [d, L) move to [0, L - d), in place; rows past
+    L - d keep their old bytes. Returns the new lengths.
     """
     M = k_cache.shape[2]
+    cap = M if cap is None else cap
     new = np.array(lens, dtype=np.int32, copy=True)
     for b in range(len(lens)):
         L = int(lens[b])
-        d = L + incoming - M
+        if L + incoming <= M:
+            continue
+        d = L - min(L, max(0, cap - incoming))
         if d <= 0:
             continue
         for cache in (k_cache, v_cache):
@@ -285,7 +297,8 @@ def gqa_attention(case, entry: str = "prefill"):
             keys = np.concatenate([to_f64(kc[b, :, :L], case.dtype), to_f64(kr[b], case.dtype)], axis=1)
             vals = np.concatenate([to_f64(vc[b, :, :L], case.dtype), to_f64(vr[b], case.dtype)], axis=1)
             _attention(case, qr, keys, vals, L, out, b)
-        lens2 = evict(kc, vc, lens, S)
+        cap = W if getattr(case, "greedy_eviction", 0) else M
+        lens2 = evict(kc, vc, lens, S, cap)
         append(kc, vc, lens2, kr, vr)
     else:
         append(kc, vc, lens, kr, vr)

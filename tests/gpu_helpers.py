@@ -58,7 +58,7 @@ class DevCase:
         return fn(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.lens_host,
                   self.lens_dev, out, scale=c.scale, local_window_size=c.local_window_size,
                   cos_cache=self.cos, sin_cache=self.sin, rotary_interleaved=c.rotary_interleaved,
-                  workspace=workspace)
+                  workspace=workspace, greedy_eviction=bool(c.greedy_eviction))
 
     def append(self):
         import grouped_query_kv_amd as gqa

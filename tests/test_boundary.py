@@ -138,6 +138,13 @@ def test_windowed_chunk_needs_the_staging_workspace(g):
             == g.lib.gqa_workspace_bytes(ctypes.byref(one), None))
 
 
+def test_greedy_eviction_needs_a_window(g):
+    opts = g.Options(0.0, -1, None, None, 0, 0, 1)
+    assert _call(g, "prefill", _shape(g, S=3, M=16), opts, lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
+    assert "window" in g.lib.gqa_last_error().decode()
+    assert _call(g, "decode", _shape(g, S=1, M=16), opts, lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
+
+
 def test_workspace_too_small(g):
     need = g.lib.gqa_workspace_bytes(ctypes.byref(_shape(g, S=1, D=128, dtype=1)), None)
     assert need > 0

@@ -193,6 +193,53 @@ def test_present_mode(spec):
 
 
 # --------------------------------------------------------------------------
+# greedy eviction (capacity M > window W): move rows only on overflow
+# --------------------------------------------------------------------------
+
+GREEDY = [
+    # dtype, B, H, Hkv, D, M, W, lens, chunk sizes per step, rotary
+    ("bf16", 4, 32, 8, 128, 1024, 768, [1024, 1000, 500, 1024], [1, 1, 1, 1], False),
+    ("fp16", 3, 28, 4, 128, 512, 200, [512, 480, 100], [64, 1, 64, 1], True),
+    ("fp16", 2, 8, 2, 128, 256, 40, [256, 250], [64, 1, 1], False),          # S > W
+    ("fp32", 2, 4, 2, 8, 40, 10, [40, 30], [1, 5, 1, 1], True),
+]
+
+
+@pytest.mark.parametrize("spec", GREEDY, ids=[f"{s[0]}-{i}" for i, s in enumerate(GREEDY)])
+def test_greedy_eviction_rolling(spec):
+    dt, B, H, Hkv, D, M, W, lens, chunks, rot = spec
+    seed = sum(map(ord, repr(spec))) % 1000
+    rng = np.random.default_rng(seed)
+    case = gi.make_case("greedy", dt, B, chunks[0], H, Hkv, D, M, lens, seed, window=W,
+                        rotary=rot, rotary_rows=(M + max(chunks) if rot else None))
+    case.greedy_eviction = 1
+    dev = DevCase(case)
+    cache_k, cache_v = dev.k_cache, dev.v_cache
+    for step, S in enumerate(chunks):
+        entry = "decode" if S == 1 else "prefill"
+        say(f"[gpu] greedy {spec[:7]} step {step}: S={S} lens={case.seqlens_k.tolist()}")
+        st, want, kc, vc, after = O.gqa_attention(case, entry)
+        assert st == O.OK
+        out = dev.run(entry)
+        gk, gv = dev.caches()
+        assert_bits_equal(gk, kc, f"greedy step {step} k_cache")
+        assert_bits_equal(gv, vc, f"greedy step {step} v_cache")
+        err = assert_close(out_f64(out, dt), want, dt, f"greedy step {step}")
+        say(f"[gpu]   max abs error {err:.3e}, lengths after {after.tolist()}")
+        if step + 1 == len(chunks):
+            break
+        nxt = case.copy()
+        nxt.new_tokens = chunks[step + 1]
+        nxt.q = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, H * D)), dt)
+        nxt.k_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        nxt.v_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        nxt.k_cache, nxt.v_cache, nxt.seqlens_k = kc, vc, after.astype(np.int32)
+        case = nxt
+        dev = DevCase(case)
+        dev.k_cache, dev.v_cache = cache_k, cache_v
+
+
+# --------------------------------------------------------------------------
 # the halves: append and eviction on their own
 # --------------------------------------------------------------------------
 

@@ -501,6 +501,54 @@ def test_present_mode_by_index_code_and_equals_shared_mode():
     assert st3 == O.INVALID and np.array_equal(kc3, case.k_cache)
 
 
+def test_greedy_eviction_matches_default_outputs_and_moves_less():
+    """Greedy eviction (cache capacity M > window W): the attention outputs
+    equal the default mode's at every step (both keep every key a window can
+    reach), the buffer always holds the most recent tokens of the history,
+    oldest first, and rows move only in steps whose append would overflow,
+    which then leave exactly the W most recent tokens (all new ones if S > W)."""
+    rng = np.random.default_rng(17)
+    B, Hkv, D, M, W = 2, 1, 2, 12, 5
+    history = [[] for _ in range(B)]
+    base = tiny("fp32", B=B, S=1, H=2, Hkv=Hkv, D=D, M=M, lens=(0, 0), window=W)
+    greedy, default = base.copy(), base.copy()
+    greedy.greedy_eviction = 1
+    serial, moves = 0, 0
+    for step in range(40):
+        S = int(rng.integers(1, 7 if step % 5 else 2))
+        codes = np.zeros((B, S, Hkv * D))
+        for b in range(B):
+            for i in range(S):
+                serial += 1
+                codes[b, i, :] = serial
+                history[b].append(serial)
+        q = gi.to_bits(rng.standard_normal((B, S, 2 * D)), "fp32")
+        outs = []
+        for c in (greedy, default):
+            c.new_tokens, c.q = S, q
+            c.k_new, c.v_new = gi.to_bits(codes, "fp32"), gi.to_bits(-codes, "fp32")
+            before = np.asarray(c.seqlens_k).copy()
+            st, out, kc, vc, lens = O.gqa_attention(c)
+            assert st == O.OK
+            outs.append(out)
+            if c is greedy:
+                for b in range(B):
+                    n = int(lens[b])
+                    overflow = int(before[b]) + S > M
+                    moves += overflow
+                    want = max(W, S) if overflow else int(before[b]) + S
+                    assert n == min(want, len(history[b]))
+                    got = O.to_f64(kc[b, 0, :n, 0], "fp32").tolist()
+                    assert got == [float(x) for x in history[b][-n:]]
+            c.k_cache, c.v_cache, c.seqlens_k = kc, vc, lens.astype(np.int32)
+        np.testing.assert_allclose(outs[0], outs[1], rtol=1e-13, atol=1e-12)
+    assert 0 < moves < 40 * B // 2
+    # without a window there is nothing to keep: rejected
+    bad = base.copy()
+    bad.greedy_eviction, bad.local_window_size = 1, -1
+    assert O.validate(bad, "prefill") == O.INVALID
+
+
 def test_prefill_then_decodes_equals_one_shot_prefill():
     n, k = 7, 4
     full = tiny("fp32", B=1, S=n + k, H=4, Hkv=2, D=8, M=16, lens=(0,), seed=12, rotary=True)
