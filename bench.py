@@ -242,8 +242,32 @@ def prefill_call(gqa):
         gqa.gqa_attention_prefill(s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.lens_host, s.lens_dev,
                                   s.out, scale=c.scale, local_window_size=c.local_window_size,
                                   cos_cache=s.cos, sin_cache=s.sin,
-                                  rotary_interleaved=c.rotary_interleaved)
+                                  rotary_interleaved=c.rotary_interleaved,
+                                  greedy_eviction=bool(c.greedy_eviction))
     return call
+
+
+def present_call(gqa):
+    """Separate past (the set's caches) and present buffers."""
+    def call(s):
+        c = s.case
+        gqa.gqa_attention_prefill(s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.lens_host, s.lens_dev,
+                                  s.out, scale=c.scale, local_window_size=c.local_window_size,
+                                  present_key=s.present_k, present_value=s.present_v)
+    return call
+
+
+def run_leg(torch, name, case, call, steps, warmup, prepare=None):
+    log(f"[bench] {name} sets: building")
+    sets = make_sets(case, torch, case.seed or 7)
+    for x in sets:
+        if prepare:
+            prepare(x)
+    log(f"[bench] {name}: {len(sets)} input sets, timing {steps} steps")
+    w, d, p_ = time_calls(torch, sets, call, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return w, stats(d, p_)
 
 
 # ----------------------------------------------------------------------------
@@ -284,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="decode,prefill,continuation,window",
+    ap.add_argument("--only", default="decode,prefill,continuation,window,chunks,present,greedy",
                     help="workloads to run, comma-separated; the split-KV decode (the headline) "
                          "always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -313,7 +337,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     which = set(args.only.split(","))
-    unknown = which - {"decode", "prefill", "continuation", "window"}
+    unknown = which - {"decode", "prefill", "continuation", "window", "chunks", "present", "greedy"}
     if unknown:
         sys.exit(f"--only: unknown workloads {sorted(unknown)}")
     result = {}
@@ -378,6 +402,57 @@ def main():
             "ms_per_call_wall": w, **st}
         del sets
         torch.cuda.empty_cache()
+
+    if "chunks" in which:
+        # chunks of 128 tokens into the full window caches: attention over
+        # past ++ new (staging frames), then eviction of 128 rows and append
+        ch = gi.make_case("window-chunks-bf16", "bf16", 8, 128, 32, 8, 128, 4096, [4096] * 8, 6,
+                          window=4096)
+        w, st = run_leg(torch, "windowed chunks", ch, prefill_call(gqa), max(5, args.steps // 2),
+                        max(2, args.warmup // 2))
+        fl = prefill_flops(ch)
+        kept = 8 * 8 * (4096 - 128) * 128 * 2 * 2          # K and V rows that move, bytes
+        extra["windowed_chunks"] = {
+            "workload": "bf16 windowed chunks B=8 H=32 Hkv=8 D=128 M=W=4096, full cache, S=128",
+            "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12, "flops": fl,
+            "kept_rows_move_bytes_rw": 2 * kept, "ms_per_call_wall": w, **st}
+    if "present" in which:
+        pc = gi.workload("split-kv-decode-fp16")
+
+        def with_present(x):
+            x.present_k = torch.empty_like(x.k_cache)
+            x.present_v = torch.empty_like(x.v_cache)
+        w, st = run_leg(torch, "present-mode decode", pc, present_call(gqa), args.steps, args.warmup,
+                        with_present)
+        copy = sum(int(L) for L in pc.seqlens_k) * 8 * 128 * 2 * 2 * 2   # past rows read + written
+        byts = decode_bytes(pc, [int(x) for x in pc.seqlens_k]) + copy
+        extra["present_decode"] = {
+            "workload": "fp16 decode as the split-KV decode, past and present in separate buffers",
+            "gbs": byts / (st["mean_ms"] * 1e-3) / 1e9, "bytes_per_call": byts,
+            "frac_hbm_peak": byts / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_per_call_wall": w, **st}
+    if "greedy" in which:
+        # capacity 4608 rows, window 4096: a step that fits only attends
+        # (4096 keys); one step in 512 overflows and first keeps the 4095
+        # newest rows
+        M, W = 4608, 4096
+        plain = gi.make_case("greedy-window-bf16", "bf16", 8, 1, 32, 8, 128, M, [4096] * 8, 8,
+                             window=W)
+        plain.greedy_eviction = 1
+        full = gi.make_case("greedy-window-bf16", "bf16", 8, 1, 32, 8, 128, M, [M] * 8, 8, window=W)
+        full.greedy_eviction = 1
+        w1, st1 = run_leg(torch, "greedy window decode (fits)", plain, prefill_call(gqa), args.steps,
+                          args.warmup)
+        w2, st2 = run_leg(torch, "greedy window decode (overflows)", full, prefill_call(gqa),
+                          max(5, args.steps // 2), max(2, args.warmup // 2))
+        att = decode_bytes(plain, [4095] * 8, window=W)
+        amort = (st2["mean_ms"] + (M - W - 1) * st1["mean_ms"]) / (M - W)
+        extra["greedy_window_decode"] = {
+            "workload": "bf16 window decode B=8 H=32 Hkv=8 D=128 W=4096, capacity 4608, greedy eviction",
+            "fits_ms": st1["mean_ms"], "overflow_ms": st2["mean_ms"],
+            "amortized_ms_per_step": amort, "attention_bytes": att,
+            "attention_gbs_when_fits": att / (st1["mean_ms"] * 1e-3) / 1e9,
+            "fits_wall_ms": w1, "overflow_wall_ms": w2}
 
     cpu = None
     if not args.no_cpu_baseline:
