@@ -47,11 +47,11 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "54b02924ca1b01c9bd0eded68248a412fae317c817a3568a7b2b676c880486af",
+                "4366ce18d2a2f69ac34e5e098cc1ec4c3d291a5f4a3b01994d8e48e90cb5ee9c",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "d027341bb70095180b1770782f0b845e62eb2f2be5daa28a5e726f7d822827ff"},
-    "fetch_kib": 74189.48, "write_kib": 1050.28,
-    "fetch_scale": 524288.0 / 262156.81, "write_scale": 1.0,
+                "05bcc4acc7c013e31fb5f97f28e954e6313632b1cac4d940527820c775e848be"},
+    "fetch_kib": 74133.375, "write_kib": 1050.28125,
+    "fetch_scale": 524288.0 / 262156.9625, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
