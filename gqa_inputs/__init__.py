@@ -87,6 +87,7 @@ class Case:
     sin: Optional[np.ndarray] = None
     rotary_interleaved: int = 0
     greedy_eviction: int = 0              # 1: evict only on overflow, keep the latest W
+    attention_bias: Optional[np.ndarray] = None   # bits [B or 1, H or 1, S, T] or None
     seed: int = 0
     extra: dict = dataclasses.field(default_factory=dict)
 

@@ -52,7 +52,9 @@ class Options(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_float), ("local_window_size", ctypes.c_int32),
                 ("cos_cache", ctypes.c_void_p), ("sin_cache", ctypes.c_void_p),
                 ("rotary_rows", ctypes.c_int32), ("rotary_interleaved", ctypes.c_int32),
-                ("greedy_eviction", ctypes.c_int32)]
+                ("greedy_eviction", ctypes.c_int32),
+                ("attention_bias", ctypes.c_void_p), ("bias_batch", ctypes.c_int32),
+                ("bias_heads", ctypes.c_int32), ("bias_total", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -149,10 +151,16 @@ def make_shape(B, S, H, Hkv, D, M, dtype) -> Shape:
 
 
 def make_options(scale=0.0, local_window_size=-1, cos_cache=None, sin_cache=None,
-                 rotary_interleaved=False, greedy_eviction=False) -> Options:
+                 rotary_interleaved=False, greedy_eviction=False, attention_bias=None) -> Options:
     rows = int(cos_cache.shape[0]) if cos_cache is not None else 0
+    bb = bh = bt = 0
+    if attention_bias is not None:
+        if attention_bias.dim() != 4:
+            raise GQAError(GQA_ERR_INVALID_ARG, "attention_bias must be [B or 1, H or 1, S, T]")
+        bb, bh, bt = (int(attention_bias.shape[i]) for i in (0, 1, 3))
     return Options(float(scale), int(local_window_size), _ptr(cos_cache), _ptr(sin_cache), rows,
-                   int(bool(rotary_interleaved)), int(bool(greedy_eviction)))
+                   int(bool(rotary_interleaved)), int(bool(greedy_eviction)), _ptr(attention_bias),
+                   bb, bh, bt)
 
 
 _workspaces = {}
@@ -208,7 +216,8 @@ def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
 
 def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev, out,
                scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
-               present_key, present_value, workspace, stream, greedy_eviction=False):
+               present_key, present_value, workspace, stream, greedy_eviction=False,
+               attention_bias=None):
     past_k = past_v = None
     past_rows = 0
     if (present_key is None) != (present_value is None):
@@ -238,8 +247,13 @@ def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise GQAError(GQA_ERR_INVALID_ARG, "out must match q")
     shape = make_shape(B, S, H, Hkv, D, M, dtype_code(q))
+    if attention_bias is not None:
+        _contig(attention_bias)
+        if (attention_bias.dtype != q.dtype or attention_bias.dim() != 4
+                or int(attention_bias.shape[2]) != S):
+            raise GQAError(GQA_ERR_INVALID_ARG, "attention_bias must be [B or 1, H or 1, S, T] in q's dtype")
     opts = make_options(scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
-                        greedy_eviction)
+                        greedy_eviction, attention_bias)
     hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
     if workspace is None:
         ws, nbytes = workspace_for(shape, q.device, opts)
@@ -263,7 +277,8 @@ def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_
 def gqa_attention_prefill(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
                           out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
                           sin_cache=None, rotary_interleaved=False, present_key=None,
-                          present_value=None, workspace=None, stream=None, greedy_eviction=False):
+                          present_value=None, workspace=None, stream=None, greedy_eviction=False,
+                          attention_bias=None):
     """The whole op for S >= 1 new tokens; returns out [B, S, H*D].
 
     With present_key/present_value in buffers other than k_cache/v_cache,
@@ -272,18 +287,19 @@ def gqa_attention_prefill(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seq
     return _attention(lib.gqa_attention_prefill, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
                       seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
                       rotary_interleaved, present_key, present_value, workspace, stream,
-                      greedy_eviction)
+                      greedy_eviction, attention_bias)
 
 
 def gqa_attention_decode(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
                          out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
                          sin_cache=None, rotary_interleaved=False, present_key=None,
-                         present_value=None, workspace=None, stream=None, greedy_eviction=False):
+                         present_value=None, workspace=None, stream=None, greedy_eviction=False,
+                         attention_bias=None):
     """The whole op for one new token per sequence; returns out [B, 1, H*D]."""
     return _attention(lib.gqa_attention_decode, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
                       seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
                       rotary_interleaved, present_key, present_value, workspace, stream,
-                      greedy_eviction)
+                      greedy_eviction, attention_bias)
 
 
 def gqa_evict_window(k_cache, v_cache, seqlens_k_host, seqlens_k_dev, incoming: int, *,

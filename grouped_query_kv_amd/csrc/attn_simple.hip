@@ -25,6 +25,9 @@ struct SimpleArgs {
   int cap;             // rows an evicting sequence keeps: min(L, max(0, cap - S))
   int rot, rot_rows, interleaved;
   float scale_log2;
+  const void* bias;    // nullptr: none; element (b, h, i, col) at b bs + h hs + i T + col
+  int64_t bias_bs, bias_hs;
+  int bias_T;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -60,6 +63,9 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(SimpleArgs a) {
   }
   __syncthreads();
 
+  const Bits* bias_row = a.bias ? static_cast<const Bits*>(a.bias) + b * a.bias_bs + h * a.bias_hs +
+                                      int64_t(i) * a.bias_T
+                                : nullptr;
   const Bits* K = static_cast<const Bits*>(a.k_cache) + (int64_t(b) * a.Hkv + g) * a.M * D;
   const Bits* V = static_cast<const Bits*>(a.v_cache) + (int64_t(b) * a.Hkv + g) * a.M * D;
   float m = -INFINITY, l = 0.f;
@@ -72,6 +78,8 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(SimpleArgs a) {
       float dot = 0.f;
       for (int d = 0; d < D; ++d) dot = fmaf(qs[d], T::to_float(kr[d]), dot);
       s = dot * a.scale_log2;
+      if (bias_row)   // the key at row j after an eviction of L - Lp rows is at position j + L - Lp
+        s = fmaf(T::to_float(bias_row[j + (L - Lp)]), kLog2e, s);
     }
     const float mn = fmaxf(m, wave_max(s));
     const float alpha = exp2f(m - mn);
@@ -110,6 +118,7 @@ hipError_t launch_attention_simple(const Problem& p, hipStream_t st) {
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.D = p.D; a.M = p.M;
   a.W = p.window; a.cap = p.cap; a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
   a.scale_log2 = p.scale * kLog2e;
+  a.bias = p.bias; a.bias_bs = p.bias_bs; a.bias_hs = p.bias_hs; a.bias_T = p.bias_T;
   const dim3 grid(p.S, p.H, p.B);
   if (p.dtype == GQA_FP32) hipLaunchKernelGGL(attn_simple_kernel<F32>, grid, dim3(64), 0, st, a);
   else if (p.dtype == GQA_FP16) hipLaunchKernelGGL(attn_simple_kernel<F16>, grid, dim3(64), 0, st, a);

@@ -102,6 +102,8 @@ struct DecodeArgs {
   int64_t total;                        // T: blocks over all units
   int fits32;                           // (T + 1) * workers < 2^32: slice bounds in 32 bits
   float scale_log2;
+  const uint16_t* bias;                 // additive bias (b, h, column) at b bias_bs + h bias_hs + column
+  int64_t bias_bs, bias_hs;
   int32_t hl[kDecodeArgBatch];          // past lengths
   int32_t pb[kDecodeArgBatch + 1];      // first global block of sequence b (all its units)
 };
@@ -129,6 +131,7 @@ struct Blk {
   int kb, kend, Lp;        // first key, unit end, new-token row
   int b, g, ub, i, nb;
   int d;                   // fused eviction: key r is read from buffer row r + d
+  int coff;                // bias column of key r: r + coff (its position before any eviction)
 };
 
 __device__ inline void set_unit(Blk& k, const DecodeArgs& a) {
@@ -142,6 +145,7 @@ __device__ inline void set_unit(Blk& k, const DecodeArgs& a) {
   k.nb = s.nb;
   k.kb = s.kstart + kKeys * k.i;
   k.d = s.d;
+  k.coff = s.L - s.Lp;
 }
 
 __device__ inline Blk locate(const DecodeArgs& a, int64_t x) {
@@ -242,6 +246,7 @@ __device__ inline void wave_lds_sync() {
 // value: an indexed array here would end up in memory.
 struct KV {
   uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  uint32_t b01, b23;       // with a bias: the lane's four bias values (keys 4 q4 .. + 3 of head n)
 };
 
 // Q^T of a unit for lane (n, q4): head n, dims 32 i + 8 q4 .. + 7 in member i.
@@ -251,6 +256,7 @@ struct Q4 {
 
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+template <bool kBias>
 __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
   // fused eviction: key `row` is buffer row row + d. The first row of the
@@ -268,6 +274,23 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   KV r;
   r.k0 = ld16(kp); r.k1 = ld16(kp + 32); r.k2 = ld16(kp + 64); r.k3 = ld16(kp + 96);
   r.v0 = ld16(vp); r.v1 = ld16(vp + 32); r.v2 = ld16(vp + 64); r.v3 = ld16(vp + 96);
+  if (kBias) {
+    // head column n of the unit (padding columns reuse head h0; their
+    // scores are never written out), keys kb + 4 q4 + e clamped to the
+    // unit's last key: columns stay below L_b + 1 <= bias_total
+    const int hg = k.ub % a.n_hg;
+    const int h0 = k.g * a.G + hg * a.hg_size;
+    const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
+    const uint16_t* brow = a.bias + k.b * a.bias_bs + int64_t(h0 + (n < nheads ? n : 0)) * a.bias_hs;
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = k.kb + 4 * q4 + j < k.kend ? k.kb + 4 * q4 + j : k.kend - 1;
+      e[j] = brow[key + k.coff];
+    }
+    r.b01 = e[0] | (e[1] << 16);
+    r.b23 = e[2] | (e[3] << 16);
+  }
   return r;
 }
 
@@ -298,7 +321,7 @@ __device__ inline uint32_t pack2(float x, float y) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <class T>
+template <class T, bool kBias>
 __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
                                const DecodeArgs& a, int lane, unsigned char* vt) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -354,8 +377,14 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
   acc = Mma<T>::qk(r.k3, qv.c3, acc);
   float sv[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-    sv[rr] = k.kb + 4 * q4 + rr < k.kend ? acc[rr] * a.scale_log2 : -INFINITY;
+  for (int rr = 0; rr < 4; ++rr) {
+    float x = acc[rr] * a.scale_log2;
+    if (kBias) {
+      const uint32_t w = rr < 2 ? r.b01 : r.b23;
+      x = fmaf(T::to_float(typename T::bits((w >> (16 * (rr & 1))) & 0xFFFFu)), kLog2e, x);
+    }
+    sv[rr] = k.kb + 4 * q4 + rr < k.kend ? x : -INFINITY;
+  }
   float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
@@ -582,7 +611,7 @@ __device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds
 // One launch: workgroups of kDecodeWaves waves; every wave of the grid
 // streams its own slice (see the top of the file), then the workgroup
 // combines the partials its waves left.
-template <class T>
+template <class T, bool kBias>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
   __shared__ int sh_tab[kDecodeWaves][2][2];        // per wave, slot: (b, ub) or b = -1
@@ -611,7 +640,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (S < E) {
     Blk cur = locate(a, S);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
-    KV rc = load_kv(a, cur, n, q4, S + 1 >= E);
+    KV rc = load_kv<kBias>(a, cur, n, q4, S + 1 >= E);
     Acc s;
     acc_reset(s);
     bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
@@ -621,7 +650,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // next (x + 2), clamped to the slice's last block. Q rows are loaded when
     // their unit starts (a small, cache-resident read).
     Blk nxt = S + 1 < E ? next_block(a, cur) : cur;        // block x + 1
-    KV r1 = load_kv(a, nxt, n, q4, S + 2 >= E);
+    KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
     Blk ahead = S + 2 < E ? next_block(a, nxt) : nxt;       // block x + 2
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
@@ -629,8 +658,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv(a, ahead, n, q4, x + 3 >= E);   // ahead = min(x + 2, E - 1)
-      compute<T>(s, r_cur, qv, cur, a, lane, vt);
+      r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E);   // ahead = min(x + 2, E - 1)
+      compute<T, kBias>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
         if (shared) {
@@ -807,6 +836,8 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.n_hg = ceil_div(p.G, kDecodeMaxHG);
   a.hg_size = ceil_div(p.G, a.n_hg);
   a.scale_log2 = p.scale * kLog2e;
+  a.bias = static_cast<const uint16_t*>(p.bias);
+  a.bias_bs = p.bias_bs; a.bias_hs = p.bias_hs;
   const int units_per_seq = p.Hkv * a.n_hg;
   int64_t total = 0;
   for (int b = 0; b < p.B; ++b) {
@@ -837,10 +868,15 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.dtype == GQA_FP16)
-    hipLaunchKernelGGL(decode_kernel<F16>, dim3(blocks), dim3(kThreads), 0, st, a);
+  const bool fp16 = p.dtype == GQA_FP16;
+  if (p.bias && fp16)
+    hipLaunchKernelGGL((decode_kernel<F16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else if (p.bias)
+    hipLaunchKernelGGL((decode_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else if (fp16)
+    hipLaunchKernelGGL((decode_kernel<F16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(decode_kernel<BF16>, dim3(blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

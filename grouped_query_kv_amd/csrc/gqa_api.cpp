@@ -113,7 +113,24 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
         return fail(GQA_ERR_NO_ROOM, "sequence %d: %d past + %d new > max_seq_len %d", b,
                     lens_host[b], S, M);
   }
+  const int64_t H = s->num_heads;
+  const bool biased = o->attention_bias != nullptr && entry != kAppend;
+  if (biased) {
+    if (o->bias_batch != 1 && o->bias_batch != B)
+      return fail(GQA_ERR_INVALID_ARG, "bias_batch %d is neither 1 nor batch %d", o->bias_batch, B);
+    if (o->bias_heads != 1 && o->bias_heads != H)
+      return fail(GQA_ERR_INVALID_ARG, "bias_heads %d is neither 1 nor num_heads %d",
+                  o->bias_heads, (int)H);
+    int need = 1;
+    for (int b = 0; b < B; ++b) need = std::max(need, lens_host[b] + S);
+    if (o->bias_total < need)
+      return fail(GQA_ERR_INVALID_ARG, "bias_total %d < %d (past + new tokens)", o->bias_total, need);
+  }
   Problem& P = *p;
+  P.bias = biased ? o->attention_bias : nullptr;
+  P.bias_T = biased ? o->bias_total : 0;
+  P.bias_hs = biased && o->bias_heads != 1 ? int64_t(S) * o->bias_total : 0;
+  P.bias_bs = biased && o->bias_batch != 1 ? int64_t(o->bias_heads) * S * o->bias_total : 0;
   P.B = B; P.S = S; P.H = s->num_heads; P.Hkv = s->kv_num_heads; P.G = P.H / P.Hkv;
   P.D = D; P.M = M; P.dtype = s->dtype; P.window = W; P.cap = cap;
   P.scale = o->scale != 0.0f ? o->scale : 1.0f / sqrtf((float)D);
@@ -139,8 +156,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Attention over one call's rows on the buffers the Problem names (the new
 // rows already appended there).
 hipError_t attend(const Problem& P, void* ws, const WorkspaceLayout& lay, hipStream_t hs) {
-  return prefill_fast_supported(P) ? launch_prefill_fast(P, ws, lay, hs)
-                                   : launch_attention_simple(P, hs);
+  return prefill_fast_supported(P) && !P.bias ? launch_prefill_fast(P, ws, lay, hs)
+                                             : launch_attention_simple(P, hs);
 }
 
 // S > 1 with a window where some sequence must evict. Queries early in the

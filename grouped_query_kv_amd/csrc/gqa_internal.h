@@ -32,6 +32,11 @@ struct Problem {
   void* out;
   const int32_t* lens_dev;
   const int32_t* lens_host;
+  // additive bias (bias == nullptr: none): element of (b, h, i, column) at
+  // b * bias_bs + h * bias_hs + i * bias_T + column (strides 0 broadcast)
+  const void* bias;
+  int64_t bias_bs, bias_hs;
+  int bias_T;
 };
 
 // Workspace carving (byte offsets from the workspace base). The layout is a

@@ -46,8 +46,13 @@
  *      of either cache is written;
  *   4. attention: query i of head h at position p = L'_b + i sees key j iff
  *      j <= p and (window off or j >= p - W + 1); out = softmax(scale *
- *      q k^T) v with fp32 accumulation; bytes of the cache past L'_b + S are
- *      never read.
+ *      q k^T + bias) v with fp32 accumulation; bytes of the cache past
+ *      L'_b + S are never read. The optional bias (attention_bias, the
+ *      sliding-window follow-up of the GroupQueryAttention clarification
+ *      gives its shape) takes bias[b, h, i, j + d_b] for the key at row j
+ *      after an eviction of d_b rows, i.e. its column is the key's position
+ *      in past ++ new. With a bias the split-KV decode (S = 1, fp16/bf16,
+ *      D = 128) keeps its fast kernel; other calls use the plain kernel.
  *
  * Ownership and threading: every pointer except *_host arguments is device
  * memory owned by the caller. The library never allocates, frees or
@@ -113,6 +118,14 @@ typedef struct gqa_options {
                                   so the buffer then holds the W most recent
                                   tokens and the next M - W steps append
                                   without moving anything */
+  const void* attention_bias;  /* NULL: none; else device [bias_batch,
+                                  bias_heads, S, bias_total] in the dtype,
+                                  added to scale * q.k before the softmax */
+  int32_t bias_batch;          /* B, or 1 to share one bias across sequences */
+  int32_t bias_heads;          /* H, or 1 to share one bias across heads */
+  int32_t bias_total;          /* T >= max_b (L_b + S): column j is the key at
+                                  position j of past ++ new (before any
+                                  eviction of this call) */
 } gqa_options;
 
 /*

@@ -48,6 +48,7 @@ def brute_attention(case, window_before_evict: bool = True):
     B, S, H, Hkv, D, M = (case.batch, case.new_tokens, case.num_heads,
                           case.kv_num_heads, case.head_size, case.max_seq_len)
     W, dt = case.local_window_size, case.dtype
+    bias = getattr(case, "attention_bias", None)
     G = H // Hkv
     sc = case.scale if case.scale != 0.0 else 1.0 / math.sqrt(D)
     kc = [[[[int(case.k_cache[b, g, t, d]) for d in range(D)] for t in range(M)]
@@ -88,7 +89,12 @@ def brute_attention(case, window_before_evict: bool = True):
                     dot = 0.0
                     for d in range(D):
                         dot += _val(qrow[i][h][d], dt) * _val(logical_k[g][j][d], dt)
-                    scores.append((j, dot * sc))
+                    extra = 0.0
+                    if bias is not None:   # column j: position j of past ++ new
+                        bb_ = b if bias.shape[0] > 1 else 0
+                        hh_ = h if bias.shape[1] > 1 else 0
+                        extra = _val(int(bias[bb_, hh_, i, j]), dt)
+                    scores.append((j, dot * sc + extra))
                 mx = max(s for _, s in scores)
                 den = sum(math.exp(s - mx) for _, s in scores)
                 for d in range(D):

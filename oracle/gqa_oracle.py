@@ -125,6 +125,12 @@ def validate(case, entry: str) -> str:
             return INVALID
         if B and S and int(lens.max()) + S > case.cos.shape[0]:
             return INVALID
+    bias = getattr(case, "attention_bias", None)
+    if bias is not None and entry != "append":
+        if bias.ndim != 4 or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H):
+            return INVALID
+        if bias.shape[2] != S or (B and bias.shape[3] < int((lens + S).max())) or bias.shape[3] < 1:
+            return INVALID
     windowed = W > 0 and entry != "append"
     if getattr(case, "greedy_eviction", 0) and entry != "append" and not windowed:
         return INVALID                      # greedy eviction keeps the latest W: needs a window
@@ -240,9 +246,12 @@ def allowed_mask(S: int, T: int, past: int, W: int) -> np.ndarray:
 
 
 def attend_one(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.ndarray,
-               scale: float, return_weights: bool = False):
-    """softmax(scale * q k^T, masked) v for one head; q [S,D], k/v [T,D] fp64."""
+               scale: float, return_weights: bool = False, bias: Optional[np.ndarray] = None):
+    """softmax(scale * q k^T + bias, masked) v for one head; q [S,D], k/v [T,D]
+    fp64, bias [S,T] fp64 or None."""
     s = (q @ k.T) * scale
+    if bias is not None:
+        s = s + bias
     s = np.where(allowed, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     e = np.where(allowed, np.exp(s - m), 0.0)
@@ -264,9 +273,16 @@ def _attention(case, qr_bits, keys_f64, vals_f64, past, out, b):
     allowed = allowed_mask(S, T, past, case.local_window_size)
     qf = to_f64(qr_bits[b], case.dtype)           # [H, S, D]
     sc = scale_of(case)
+    bias = getattr(case, "attention_bias", None)
     for h in range(H):
         g = h // G
-        out[b, h] = attend_one(qf[h], keys_f64[g], vals_f64[g], allowed, sc)
+        # the bias column of a key is its position in past ++ new, which is
+        # its index in `keys_f64` here (both branches of the whole op)
+        bh = None
+        if bias is not None:
+            bh = to_f64(bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0, :, :T],
+                        case.dtype)
+        out[b, h] = attend_one(qf[h], keys_f64[g], vals_f64[g], allowed, sc, bias=bh)
 
 
 def gqa_attention(case, entry: str = "prefill"):

@@ -41,6 +41,9 @@ class DevCase:
         self.v_cache = to_dev(case.v_cache, dt, device)
         self.lens_host = np.asarray(case.seqlens_k, np.int32).copy()
         self.lens_dev = torch.from_numpy(self.lens_host.copy()).to(device)
+        self.bias = None
+        if getattr(case, "attention_bias", None) is not None:
+            self.bias = to_dev(case.attention_bias, dt, device)
         self.cos = self.sin = None
         if case.cos is not None:
             self.cos = torch.from_numpy(case.cos).to(device)
@@ -58,7 +61,8 @@ class DevCase:
         return fn(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.lens_host,
                   self.lens_dev, out, scale=c.scale, local_window_size=c.local_window_size,
                   cos_cache=self.cos, sin_cache=self.sin, rotary_interleaved=c.rotary_interleaved,
-                  workspace=workspace, greedy_eviction=bool(c.greedy_eviction))
+                  workspace=workspace, greedy_eviction=bool(c.greedy_eviction),
+                  attention_bias=self.bias)
 
     def append(self):
         import grouped_query_kv_amd as gqa

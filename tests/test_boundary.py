@@ -145,6 +145,20 @@ def test_greedy_eviction_needs_a_window(g):
     assert _call(g, "decode", _shape(g, S=1, M=16), opts, lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
 
 
+def test_bias_validation(g):
+    sh = _shape(g, S=3, M=16)              # B = 2, H = 4
+    def opts(bb, bh, bt):
+        o = g.Options(0.0, -1, None, None, 0, 0, 0)
+        o.attention_bias, o.bias_batch, o.bias_heads, o.bias_total = FAKE, bb, bh, bt
+        return o
+    assert _call(g, "prefill", sh, opts(3, 1, 16), lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
+    assert _call(g, "prefill", sh, opts(1, 2, 16), lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
+    # past + new reaches 6 columns
+    assert _call(g, "prefill", sh, opts(2, 4, 5), lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
+    assert "bias_total" in g.lib.gqa_last_error().decode()
+    assert _call(g, "decode", _shape(g, S=1, M=16), opts(1, 1, 3), lens=(3, 2)) == g.GQA_ERR_INVALID_ARG
+
+
 def test_workspace_too_small(g):
     need = g.lib.gqa_workspace_bytes(ctypes.byref(_shape(g, S=1, D=128, dtype=1)), None)
     assert need > 0

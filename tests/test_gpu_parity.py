@@ -240,6 +240,48 @@ def test_greedy_eviction_rolling(spec):
 
 
 # --------------------------------------------------------------------------
+# additive attention bias: column = the key's position in past ++ new
+# --------------------------------------------------------------------------
+
+BIAS = [
+    # dtype, B, S, H, Hkv, D, M, lens, window, rotary, bias (batch, heads), extra columns, greedy
+    ("fp16", 4, 1, 32, 8, 128, 1024, [0, 100, 700, 1023], -1, False, "BH", 5, 0),    # fast decode
+    ("bf16", 2, 1, 16, 4, 128, 512, [512, 300], 512, False, "1H", 0, 0),             # fused eviction
+    ("bf16", 2, 1, 8, 2, 128, 300, [300, 17], 64, True, "B1", 3, 0),                 # eviction kernel
+    ("fp16", 2, 1, 8, 2, 128, 256, [256, 50], 100, False, "BH", 0, 1),               # greedy: drop 157
+    ("fp32", 2, 1, 4, 2, 8, 40, [40, 3], 40, False, "BH", 0, 0),                     # generic decode
+    ("fp16", 2, 33, 8, 2, 128, 200, [0, 100], -1, True, "BH", 2, 0),                 # prefill (generic)
+    ("bf16", 2, 20, 8, 2, 128, 128, [128, 120], 128, False, "11", 0, 0),             # chunk, staging
+]
+
+
+def _attach_bias(case, kind, extra, rng):
+    B, H, S = case.batch, case.num_heads, case.new_tokens
+    Bb = B if kind[0] == "B" else 1
+    Hb = H if kind[1] == "H" else 1
+    T = int((np.asarray(case.seqlens_k) + S).max()) + extra
+    case.attention_bias = gi.to_bits(rng.standard_normal((Bb, Hb, S, T)), case.dtype)
+    return case
+
+
+@pytest.mark.parametrize("spec", BIAS, ids=[f"{s[0]}-{s[10]}-{i}" for i, s in enumerate(BIAS)])
+def test_attention_bias(spec):
+    dt, B, S, H, Hkv, D, M, lens, W, rot, kind, extra, greedy = spec
+    seed = sum(map(ord, repr(spec))) % 1000
+    case = gi.make_case("bias", dt, B, S, H, Hkv, D, M, lens, seed, window=W, rotary=rot,
+                        rotary_rows=(M + S if rot else None))
+    case.greedy_eviction = greedy
+    _attach_bias(case, kind, extra, np.random.default_rng(seed))
+    check_full(case, "decode" if S == 1 else "prefill", f"bias {spec}")
+
+
+def test_attention_bias_decode_full_size():
+    case = gi.workload("split-kv-decode-fp16")
+    _attach_bias(case, "BH", 1, np.random.default_rng(77))
+    check_full(case, "decode", "split-KV decode with a [B, H, 1, T] bias")
+
+
+# --------------------------------------------------------------------------
 # the halves: append and eviction on their own
 # --------------------------------------------------------------------------
 

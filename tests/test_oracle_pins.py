@@ -549,6 +549,98 @@ def test_greedy_eviction_matches_default_outputs_and_moves_less():
     assert O.validate(bad, "prefill") == O.INVALID
 
 
+# --------------------------------------------------------------------------
+# additive attention bias ([P1] sliding-window follow-up gives its shape)
+# --------------------------------------------------------------------------
+
+def _with_bias(case, shape_bh=None, T=None, values=None, rng=None):
+    B, H, S = case.batch, case.num_heads, case.new_tokens
+    Bb, Hb = shape_bh or (B, H)
+    T = T or int((np.asarray(case.seqlens_k) + S).max())
+    if values is None:
+        values = (rng or np.random.default_rng(5)).standard_normal((Bb, Hb, S, T))
+    c = case.copy()
+    c.attention_bias = gi.to_bits(values, case.dtype)
+    return c
+
+
+@pytest.mark.parametrize("kw,bh", [
+    (dict(dtype="fp32"), None),
+    (dict(dtype="fp16", H=6, Hkv=2, lens=(7, 0)), (1, 6)),
+    (dict(dtype="bf16", S=1, M=8, lens=(8, 3), window=8), (2, 1)),     # decode with eviction
+    (dict(dtype="fp32", S=3, M=8, lens=(8, 6), window=5), (1, 1)),     # chunk with eviction
+])
+def test_bias_brute_force_matches_oracle(kw, bh):
+    base = tiny(**kw)
+    case = _with_bias(base, bh, T=int((np.asarray(base.seqlens_k) + base.new_tokens).max()) + 2)
+    st, out, kc, vc, _ = O.gqa_attention(case, "decode" if case.new_tokens == 1 else "prefill")
+    assert st == O.OK
+    bout, bk, bv = brute.brute_attention(case)
+    np.testing.assert_allclose(out, np.asarray(bout), rtol=0, atol=1e-12)
+
+
+def test_bias_zero_and_row_constants_change_nothing():
+    case = tiny("fp32", S=4, lens=(3, 9), window=6, rotary=True)
+    st0, ref, *_ = O.gqa_attention(case)
+    T = 13
+    zero = _with_bias(case, T=T, values=np.zeros((2, 4, 4, T)))
+    np.testing.assert_array_equal(O.gqa_attention(zero)[1], ref)
+    # softmax is shift invariant: a constant per (b, h, query) row cancels
+    row = np.broadcast_to(np.arange(2 * 4 * 4, dtype=float).reshape(2, 4, 4, 1) - 7.0, (2, 4, 4, T))
+    np.testing.assert_allclose(O.gqa_attention(_with_bias(case, T=T, values=row))[1], ref,
+                               rtol=0, atol=1e-12)
+
+
+def test_bias_of_minus_infinity_outside_a_window_is_that_window():
+    """-inf on every column below p - W' + 1 equals the window-W' op: the
+    bias columns are the keys' positions in past ++ new."""
+    case = tiny("fp32", S=5, H=4, Hkv=2, lens=(2, 7), M=16)
+    Wp = 3
+    T = 12
+    _, wanted, *_ = O.gqa_attention(_win(case, Wp))
+    # the past lengths differ per sequence: one bias row block per sequence
+    vals = np.zeros((2, 1, 5, T))
+    for b, L in enumerate(case.seqlens_k):
+        for i in range(5):
+            vals[b, 0, i, :max(0, L + i - Wp + 1)] = -np.inf
+    got = O.gqa_attention(_with_bias(case, (2, 1), T=T, values=vals))[1]
+    np.testing.assert_allclose(got, wanted, rtol=0, atol=1e-13)
+
+
+def _win(case, W):
+    c = case.copy()
+    c.local_window_size = W
+    return c
+
+
+def test_bias_column_is_the_position_before_eviction():
+    """A full window cache takes one token (the oldest row is dropped); a
+    large bias on the column of one kept key makes the output that key's V
+    row (the weights of the others are below e^-60)."""
+    case = tiny("fp32", B=1, S=1, H=2, Hkv=1, D=4, M=6, lens=(6,), window=6, seed=3)
+    T = 7
+    target = 4                     # position 4 of past ++ new = buffer row 3 after the drop
+    vals = np.zeros((1, 1, 1, T))
+    vals[0, 0, 0, target] = 80.0
+    st, out, kc, vc, lens = O.gqa_attention(_with_bias(case, (1, 1), T=T, values=vals), "decode")
+    assert st == O.OK and lens.tolist() == [6]
+    want_v = O.to_f64(case.v_cache[0, 0, target], "fp32")
+    np.testing.assert_allclose(out[0, 0, :4], want_v, rtol=0, atol=1e-20)
+    np.testing.assert_array_equal(O.to_f64(vc[0, 0, target - 1], "fp32"), want_v)
+
+
+def test_bias_broadcast_equals_expanded_and_bad_shapes_are_rejected():
+    case = tiny("bf16", S=2, H=4, Hkv=2, lens=(4, 1))
+    rng = np.random.default_rng(8)
+    one = rng.standard_normal((1, 1, 2, 7))
+    a = O.gqa_attention(_with_bias(case, (1, 1), T=7, values=one))[1]
+    b = O.gqa_attention(_with_bias(case, (2, 4), T=7, values=np.broadcast_to(one, (2, 4, 2, 7))))[1]
+    np.testing.assert_array_equal(a, b)
+    assert O.validate(_with_bias(case, (3, 1), T=7), "prefill") == O.INVALID
+    assert O.validate(_with_bias(case, (1, 2), T=7), "prefill") == O.INVALID
+    assert O.validate(_with_bias(case, (1, 1), T=5), "prefill") == O.INVALID   # L + S = 6 > 5
+
+
 def test_prefill_then_decodes_equals_one_shot_prefill():
     n, k = 7, 4
     full = tiny("fp32", B=1, S=n + k, H=4, Hkv=2, D=8, M=16, lens=(0,), seed=12, rotary=True)
