@@ -236,6 +236,16 @@ def decode_call(gqa):
     return call
 
 
+def biased_call(gqa):
+    """Either entry with the set's additive bias (`s.bias`)."""
+    def call(s):
+        c = s.case
+        gqa.gqa_attention_prefill(s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.lens_host, s.lens_dev,
+                                  s.out, scale=c.scale, local_window_size=c.local_window_size,
+                                  cos_cache=s.cos, sin_cache=s.sin, attention_bias=s.bias)
+    return call
+
+
 def prefill_call(gqa):
     def call(s):
         c = s.case
@@ -308,7 +318,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="decode,prefill,continuation,window,chunks,present,greedy",
+    ap.add_argument("--only", default="decode,prefill,continuation,window,chunks,present,greedy,bias",
                     help="workloads to run, comma-separated; the split-KV decode (the headline) "
                          "always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -337,7 +347,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     which = set(args.only.split(","))
-    unknown = which - {"decode", "prefill", "continuation", "window", "chunks", "present", "greedy"}
+    unknown = which - {"decode", "prefill", "continuation", "window", "chunks", "present", "greedy",
+                       "bias"}
     if unknown:
         sys.exit(f"--only: unknown workloads {sorted(unknown)}")
     result = {}
@@ -453,6 +464,38 @@ def main():
             "amortized_ms_per_step": amort, "attention_bytes": att,
             "attention_gbs_when_fits": att / (st1["mean_ms"] * 1e-3) / 1e9,
             "fits_wall_ms": w1, "overflow_wall_ms": w2}
+
+    if "bias" in which:
+        # additive bias [B, H, S, T], T = the longest past + new: the
+        # split-KV decode keeps its kernel; S > 1 runs the plain kernel
+        def add_bias(T):
+            def prep(x):
+                c = x.case
+                x.bias = torch.randn((c.batch, c.num_heads, c.new_tokens, T), device="cuda",
+                                     dtype=torch.float32).to(x.q.dtype)
+            return prep
+        bd = gi.workload("split-kv-decode-fp16")
+        T = int(bd.seqlens_k.max()) + 1
+        w, st = run_leg(torch, "decode with bias", bd, biased_call(gqa), args.steps, args.warmup,
+                        add_bias(T))
+        bias_read = sum(int(L) + 1 for L in bd.seqlens_k) * bd.num_heads * 2
+        byts = decode_bytes(bd, [int(x) for x in bd.seqlens_k]) + bias_read
+        extra["decode_with_bias"] = {
+            "workload": "fp16 split-KV decode as the headline plus a [16, 32, 1, T] fp16 bias",
+            "gbs": byts / (st["mean_ms"] * 1e-3) / 1e9, "bytes_per_call": byts,
+            "frac_hbm_peak": byts / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_per_call_wall": w, **st}
+        bc = gi.workload("ragged-continuation-fp16")
+        T = int(bc.seqlens_k.max()) + bc.new_tokens
+        w, st = run_leg(torch, "continuation with bias (plain kernel)", bc, biased_call(gqa), 5, 1,
+                        add_bias(T))
+        fl = prefill_flops(bc)
+        extra["continuation_with_bias"] = {
+            "workload": "fp16 ragged continuation B=8 H=28 Hkv=4 S=128 plus a [8, 28, 128, T] bias "
+                        "(plain kernel)",
+            "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
+            "frac_mfma_peak": fl / (st["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+            "ms_per_call_wall": w, **st}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -156,8 +156,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Attention over one call's rows on the buffers the Problem names (the new
 // rows already appended there).
 hipError_t attend(const Problem& P, void* ws, const WorkspaceLayout& lay, hipStream_t hs) {
-  return prefill_fast_supported(P) && !P.bias ? launch_prefill_fast(P, ws, lay, hs)
-                                             : launch_attention_simple(P, hs);
+  return prefill_fast_supported(P) ? launch_prefill_fast(P, ws, lay, hs)
+                                   : launch_attention_simple(P, hs);
 }
 
 // S > 1 with a window where some sequence must evict. Queries early in the

@@ -112,6 +112,10 @@ struct PrefillArgs {
   int* counters;      // splitting: per row block, finished ranges (kept zero)
   int plan_n;         // > 0: workgroup w takes plan[w] = row block | range << 16 | ranges << 24
   uint32_t plan[kPrefillPlanMax];
+  const uint16_t* bias;   // additive bias: (b, h, i, column) at b bias_bs + h bias_hs + i bias_T + column
+  int64_t bias_bs, bias_hs;
+  int bias_T;             // a multiple of 4 (four columns per 8-byte load)
+  float bias_mul;         // log2(e) / scale_log2 = 1 / |scale|: a bias in units of the raw scores
   int hl_ok;          // past lengths below are valid (B <= kPrefillArgBatch)
   int hl[kPrefillArgBatch];   // past lengths from the host (the same values as lens)
 };
@@ -268,9 +272,29 @@ struct RowState {
   float l;       // this lane's share of the sum of the packed weights
 };
 
-template <class T, bool kMask>
+// The lane's bias values of one tile: columns tb + 4 c + 32 h + 8 j + e in
+// member 4 h + j (four halves each), matching the lane's scores.
+struct BiasTile {
+  uint2 v[8];
+};
+
+template <class T, bool kMask, bool kBias>
 __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4], uint4 (&pk)[4],
-                                    float cs, int lim_hi, int span) {
+                                    float cs, int lim_hi, int span, const BiasTile& bt,
+                                    float bias_mul) {
+  if (kBias) {
+    // the bias joins the raw score scaled by 1 / |scale|, so that the
+    // exponent cs * s becomes scale * q.k + bias (in log2 units)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint2 w = bt.v[4 * h + (v >> 2)];
+        const uint32_t x = (v & 2) ? w.y : w.x;
+        const float bv = T::to_float(typename T::bits((x >> (16 * (v & 1))) & 0xFFFFu));
+        s[h][v] = fmaf(bv, bias_mul, s[h][v]);
+      }
+  }
   if (kMask) {
     // key offset within the lane's keys: 32 h + 8 (v / 4) + v % 4; visible iff
     // 0 <= lim_hi - offset <= span (causal limit and window start together)
@@ -409,21 +433,36 @@ __device__ inline void products(int t, int wt0, int wt1, const unsigned char* kt
 #endif
 }
 
-template <class T>
+template <class T, bool kBias>
 __device__ inline void softmax_step(int t, int wt0, int wt1, f32x16 (&sc)[2], RowState& rs,
                                     f32x16 (&o)[4], uint4 (&pk)[4], float cs, int my_p, int span,
-                                    int w_full_lo, int w_full_hi, int c) {
+                                    int w_full_lo, int w_full_hi, int c, const BiasTile& bt,
+                                    float bias_mul) {
   if (t < wt0 || t >= wt1) return;
   const int tb = t * kBK;
   const bool full = tb + kBK - 1 <= w_full_hi && tb >= w_full_lo;
   const int lim_hi = my_p - (tb + 4 * c);
   if (full)
-    softmax_tile<T, false>(sc, rs, o, pk, cs, lim_hi, span);
+    softmax_tile<T, false, kBias>(sc, rs, o, pk, cs, lim_hi, span, bt, bias_mul);
   else
-    softmax_tile<T, true>(sc, rs, o, pk, cs, lim_hi, span);
+    softmax_tile<T, true, kBias>(sc, rs, o, pk, cs, lim_hi, span, bt, bias_mul);
 }
 
-template <class T>
+// The bias values of tile t for the lane's row. Columns are clamped to the
+// last aligned group below bias_T: past the causal limit the scores are
+// masked whatever the value, and below it every column is < L + S <= T.
+__device__ inline void bias_load(BiasTile& bt, const uint16_t* brow, int t, int c, int T) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int col = t * kBK + 4 * c + 32 * h + 8 * j;
+      col = col <= T - 4 ? col : T - 4;
+      bt.v[4 * h + j] = *reinterpret_cast<const uint2*>(brow + col);
+    }
+}
+
+template <class T, bool kBias>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   // four separately declared tiles, each used at fixed places of the
   // two-iteration loop body: the compiler can then tell the tiles being read
@@ -563,19 +602,33 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     if (t + 1 < t_end) tile_load<false>(kc, kvalid, kn, (t + 1) * kBK, lo, wave);
     if (t < t_end) tile_load<true>(vc, kvalid, vn, t * kBK, lo, wave);
   };
+  // bias of tile t for this lane's row: group 0 issues it before the step's
+  // tile loads and uses it after the products (its wait then does not take
+  // in the tile loads issued later); group 1 issues it before its products
+  // and uses it in the next step, after that step's full wait
+  BiasTile bt;
+  const uint16_t* brow = nullptr;
+  if (kBias) brow = a.bias + b * a.bias_bs + int64_t(my_h) * a.bias_hs + int64_t(my_i) * a.bias_T;
+  auto bias_tile = [&](int t) {
+    if (kBias && t >= wt0 && t < wt1) bias_load(bt, brow, t, c, a.bias_T);
+  };
   auto step0 = [&](int t, const unsigned char* kt, const unsigned char* vt, unsigned char* kn,
                    unsigned char* vn) {
+    bias_tile(t);
     loads(t, kn, vn);
     products<T>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
     phase_barrier();
-    softmax_step<T>(t, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c);
+    softmax_step<T, kBias>(t, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c, bt,
+                           a.bias_mul);
     tiles_landed_barrier();
   };
   auto step1 = [&](int t, const unsigned char* kt, const unsigned char* vt, unsigned char* kn,
                    unsigned char* vn) {
     loads(t, kn, vn);
-    softmax_step<T>(t - 1, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c);
+    softmax_step<T, kBias>(t - 1, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c,
+                           bt, a.bias_mul);
     phase_barrier();
+    bias_tile(t);
     products<T>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
     tiles_landed_barrier();
   };
@@ -674,8 +727,10 @@ bool prefill_fast_supported(const Problem& p) {
   // buffer ranges are 32-bit byte counts; cos/sin rows are read as float4
   const bool rot_aligned = !p.rot || ((reinterpret_cast<uintptr_t>(p.cos) |
                                        reinterpret_cast<uintptr_t>(p.sin)) & 15) == 0;
+  // a bias is read four columns per 8-byte load
+  const bool bias_ok = !p.bias || (p.bias_T % 4 == 0 && (reinterpret_cast<uintptr_t>(p.bias) & 7) == 0);
   return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.M <= (1 << 23) &&
-         rot_aligned;
+         rot_aligned && bias_ok;
 }
 
 namespace {
@@ -707,6 +762,9 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
   a.n_rb = ceil_div(p.S * p.G, kWgRows);
   a.scale_log2 = fabsf(p.scale) * kLog2e;
   a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
+  a.bias = static_cast<const uint16_t*>(p.bias);
+  a.bias_bs = p.bias_bs; a.bias_hs = p.bias_hs; a.bias_T = p.bias_T;
+  a.bias_mul = kLog2e / a.scale_log2;
   a.hl_ok = p.lens_host != nullptr && p.B <= kPrefillArgBatch;
   if (a.hl_ok)
     for (int b = 0; b < p.B; ++b) a.hl[b] = p.lens_host[b];
@@ -758,10 +816,15 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
     }
     blocks = a.plan_n;
   }
-  if (p.dtype == GQA_FP16)
-    hipLaunchKernelGGL(prefill_kernel<F16>, dim3(blocks), dim3(kThreads), 0, st, a);
+  const bool fp16 = p.dtype == GQA_FP16;
+  if (p.bias && fp16)
+    hipLaunchKernelGGL((prefill_kernel<F16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else if (p.bias)
+    hipLaunchKernelGGL((prefill_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else if (fp16)
+    hipLaunchKernelGGL((prefill_kernel<F16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<BF16>, dim3(blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

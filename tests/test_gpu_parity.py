@@ -252,6 +252,12 @@ BIAS = [
     ("fp32", 2, 1, 4, 2, 8, 40, [40, 3], 40, False, "BH", 0, 0),                     # generic decode
     ("fp16", 2, 33, 8, 2, 128, 200, [0, 100], -1, True, "BH", 2, 0),                 # prefill (generic)
     ("bf16", 2, 20, 8, 2, 128, 128, [128, 120], 128, False, "11", 0, 0),             # chunk, staging
+    # T % 4 == 0: the MFMA prefill kernel reads the bias (four columns per load)
+    ("fp16", 2, 33, 8, 2, 128, 200, [0, 100], -1, True, "BH", 3, 0),
+    ("bf16", 3, 40, 8, 2, 128, 2048, [0, 700, 1999], -1, True, "1H", 1, 0),       # key-split plan
+    ("bf16", 2, 33, 16, 2, 128, 200, [100, 0], 40, False, "B1", 3, 0),            # window
+    ("fp16", 2, 130, 28, 4, 128, 512, [380, 0], -1, False, "BH", 2, 0),           # several row blocks
+    ("bf16", 2, 20, 8, 2, 128, 128, [128, 120], 128, False, "11", 1, 0),          # staging, plain kernel
 ]
 
 
