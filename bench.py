@@ -47,11 +47,11 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "4366ce18d2a2f69ac34e5e098cc1ec4c3d291a5f4a3b01994d8e48e90cb5ee9c",
+                "1e44c534703b15317b6a8c102aa4f84f9c7884fa50b49c86d13c0ddaa6f35d5f",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "05bcc4acc7c013e31fb5f97f28e954e6313632b1cac4d940527820c775e848be"},
-    "fetch_kib": 74133.375, "write_kib": 1050.28125,
-    "fetch_scale": 524288.0 / 262156.9625, "write_scale": 1.0,
+                "7be24418e1df66d2315e9b0ed0e85b8aea2ceedd0ac6fdee1b59cb8a3c29b4e1"},
+    "fetch_kib": 74142.423, "write_kib": 1050.286,
+    "fetch_scale": 524288.0 / 262156.8, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
@@ -466,8 +466,8 @@ def main():
             "fits_wall_ms": w1, "overflow_wall_ms": w2}
 
     if "bias" in which:
-        # additive bias [B, H, S, T], T = the longest past + new: the
-        # split-KV decode keeps its kernel; S > 1 runs the plain kernel
+        # additive bias [B, H, S, T], T >= the longest past + new: both the
+        # split-KV decode and the prefill kernel read it in their tile loops
         def add_bias(T):
             def prep(x):
                 c = x.case
@@ -486,13 +486,13 @@ def main():
             "frac_hbm_peak": byts / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "ms_per_call_wall": w, **st}
         bc = gi.workload("ragged-continuation-fp16")
-        T = int(bc.seqlens_k.max()) + bc.new_tokens
-        w, st = run_leg(torch, "continuation with bias (plain kernel)", bc, biased_call(gqa), 5, 1,
-                        add_bias(T))
+        T = -(-(int(bc.seqlens_k.max()) + bc.new_tokens) // 4) * 4   # a multiple of 4: MFMA kernel
+        w, st = run_leg(torch, "continuation with bias", bc, biased_call(gqa), args.steps,
+                        args.warmup, add_bias(T))
         fl = prefill_flops(bc)
         extra["continuation_with_bias"] = {
-            "workload": "fp16 ragged continuation B=8 H=28 Hkv=4 S=128 plus a [8, 28, 128, T] bias "
-                        "(plain kernel)",
+            "workload": "fp16 ragged continuation B=8 H=28 Hkv=4 S=128 plus a [8, 28, 128, T] fp16 "
+                        "bias, T a multiple of 4",
             "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
             "frac_mfma_peak": fl / (st["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
             "ms_per_call_wall": w, **st}
