@@ -179,12 +179,28 @@ gqa_status windowed_chunk(const Problem& P, int max_drop, void* ws, const Worksp
   const int row_bytes = P.D * elem_bytes(P.dtype);
   int max_len = 0;
   for (int b = 0; b < P.B; ++b) max_len = std::max(max_len, P.lens_host[b]);
+  // the MFMA kernel reads whole 64-key tiles of the past from the cache
+  // itself and only the tile holding L_b and the new rows from the frame;
+  // the plain kernel reads everything from the frame, from the tile the
+  // window reaches on
+  const bool direct = prefill_fast_supported(F);
   hipError_t e = launch_copy_prefix(P.k_cache, P.v_cache, P.M, F.k_cache, F.v_cache, F.M,
-                                    P.lens_dev, P.B, P.Hkv, row_bytes, P.window, max_len, hs);
+                                    P.lens_dev, P.B, P.Hkv, row_bytes, direct ? 1 : P.window,
+                                    max_len, hs);
   if (e != hipSuccess) return hip_fail(e, "staging copy");
   e = launch_append(F, false, hs);
   if (e != hipSuccess) return hip_fail(e, "staging append");
-  e = attend(F, ws, lay, hs);
+  if (direct) {
+    Problem A = F;
+    A.stage_k = F.k_cache;
+    A.stage_v = F.v_cache;
+    A.k_cache = P.k_cache;
+    A.v_cache = P.v_cache;
+    A.cache_rows = P.M;
+    e = launch_prefill_fast(A, ws, lay, hs);
+  } else {
+    e = attend(F, ws, lay, hs);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention");
   e = launch_evict(P, P.S, max_drop, ws, lay, hs);
   if (e != hipSuccess) return hip_fail(e, "eviction");

@@ -34,9 +34,16 @@ struct Problem {
   const int32_t* lens_host;
   // additive bias (bias == nullptr: none): element of (b, h, i, column) at
   // b * bias_bs + h * bias_hs + i * bias_T + column (strides 0 broadcast)
-  const void* bias;
-  int64_t bias_bs, bias_hs;
-  int bias_T;
+  const void* bias = nullptr;
+  int64_t bias_bs = 0, bias_hs = 0;
+  int bias_T = 0;
+  // windowed chunk on the MFMA prefill (stage_k != nullptr): M is the
+  // staging frame's row count (M + S of the cache); keys from each
+  // sequence's 64-aligned past length on are read from the frame, earlier
+  // ones from k_cache/v_cache, whose row count is cache_rows
+  const void* stage_k = nullptr;
+  const void* stage_v = nullptr;
+  int cache_rows = 0;
 };
 
 // Workspace carving (byte offsets from the workspace base). The layout is a

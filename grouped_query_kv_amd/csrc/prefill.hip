@@ -103,6 +103,13 @@ struct PrefillArgs {
   const float* cosv;
   const float* sinv;
   int B, S, H, Hkv, G, M, W;
+  // windowed chunk: keys from each sequence's 64-aligned past length on come
+  // from the staging frame (M rows per (b, kv head), row = key), earlier
+  // keys from the cache (kv_rows rows per (b, kv head)); without a frame
+  // everything comes from the cache and kv_rows = M
+  const uint16_t* k_stage;
+  const uint16_t* v_stage;
+  int kv_rows;
   int rot, rot_rows, interleaved;
   int n_rb;           // row blocks per (b, kv head)
   float scale_log2;   // |scale| * log2(e)
@@ -539,12 +546,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int wt0 = wave_has_rows ? max(w_kstart / kBK, t_begin) : t_end;
   const int wt1 = wave_has_rows ? min((w_kend + kBK - 1) / kBK, t_end) : t_end;
 
-  const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
+  const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.kv_rows * kD;
   const uint16_t* kc = a.k_cache + kvbase;
   const uint16_t* vc = a.v_cache + kvbase;
+  // tiles at or past `stage_from` come from the staging frame (same key rows)
+  const int stage_from = a.k_stage ? (L & ~(kBK - 1)) : INT_MAX;
+  const int64_t sbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
+  const uint16_t* k_frame = a.k_stage ? a.k_stage + sbase : kc;
+  const uint16_t* v_frame = a.k_stage ? a.v_stage + sbase : vc;
 
   const LoadOffsets lo = load_offsets(wave, lane);
-  tile_load<false>(kc, kvalid, k_even, t_begin * kBK, lo, wave);
+  tile_load<false>(t_begin * kBK < stage_from ? kc : k_frame, kvalid, k_even, t_begin * kBK, lo, wave);
 
   // ---- Q^T (B operand): lane holds Q[row][16 ks + 8 c + e] ----
   uint4 qv[8];
@@ -599,8 +611,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_barrier();
   };
   auto loads = [&](int t, unsigned char* kn, unsigned char* vn) {
-    if (t + 1 < t_end) tile_load<false>(kc, kvalid, kn, (t + 1) * kBK, lo, wave);
-    if (t < t_end) tile_load<true>(vc, kvalid, vn, t * kBK, lo, wave);
+    if (t + 1 < t_end)
+      tile_load<false>((t + 1) * kBK < stage_from ? kc : k_frame, kvalid, kn, (t + 1) * kBK, lo, wave);
+    if (t < t_end) tile_load<true>(t * kBK < stage_from ? vc : v_frame, kvalid, vn, t * kBK, lo, wave);
   };
   // bias of tile t for this lane's row: group 0 issues it before the step's
   // tile loads and uses it after the products (its wait then does not take
@@ -758,6 +771,9 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
   a.lens = p.lens_dev;
   a.cosv = p.cos; a.sinv = p.sin;
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window;
+  a.k_stage = static_cast<const uint16_t*>(p.stage_k);
+  a.v_stage = static_cast<const uint16_t*>(p.stage_v);
+  a.kv_rows = p.stage_k ? p.cache_rows : p.M;
   a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
   a.n_rb = ceil_div(p.S * p.G, kWgRows);
   a.scale_log2 = fabsf(p.scale) * kLog2e;
