@@ -49,9 +49,9 @@ DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
                 "1e44c534703b15317b6a8c102aa4f84f9c7884fa50b49c86d13c0ddaa6f35d5f",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "7be24418e1df66d2315e9b0ed0e85b8aea2ceedd0ac6fdee1b59cb8a3c29b4e1"},
-    "fetch_kib": 74142.423, "write_kib": 1050.286,
-    "fetch_scale": 524288.0 / 262156.8, "write_scale": 1.0,
+                "99ab9293511c96fd9c6ed6c19350b91f1b11766870f6c5957417cdc6bbd1ec4e"},
+    "fetch_kib": 74137.803, "write_kib": 1050.281,
+    "fetch_scale": 524288.0 / 262156.775, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
