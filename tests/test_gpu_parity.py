@@ -435,6 +435,54 @@ def test_ragged_continuation_full_size_sampled():
 
 
 # --------------------------------------------------------------------------
+# no shared state: two calls in flight on two streams, own workspaces
+# --------------------------------------------------------------------------
+
+def test_concurrent_streams_with_own_workspaces():
+    """The library keeps no state between calls: two decodes and two
+    prefills enqueued on two streams (default priority) at once, each with
+    its own workspace, give exactly the outputs and caches of the same calls
+    made one after the other."""
+    import torch
+    import grouped_query_kv_amd as gqa
+    cases = [gi.make_case("streams", "fp16", 4, 1, 32, 8, 128, 2048, [2047, 5, 900, 1500], 61),
+             gi.make_case("streams", "bf16", 3, 1, 16, 4, 128, 1024, [100, 1023, 512], 62),
+             gi.make_case("streams", "bf16", 2, 40, 8, 2, 128, 2048, [1900, 0], 63, rotary=True,
+                          rotary_rows=2100),
+             gi.make_case("streams", "fp16", 2, 70, 28, 4, 128, 512, [300, 17], 64)]
+    entries = ["decode", "decode", "prefill", "prefill"]
+
+    def ws_for(c):
+        n = gqa.gqa_workspace_bytes(c.batch, c.new_tokens, c.num_heads, c.kv_num_heads, c.head_size,
+                                    c.max_seq_len, gqa.GQA_FP16 if c.dtype == "fp16" else gqa.GQA_BF16)
+        return torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    # one after the other on the current stream
+    ref = []
+    for c, e in zip(cases, entries):
+        d = DevCase(c)
+        out = d.run(e, workspace=ws_for(c))
+        torch.cuda.synchronize()
+        ref.append((to_bits(out), *d.caches()))
+    # all four in flight, alternating between two streams
+    say("[gpu] four calls on two streams")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    devs = [DevCase(c) for c in cases]
+    wss = [ws_for(c) for c in cases]
+    torch.cuda.synchronize()
+    outs = []
+    for k, (d, e, w) in enumerate(zip(devs, entries, wss)):
+        with torch.cuda.stream(streams[k % 2]):
+            outs.append(d.run(e, workspace=w))
+    torch.cuda.synchronize()
+    for k, d in enumerate(devs):
+        gk, gv = d.caches()
+        assert_bits_equal(to_bits(outs[k]), ref[k][0], f"stream call {k} out")
+        assert_bits_equal(gk, ref[k][1], f"stream call {k} k_cache")
+        assert_bits_equal(gv, ref[k][2], f"stream call {k} v_cache")
+
+
+# --------------------------------------------------------------------------
 # prefill then decodes equals a one-shot prefill (the worked example's story)
 # --------------------------------------------------------------------------
 
