@@ -280,6 +280,26 @@ def run_leg(torch, name, case, call, steps, warmup, prepare=None):
     return w, stats(d, p_)
 
 
+def device_info(torch):
+    """The GPU as torch sees it, and its clocks as rocm-smi reports them right
+    after a timed leg (a child process with a time limit; None if unavailable)."""
+    import subprocess
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1), "clocks": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        if r.returncode == 0:
+            data = json.loads(r.stdout)
+            card = next(iter(data.values())) if isinstance(data, dict) and data else {}
+            info["clocks"] = {k: v for k, v in card.items() if "clk" in k.lower()} or card
+    except Exception as e:  # noqa: BLE001
+        info["clocks"] = f"unavailable: {type(e).__name__}"
+    return info
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
@@ -365,6 +385,7 @@ def main():
     value = dec_bytes / (wall * 1e-3) / 1e9
     del sets
     torch.cuda.empty_cache()
+    device = device_info(torch)
 
     extra = {}
     if "prefill" in which:
@@ -515,6 +536,7 @@ def main():
                      "kernel": "decode call (all launches of gqa_attention_decode)",
                      "bytes_per_call": dec_bytes, **st_dec},
         "cpu_baseline": cpu,
+        "device": device,
         **extra,
     }
     print(json.dumps(line), flush=True)
