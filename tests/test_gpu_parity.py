@@ -511,6 +511,44 @@ def test_prefill_then_decodes_match_one_shot(dt, D):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("dt,D,lens", [("fp16", 128, [0, 0]), ("bf16", 128, [0, 0]),
+                                       ("fp32", 8, [0, 0])])
+def test_prefill_then_chunks_match_one_shot(dt, D, lens):
+    """A prefill of n tokens followed by continuation chunks of 37 and 90
+    tokens gives, for each chunk, the same rows as a one-shot prefill of all
+    of them (chunked continuation, as in the ragged continuation workload)."""
+    import torch
+    n, chunks = 200, [37, 90]
+    tot = n + sum(chunks)
+    full = gi.make_case("inc-chunks", dt, 2, tot, 28, 4, D, 512, lens, 78, rotary=True,
+                        rotary_rows=512)
+    st, ref, kc_ref, vc_ref, _ = O.gqa_attention(full)
+    assert st == O.OK
+    part = full.copy()
+    part.new_tokens = n
+    part.q, part.k_new, part.v_new = full.q[:, :n], full.k_new[:, :n], full.v_new[:, :n]
+    say(f"[gpu] incremental {dt}: prefill {n} then chunks {chunks}")
+    dev = DevCase(part)
+    out = dev.run("prefill")
+    assert_close(out_f64(out, dt), ref[:, :n], dt, "prefill part")
+    start = n
+    for c in chunks:
+        step = full.copy()
+        step.new_tokens = c
+        step.q, step.k_new, step.v_new = (x[:, start:start + c].copy()
+                                          for x in (full.q, full.k_new, full.v_new))
+        dev.case = step
+        dev.q, dev.k_new, dev.v_new = (to_dev(getattr(step, a), dt) for a in ("q", "k_new", "v_new"))
+        dev.set_lengths([start, start])
+        out = dev.run("prefill")
+        assert_close(out_f64(out, dt), ref[:, start:start + c], dt, f"chunk at {start}")
+        start += c
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc_ref, "chunked k_cache")
+    assert_bits_equal(gv, vc_ref, "chunked v_cache")
+    torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------
 # split prefill: the workspace counters return to zero, repeated calls agree
 # --------------------------------------------------------------------------

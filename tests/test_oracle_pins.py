@@ -659,6 +659,28 @@ def test_prefill_then_decodes_equals_one_shot_prefill():
         np.testing.assert_allclose(out[:, 0], ref[:, n + s], rtol=0, atol=1e-13)
 
 
+def test_prefill_then_chunks_equals_one_shot_prefill():
+    n, chunks = 5, [3, 4]
+    tot = n + sum(chunks)
+    full = tiny("fp32", B=2, S=tot, H=4, Hkv=2, D=8, M=16, lens=(0, 0), seed=13, rotary=True)
+    _, ref, kc_ref, vc_ref, _ = O.gqa_attention(full)
+    part = full.copy()
+    part.new_tokens = n
+    part.q, part.k_new, part.v_new = full.q[:, :n], full.k_new[:, :n], full.v_new[:, :n]
+    _, out, kc, vc, lens = O.gqa_attention(part)
+    np.testing.assert_allclose(out, ref[:, :n], rtol=0, atol=1e-13)
+    start = n
+    for c in chunks:
+        step = full.copy()
+        step.new_tokens = c
+        step.q, step.k_new, step.v_new = (x[:, start:start + c] for x in (full.q, full.k_new, full.v_new))
+        step.k_cache, step.v_cache, step.seqlens_k = kc, vc, lens.astype(np.int32)
+        _, out, kc, vc, lens = O.gqa_attention(step)
+        np.testing.assert_allclose(out, ref[:, start:start + c], rtol=0, atol=1e-13)
+        start += c
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+
+
 # --------------------------------------------------------------------------
 # the worked example's shapes (rocMLIR "KV Cache")
 # --------------------------------------------------------------------------
