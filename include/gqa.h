@@ -52,7 +52,9 @@
  *      gives its shape) takes bias[b, h, i, j + d_b] for the key at row j
  *      after an eviction of d_b rows, i.e. its column is the key's position
  *      in past ++ new. With a bias the split-KV decode (S = 1, fp16/bf16,
- *      D = 128) keeps its fast kernel; other calls use the plain kernel.
+ *      D = 128) and the MFMA prefill (fp16/bf16, D = 128, bias_total a
+ *      multiple of 4, bias 8-byte aligned) keep their kernels; other calls
+ *      use the plain kernel.
  *
  * Ownership and threading: every pointer except *_host arguments is device
  * memory owned by the caller. The library never allocates, frees or
@@ -161,10 +163,12 @@ gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts,
  * partials (kept in the workspace) the last one merges by log-sum-exp.
  * With a window, S > 1 and an eviction needed by some sequence, queries
  * early in the chunk see keys the eviction drops: attention then runs over
- * each sequence before its eviction (past ++ new, positions L_b + i), in
- * staging frames in the workspace that hold the past rows the window
- * reaches and the new rows, and the cache then takes the eviction (keep the
- * min(L_b + S, M) most recent tokens at rows 0..) and the append. Source:
+ * each sequence before its eviction (past ++ new, positions L_b + i): the
+ * new rows, and the past rows from the 64-key tile holding L_b on, go to
+ * staging frames in the workspace, from which the MFMA kernel reads those
+ * tiles while it reads earlier tiles from the cache (the plain kernel
+ * reads every row the window reaches from the frames); the cache then
+ * takes the eviction and the append. Source:
  * all three pages as summarised above; the key-tile loop ends at each
  * sequence's length ("KV Cache", notes and short-term plan); the window
  * keeps the most recent tokens contiguously (sliding-window follow-up of
@@ -179,11 +183,14 @@ gqa_status gqa_attention_prefill(const gqa_shape* shape, const gqa_options* opts
 
 /*
  * The whole op for exactly one new token per sequence (S must be 1):
- * split-KV attention in which each workgroup streams one slice of a
- * sequence's valid keys once and the last workgroup of the sequence merges
- * the slices by log-sum-exp. With a window and L_b = M it evicts one row
- * first instead of failing. Source: as for prefill; decoding phase of the
- * "KV Cache" worked example.
+ * split-KV attention (fp16/bf16, D = 128, B <= 64; the plain kernel
+ * otherwise). The valid 16-key blocks of all (sequence, kv head) units form
+ * one list cut into equal slices, one per wave; each wave streams its slice
+ * once, with the new token's append fused, and a unit cut between
+ * workgroups is merged by log-sum-exp by the last of them to finish. With a
+ * window and L_b = M it evicts instead of failing (one row, or with
+ * greedy_eviction down to W - 1 rows). Source: as for prefill; decoding
+ * phase of the "KV Cache" worked example.
  */
 gqa_status gqa_attention_decode(const gqa_shape* shape, const gqa_options* opts,
                                 const void* q, const void* k_new, const void* v_new,
