@@ -437,14 +437,22 @@ struct UnitInfo {
   int unit, h0, nheads, w_first, w_last;
 };
 
-__device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub) {
+// Per-sequence plan values the end phase needs, copied to LDS when the
+// kernel starts (reading them from the argument block at a runtime index
+// there costs a memory round trip per unit).
+struct SeqTable {
+  int nb[kDecodeArgBatch];   // blocks per unit
+  int pb[kDecodeArgBatch];   // first global block
+};
+
+__device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub, const SeqTable& st) {
   UnitInfo u;
   const int g = ub / a.n_hg, hg = ub % a.n_hg;
   u.h0 = g * a.G + hg * a.hg_size;
   u.nheads = min(a.hg_size, a.G - hg * a.hg_size);
   u.unit = b * a.Hkv * a.n_hg + ub;
-  const int nb = seq_of(a, b).nb;
-  const int64_t x0 = a.pb[b] + int64_t(ub) * nb;
+  const int nb = __builtin_amdgcn_readfirstlane(st.nb[b]);
+  const int64_t x0 = __builtin_amdgcn_readfirstlane(st.pb[b]) + int64_t(ub) * nb;
   u.w_first = owner_worker(a, x0);
   u.w_last = owner_worker(a, x0 + nb - 1);
   return u;
@@ -533,9 +541,10 @@ __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, 
 // unit) by log-sum-exp, write the output and reset the unit's counter. All
 // threads of the workgroup; `lds` holds 2 kMergeMax x 16 floats.
 template <class T>
-__device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds) {
+__device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds,
+                                  const SeqTable& st) {
   const int tid = threadIdx.x;
-  const UnitInfo u = unit_info(a, b, ub);
+  const UnitInfo u = unit_info(a, b, ub, st);
   const int wg_first = u.w_first / kDecodeWaves, wg_last = u.w_last / kDecodeWaves;
   const int count = wg_last - wg_first + 1;
   const float* base = a.partials + int64_t(wg_first + u.unit) * kSlotFloats;
@@ -616,6 +625,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
   __shared__ int sh_tab[kDecodeWaves][2][2];        // per wave, slot: (b, ub) or b = -1
   __shared__ int sh_flag[2];
+  __shared__ SeqTable sh_seq;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -626,6 +636,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   float* slot1 = reinterpret_cast<float*>(lds + wv * kWaveLds + kSlotBytes);
   unsigned char* vt = lds + wv * kWaveLds + kSlotBytes;     // the V tile while streaming
   if (lane < 4) sh_tab[wv][lane >> 1][lane & 1] = -1;
+  if (tid < a.B) {   // read by the end phase, after the barrier that follows the streaming
+    sh_seq.nb[tid] = seq_of(a, tid).nb;
+    sh_seq.pb[tid] = a.pb[tid];
+  }
 
   int64_t S = 0, E = 0;
   if (worker < a.workers) {
@@ -711,7 +725,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     const int b = tb[e], ub = tu[e];
     if (b < 0 || (b == prev_b && ub == prev_ub)) continue;   // empty, or not a unit's first entry
     prev_b = b; prev_ub = ub;
-    const UnitInfo u = unit_info(a, b, ub);
+    const UnitInfo u = unit_info(a, b, ub, sh_seq);
     const bool inside = u.w_first >= wg * kDecodeWaves && u.w_last < (wg + 1) * kDecodeWaves;
     float* gslot = a.partials + int64_t(wg + u.unit) * kSlotFloats;
     for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
@@ -770,8 +784,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
-  if (sh_flag[0]) merge_unit<T>(a, gb0, gub0, mlds);
-  if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds);
+  if (sh_flag[0]) merge_unit<T>(a, gb0, gub0, mlds, sh_seq);
+  if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds, sh_seq);
 }
 
 // Fused eviction, before the decode kernel: for the last block i of every
