@@ -113,9 +113,30 @@ struct Seq {
   int d;                                // rows dropped by the fused eviction (0 or 1)
 };
 
-__device__ inline Seq seq_of(const DecodeArgs& a, int b) {
+// The per-sequence plan values in registers: lane j holds sequence j's past
+// length and first global block (B <= 64, one lane each), loaded once per
+// wave with two vector loads; an entry is then one scalar lane read.
+// Reading the argument block at a runtime index instead costs a memory
+// round trip each time (about 0.8 us), at the start of a wave's slice, at
+// every unit it enters and in the end phase.
+struct SeqRegs {
+  int hl, pb, pb1;          // L_j, pb[j], pb[j + 1]
+};
+
+__device__ inline SeqRegs load_seq_regs(const DecodeArgs& a, int lane) {
+  const int j = lane < a.B ? lane : 0;          // every lane reads in bounds (B >= 1)
+  SeqRegs r;
+  r.hl = a.hl[j];
+  r.pb = a.pb[j];
+  r.pb1 = a.pb[j + 1];                          // pb holds B + 1 entries
+  return r;
+}
+
+__device__ inline int lane_of(int v, int b) { return __builtin_amdgcn_readlane(v, b); }
+
+__device__ inline Seq seq_of(const DecodeArgs& a, int b, const SeqRegs& sr) {
   Seq s;
-  s.L = clamp_len(a.hl[b], 0, a.M);
+  s.L = clamp_len(lane_of(sr.hl, b), 0, a.M);
   s.Lp = kept_rows(s.L, 1, a.M, a.cap);     // row of the new token (after any eviction)
   s.kend = s.Lp + 1;
   s.kstart = a.W > 0 ? (s.kend - a.W > 0 ? s.kend - a.W : 0) : 0;
@@ -132,10 +153,11 @@ struct Blk {
   int b, g, ub, i, nb;
   int d;                   // fused eviction: key r is read from buffer row r + d
   int coff;                // bias column of key r: r + coff (its position before any eviction)
+  int L;                   // past length (the new token's rotary position)
 };
 
-__device__ inline void set_unit(Blk& k, const DecodeArgs& a) {
-  const Seq s = seq_of(a, k.b);
+__device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) {
+  const Seq s = seq_of(a, k.b, sr);
   k.g = k.ub / a.n_hg;
   const int64_t base = (int64_t(k.b) * a.Hkv + k.g) * a.M * kD;
   k.kc = a.k_cache + base;
@@ -146,15 +168,16 @@ __device__ inline void set_unit(Blk& k, const DecodeArgs& a) {
   k.kb = s.kstart + kKeys * k.i;
   k.d = s.d;
   k.coff = s.L - s.Lp;
+  k.L = s.L;
 }
 
-__device__ inline Blk locate(const DecodeArgs& a, int64_t x) {
+__device__ inline Blk locate(const DecodeArgs& a, int64_t x, const SeqRegs& sr, int lane) {
   Blk k;
-  k.b = 0;
-  for (int b = 0; b < a.B; ++b)
-    if (x >= a.pb[b] && x < a.pb[b + 1]) k.b = b;
-  const int nb = seq_of(a, k.b).nb;
-  const int off = int(x - a.pb[k.b]);
+  // the lane whose sequence holds block x (none past the end: sequence 0)
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.B && x >= sr.pb && x < sr.pb1);
+  k.b = hit ? int(__builtin_ctzll(hit)) : 0;
+  const int nb = seq_of(a, k.b, sr).nb;
+  const int off = int(x - lane_of(sr.pb, k.b));
   // callers pass x < total; the clamps keep every derived address inside the
   // caches even if one did not
   const int units = a.Hkv * a.n_hg;
@@ -162,11 +185,11 @@ __device__ inline Blk locate(const DecodeArgs& a, int64_t x) {
   k.ub = k.ub < units ? (k.ub > 0 ? k.ub : 0) : units - 1;
   k.i = off - k.ub * nb;
   k.i = k.i < nb ? (k.i > 0 ? k.i : 0) : (nb > 0 ? nb - 1 : 0);
-  set_unit(k, a);
+  set_unit(k, a, sr);
   return k;
 }
 
-__device__ inline Blk next_block(const DecodeArgs& a, const Blk& c) {
+__device__ inline Blk next_block(const DecodeArgs& a, const Blk& c, const SeqRegs& sr) {
   Blk k = c;
   if (++k.i < k.nb) {
     k.kb += kKeys;
@@ -177,7 +200,7 @@ __device__ inline Blk next_block(const DecodeArgs& a, const Blk& c) {
     k.ub = 0;
     ++k.b;
   }
-  set_unit(k, a);
+  set_unit(k, a, sr);
   return k;
 }
 
@@ -339,7 +362,7 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
     const uint16_t* vn = a.v_new + kvrow;
     r.k0 = ld16(kn); r.k1 = ld16(kn + 32); r.k2 = ld16(kn + 64); r.k3 = ld16(kn + 96);
     if (a.rot) {
-      const int pos = clamp_len(clamp_len(a.hl[k.b], 0, a.M), 0, a.rot_rows - 1);
+      const int pos = clamp_len(k.L, 0, a.rot_rows - 1);
       rotate4<T>(r.k0, r.k1, r.k2, r.k3, q4, a.cosv + int64_t(pos) * (kD / 2),
                  a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
     }
@@ -437,22 +460,14 @@ struct UnitInfo {
   int unit, h0, nheads, w_first, w_last;
 };
 
-// Per-sequence plan values the end phase needs, copied to LDS when the
-// kernel starts (reading them from the argument block at a runtime index
-// there costs a memory round trip per unit).
-struct SeqTable {
-  int nb[kDecodeArgBatch];   // blocks per unit
-  int pb[kDecodeArgBatch];   // first global block
-};
-
-__device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub, const SeqTable& st) {
+__device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub, const SeqRegs& sr) {
   UnitInfo u;
   const int g = ub / a.n_hg, hg = ub % a.n_hg;
   u.h0 = g * a.G + hg * a.hg_size;
   u.nheads = min(a.hg_size, a.G - hg * a.hg_size);
   u.unit = b * a.Hkv * a.n_hg + ub;
-  const int nb = __builtin_amdgcn_readfirstlane(st.nb[b]);
-  const int64_t x0 = __builtin_amdgcn_readfirstlane(st.pb[b]) + int64_t(ub) * nb;
+  const int nb = seq_of(a, b, sr).nb;
+  const int64_t x0 = lane_of(sr.pb, b) + int64_t(ub) * nb;
   u.w_first = owner_worker(a, x0);
   u.w_last = owner_worker(a, x0 + nb - 1);
   return u;
@@ -527,7 +542,7 @@ __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, 
   const int hg = k.ub % a.n_hg;
   const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
   if (a.rot) {
-    const int pos = clamp_len(clamp_len(a.hl[k.b], 0, a.M), 0, a.rot_rows - 1);
+    const int pos = clamp_len(k.L, 0, a.rot_rows - 1);
     rotate4<T>(q.c0, q.c1, q.c2, q.c3, q4, a.cosv + int64_t(pos) * (kD / 2),
                a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
   }
@@ -542,9 +557,9 @@ __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, 
 // threads of the workgroup; `lds` holds 2 kMergeMax x 16 floats.
 template <class T>
 __device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds,
-                                  const SeqTable& st) {
+                                  const SeqRegs& sr) {
   const int tid = threadIdx.x;
-  const UnitInfo u = unit_info(a, b, ub, st);
+  const UnitInfo u = unit_info(a, b, ub, sr);
   const int wg_first = u.w_first / kDecodeWaves, wg_last = u.w_last / kDecodeWaves;
   const int count = wg_last - wg_first + 1;
   const float* base = a.partials + int64_t(wg_first + u.unit) * kSlotFloats;
@@ -625,7 +640,6 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
   __shared__ int sh_tab[kDecodeWaves][2][2];        // per wave, slot: (b, ub) or b = -1
   __shared__ int sh_flag[2];
-  __shared__ SeqTable sh_seq;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -636,10 +650,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   float* slot1 = reinterpret_cast<float*>(lds + wv * kWaveLds + kSlotBytes);
   unsigned char* vt = lds + wv * kWaveLds + kSlotBytes;     // the V tile while streaming
   if (lane < 4) sh_tab[wv][lane >> 1][lane & 1] = -1;
-  if (tid < a.B) {   // read by the end phase, after the barrier that follows the streaming
-    sh_seq.nb[tid] = seq_of(a, tid).nb;
-    sh_seq.pb[tid] = a.pb[tid];
-  }
+  const SeqRegs sr = load_seq_regs(a, lane);
 
   int64_t S = 0, E = 0;
   if (worker < a.workers) {
@@ -652,7 +663,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     }
   }
   if (S < E) {
-    Blk cur = locate(a, S);
+    Blk cur = locate(a, S, sr, lane);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
     KV rc = load_kv<kBias>(a, cur, n, q4, S + 1 >= E);
     Acc s;
@@ -663,9 +674,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // x + 1 and x + 2 are in flight. `ahead` is the block whose loads go out
     // next (x + 2), clamped to the slice's last block. Q rows are loaded when
     // their unit starts (a small, cache-resident read).
-    Blk nxt = S + 1 < E ? next_block(a, cur) : cur;        // block x + 1
+    Blk nxt = S + 1 < E ? next_block(a, cur, sr) : cur;        // block x + 1
     KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
-    Blk ahead = S + 2 < E ? next_block(a, nxt) : nxt;       // block x + 2
+    Blk ahead = S + 2 < E ? next_block(a, nxt, sr) : nxt;       // block x + 2
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
     // unit end or at the slice end. Returns false after the slice's last block.
@@ -693,7 +704,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       }
       cur = nxt;
       nxt = ahead;
-      ahead = x + 3 < E ? next_block(a, ahead) : ahead;
+      ahead = x + 3 < E ? next_block(a, ahead, sr) : ahead;
       return true;
     };
     KV r2;
@@ -725,7 +736,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     const int b = tb[e], ub = tu[e];
     if (b < 0 || (b == prev_b && ub == prev_ub)) continue;   // empty, or not a unit's first entry
     prev_b = b; prev_ub = ub;
-    const UnitInfo u = unit_info(a, b, ub, sh_seq);
+    const UnitInfo u = unit_info(a, b, ub, sr);
     const bool inside = u.w_first >= wg * kDecodeWaves && u.w_last < (wg + 1) * kDecodeWaves;
     float* gslot = a.partials + int64_t(wg + u.unit) * kSlotFloats;
     for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
@@ -784,8 +795,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
-  if (sh_flag[0]) merge_unit<T>(a, gb0, gub0, mlds, sh_seq);
-  if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds, sh_seq);
+  if (sh_flag[0]) merge_unit<T>(a, gb0, gub0, mlds, sr);
+  if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds, sr);
 }
 
 // Fused eviction, before the decode kernel: for the last block i of every
@@ -804,9 +815,11 @@ __global__ void __launch_bounds__(64) shift_halo_kernel(DecodeArgs a) {
     S = (int64_t(w) * a.total) / a.workers;
     E = (int64_t(w + 1) * a.total) / a.workers;
   }
-  if (S >= E || lane >= 32) return;
-  const Blk k = locate(a, E - 1);
-  if (!k.d || k.i + 1 >= k.nb) return;
+  if (S >= E) return;
+  // all 64 lanes take part in the lookup (one lane per sequence)
+  const SeqRegs sr = load_seq_regs(a, lane);
+  const Blk k = locate(a, E - 1, sr, lane);
+  if (lane >= 32 || !k.d || k.i + 1 >= k.nb) return;
   const bool vside = lane >= 16;
   const int part = lane & 15;
   const uint16_t* src = (vside ? k.vc : k.kc) + int64_t(k.kb + kKeys - 1 + k.d) * kD;

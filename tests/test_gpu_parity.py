@@ -110,6 +110,11 @@ SMALL = [
     # more sequences than travel in the kernel arguments: lengths read on the device
     ("bf16", 66, 3, 4, 2, 128, 64, [(7 * i) % 62 for i in range(66)], -1, True, 0, "prefill"),
     ("fp16", 66, 1, 4, 2, 128, 64, [(5 * i) % 64 for i in range(66)], -1, False, 0, "decode"),
+    # 33-64 sequences on the split-KV decode: per-sequence values held one
+    # per lane, including lanes 32-63 (plain, and with the fused eviction)
+    ("fp16", 48, 1, 8, 2, 128, 256, [(37 * i) % 256 for i in range(48)], -1, False, 0, "decode"),
+    ("bf16", 64, 1, 4, 1, 128, 192, [192 if i % 3 == 0 else (29 * i) % 192 for i in range(64)],
+     192, True, 0, "decode"),
     # windowed chunks that evict: attention over past ++ new in the staging
     # frames, then eviction and append in the cache (some sequences evict,
     # some not; the window below, at and above the chunk; S = M drops the
