@@ -184,9 +184,13 @@ gqa_status windowed_chunk(const Problem& P, int max_drop, void* ws, const Worksp
   // the plain kernel reads everything from the frame, from the tile the
   // window reaches on
   const bool direct = prefill_fast_supported(F);
-  hipError_t e = launch_copy_prefix(P.k_cache, P.v_cache, P.M, F.k_cache, F.v_cache, F.M,
-                                    P.lens_dev, P.B, P.Hkv, row_bytes, direct ? 1 : P.window,
-                                    max_len, hs);
+  // on the MFMA route only a partial tile at L_b has rows to copy
+  bool partial = !direct;
+  for (int b = 0; b < P.B && !partial; ++b) partial = P.lens_host[b] % kStageAlignRows != 0;
+  hipError_t e = hipSuccess;
+  if (partial)
+    e = launch_copy_prefix(P.k_cache, P.v_cache, P.M, F.k_cache, F.v_cache, F.M, P.lens_dev, P.B,
+                           P.Hkv, row_bytes, direct ? 1 : P.window, max_len, hs);
   if (e != hipSuccess) return hip_fail(e, "staging copy");
   e = launch_append(F, false, hs);
   if (e != hipSuccess) return hip_fail(e, "staging append");
