@@ -581,3 +581,74 @@ def test_split_prefill_repeated_calls_share_workspace(gpu):
     for o in outs:
         assert_close(o, want, case.dtype, "split prefill")
         assert np.array_equal(o, outs[0]), "the merge order depends on arrival"
+
+
+# --------------------------------------------------------------------------
+# seeded random combinations of the features (fixed seeds: a regular test)
+# --------------------------------------------------------------------------
+
+def _random_case(k):
+    rng = np.random.default_rng(1000 + k)
+    dt = ["fp16", "bf16", "fp32"][rng.integers(0, 3)]
+    D = 128 if dt != "fp32" and rng.random() < 0.8 else int(rng.choice([8, 64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 7]))
+    B = int(rng.integers(1, 5))
+    M = int(rng.choice([64, 96, 200, 320]))
+    S = 1 if rng.random() < 0.4 else int(rng.integers(2, min(M, 80) + 1))
+    window = -1
+    greedy = 0
+    if rng.random() < 0.5:
+        window = int(rng.integers(max(1, S), M + 1))
+        greedy = int(rng.random() < 0.4 and window < M)
+    if window > 0:
+        lens = [int(rng.integers(0, M + 1)) for _ in range(B)]
+    else:
+        lens = [int(rng.integers(0, M - S + 1)) for _ in range(B)]
+    rot = bool(rng.random() < 0.5)
+    inter = int(rot and rng.random() < 0.3)
+    case = gi.make_case("random", dt, B, S, G * Hkv, Hkv, D, M, lens, 2000 + k, window=window,
+                        rotary=rot, interleaved=inter, rotary_rows=(M + S if rot else None))
+    case.greedy_eviction = greedy
+    if rng.random() < 0.3:
+        T = int((np.asarray(lens) + S).max()) + int(rng.integers(0, 5))
+        Bb = B if rng.random() < 0.5 else 1
+        Hb = G * Hkv if rng.random() < 0.5 else 1
+        case.attention_bias = gi.to_bits(rng.standard_normal((Bb, Hb, S, T)), dt)
+    present_rows = int(max(lens)) + int(rng.integers(0, 8)) if rng.random() < 0.25 else None
+    return case, present_rows
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_random_feature_combinations(k):
+    import grouped_query_kv_amd as gqa
+    case, present_rows = _random_case(k)
+    entry = "decode" if case.new_tokens == 1 else "prefill"
+    desc = (f"random {k}: {case.dtype} B={case.batch} S={case.new_tokens} H={case.num_heads} "
+            f"Hkv={case.kv_num_heads} D={case.head_size} M={case.max_seq_len} W={case.local_window_size} "
+            f"greedy={case.greedy_eviction} rot={case.cos is not None} "
+            f"bias={None if case.attention_bias is None else case.attention_bias.shape} "
+            f"present={present_rows} lens={list(case.seqlens_k)}")
+    if present_rows is None:
+        check_full(case, entry, desc)
+        return
+    say(f"[gpu] {desc}")
+    rng = np.random.default_rng(3000 + k)
+    past_k = gi.fill_cache(rng, case.batch, case.kv_num_heads, present_rows, case.head_size,
+                           case.seqlens_k, case.dtype)
+    past_v = gi.fill_cache(rng, case.batch, case.kv_num_heads, present_rows, case.head_size,
+                           case.seqlens_k, case.dtype)
+    st, want, kc, vc, _ = O.gqa_attention_present(case, past_k, past_v)
+    assert st == O.OK
+    dev = DevCase(case)
+    fn = gqa.gqa_attention_decode if entry == "decode" else gqa.gqa_attention_prefill
+    out = fn(dev.q, dev.k_new, dev.v_new, to_dev(past_k, case.dtype), to_dev(past_v, case.dtype),
+             dev.lens_host, dev.lens_dev, scale=case.scale, local_window_size=case.local_window_size,
+             cos_cache=dev.cos, sin_cache=dev.sin, rotary_interleaved=case.rotary_interleaved,
+             present_key=dev.k_cache, present_value=dev.v_cache,
+             greedy_eviction=bool(case.greedy_eviction), attention_bias=dev.bias)
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, f"{desc} present k")
+    assert_bits_equal(gv, vc, f"{desc} present v")
+    err = assert_close(out_f64(out, case.dtype), want, case.dtype, desc)
+    say(f"[gpu]   max abs error {err:.3e}")
