@@ -280,7 +280,8 @@ struct Q4 {
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <bool kBias>
-__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end) {
+__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end,
+                             bool spare = false) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
   // fused eviction: key `row` is buffer row row + d. The first row of the
   // next block's sources is overwritten by that block's shifted stores. When
@@ -294,6 +295,12 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   const int64_t hrow = ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD + 8 * q4;
   const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
   const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * kD + 8 * q4;
+  // a spare load (the pipeline's refill past the slice's last block) reads
+  // the first 128 Q elements instead: one cache line for the wave, not a
+  // second copy of the last block, and the wait counts stay those of a full
+  // pipeline (a skipped load makes the compiler wait one block earlier).
+  // The bias kernel, at its register limit, measured slower with it.
+  if (!kBias && spare) { kp = a.q + 8 * q4; vp = kp; }
   KV r;
   r.k0 = ld16(kp); r.k1 = ld16(kp + 32); r.k2 = ld16(kp + 64); r.k3 = ld16(kp + 96);
   r.v0 = ld16(vp); r.v1 = ld16(vp + 32); r.v2 = ld16(vp + 64); r.v3 = ld16(vp + 96);
@@ -672,8 +679,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 
     // Blocks move through three register sets: while block x is computed,
     // x + 1 and x + 2 are in flight. `ahead` is the block whose loads go out
-    // next (x + 2), clamped to the slice's last block. Q rows are loaded when
-    // their unit starts (a small, cache-resident read).
+    // next (x + 2), clamped to the slice's last block; past it the loads are
+    // spare ones. Q rows are loaded when their unit starts (a small,
+    // cache-resident read).
     Blk nxt = S + 1 < E ? next_block(a, cur, sr) : cur;        // block x + 1
     KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
     Blk ahead = S + 2 < E ? next_block(a, nxt, sr) : nxt;       // block x + 2
@@ -683,7 +691,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E);   // ahead = min(x + 2, E - 1)
+      r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
       compute<T, kBias>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
