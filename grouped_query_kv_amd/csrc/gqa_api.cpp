@@ -109,7 +109,7 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
     *needs_evict = *max_drop > 0;
   } else {
     for (int b = 0; b < B; ++b)
-      if (lens_host[b] + S > M)
+      if (int64_t(lens_host[b]) + S > M)
         return fail(GQA_ERR_NO_ROOM, "sequence %d: %d past + %d new > max_seq_len %d", b,
                     lens_host[b], S, M);
   }
@@ -121,10 +121,11 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
     if (o->bias_heads != 1 && o->bias_heads != H)
       return fail(GQA_ERR_INVALID_ARG, "bias_heads %d is neither 1 nor num_heads %d",
                   o->bias_heads, (int)H);
-    int need = 1;
-    for (int b = 0; b < B; ++b) need = std::max(need, lens_host[b] + S);
+    int64_t need = 1;
+    for (int b = 0; b < B; ++b) need = std::max(need, int64_t(lens_host[b]) + S);
     if (o->bias_total < need)
-      return fail(GQA_ERR_INVALID_ARG, "bias_total %d < %d (past + new tokens)", o->bias_total, need);
+      return fail(GQA_ERR_INVALID_ARG, "bias_total %d < %lld (past + new tokens)", o->bias_total,
+                  (long long)need);
   }
   Problem& P = *p;
   P.bias = biased ? o->attention_bias : nullptr;

@@ -77,6 +77,13 @@ def test_no_room_when_past_plus_new_exceeds_buffer(g, entry):
     assert b"sequence 1" in g.lib.gqa_last_error()
 
 
+@pytest.mark.parametrize("entry", ["append", "prefill"])
+def test_no_room_without_integer_overflow(g, entry):
+    # past + new computed in 64 bits: a huge new_tokens is no room, not a wrap
+    st = _call(g, entry, _shape(g, S=2**31 - 1, M=16), lens=(5, 0))
+    assert st == g.GQA_ERR_NO_ROOM
+
+
 def test_no_room_in_decode_without_window(g):
     st = _call(g, "decode", _shape(g, S=1, M=16), lens=(16, 0))
     assert st == g.GQA_ERR_NO_ROOM
