@@ -412,7 +412,8 @@ gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming, void* k_ca
   if (st != GQA_OK) return st;
   if (B > 0 && !seqlens_after_host) return fail(GQA_ERR_INVALID_ARG, "seqlens_after_host is NULL");
   int max_drop = 0;
-  for (int b = 0; b < B; ++b) max_drop = std::max(max_drop, seqlens_k_host[b] + incoming - M);
+  for (int b = 0; b < B; ++b)
+    max_drop = std::max<int64_t>(max_drop, int64_t(seqlens_k_host[b]) + incoming - M);
   if (max_drop > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "cache is NULL");
   WorkspaceLayout lay;
   st = check_workspace(shape, -1, workspace, workspace_bytes, &lay);
