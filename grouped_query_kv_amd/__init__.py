@@ -146,6 +146,28 @@ def _contig(*ts):
             raise GQAError(GQA_ERR_INVALID_ARG, "tensors must be contiguous")
 
 
+def _check_aux(B, D, device, seqlens_k_dev, cos_cache, sin_cache, *tensors):
+    """What the kernels read beyond the main tensors must have the layout
+    they assume: int32 [B] device lengths, fp32 [P, D/2] rotary tables, and
+    every tensor on one device."""
+    torch = _torch()
+    for t in tensors + (seqlens_k_dev, cos_cache, sin_cache):
+        if t is not None and t.device != device:
+            raise GQAError(GQA_ERR_INVALID_ARG, f"tensor on {t.device}, expected {device}")
+    if seqlens_k_dev is not None and (seqlens_k_dev.dtype != torch.int32
+                                      or seqlens_k_dev.numel() != B
+                                      or not seqlens_k_dev.is_contiguous()):
+        raise GQAError(GQA_ERR_INVALID_ARG, f"seqlens_k_dev must be a contiguous int32 tensor of {B}")
+    if cos_cache is not None or sin_cache is not None:
+        if cos_cache is None or sin_cache is None:
+            raise GQAError(GQA_ERR_INVALID_ARG, "cos_cache and sin_cache must be given together")
+        for t in (cos_cache, sin_cache):
+            if (t.dtype != torch.float32 or t.dim() != 2 or int(t.shape[1]) != D // 2
+                    or tuple(t.shape) != tuple(cos_cache.shape) or not t.is_contiguous()):
+                raise GQAError(GQA_ERR_INVALID_ARG,
+                               f"cos_cache / sin_cache must be contiguous float32 [P, {D // 2}]")
+
+
 def make_shape(B, S, H, Hkv, D, M, dtype) -> Shape:
     return Shape(B, S, H, Hkv, D, M, dtype)
 
@@ -207,6 +229,7 @@ def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
     if tuple(k_new.shape) != tuple(v_new.shape) or k_new.dim() != 3:
         raise GQAError(GQA_ERR_INVALID_ARG, "k_new / v_new must both be [B, S, Hkv*D]")
     B, S, Hkv, M, D = _kv_common(k_new, k_cache, v_cache, None)
+    _check_aux(B, D, k_cache.device, seqlens_k_dev, cos_cache, sin_cache, k_new, v_new, v_cache)
     shape = make_shape(B, S, Hkv, Hkv, D, M, dtype_code(k_cache))
     opts = make_options(0.0, -1, cos_cache, sin_cache, rotary_interleaved)
     hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
@@ -246,6 +269,8 @@ def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_
     _contig(out)
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise GQAError(GQA_ERR_INVALID_ARG, "out must match q")
+    _check_aux(B, D, k_cache.device, seqlens_k_dev, cos_cache, sin_cache, q, k_new, v_new,
+               v_cache, out, attention_bias, past_k, past_v)
     shape = make_shape(B, S, H, Hkv, D, M, dtype_code(q))
     if attention_bias is not None:
         _contig(attention_bias)

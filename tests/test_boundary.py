@@ -276,5 +276,31 @@ def test_binding_surfaces_no_room(g):
     kc = torch.zeros(1, 1, 8, 4)
     kn = torch.zeros(1, 2, 4)
     with pytest.raises(g.GQAError) as e:
-        g.gqa_append_kv(kn, kn, kc, kc.clone(), np.array([7], np.int32), kc, stream=0)
+        g.gqa_append_kv(kn, kn, kc, kc.clone(), np.array([7], np.int32),
+                        torch.zeros(1, dtype=torch.int32), stream=0)
     assert e.value.status == g.GQA_ERR_NO_ROOM
+
+
+def test_binding_checks_lengths_and_rotary_tables(g):
+    # the kernels read these with a fixed layout: the binding refuses others
+    torch = pytest.importorskip("torch")
+    kc, vc = torch.zeros(2, 1, 8, 4), torch.zeros(2, 1, 8, 4)
+    q, kn = torch.zeros(2, 1, 8), torch.zeros(2, 1, 4)
+    lens = np.zeros(2, np.int32)
+    good = torch.zeros(2, dtype=torch.int32)
+    cos = torch.ones(9, 2)
+    bad_calls = [
+        dict(seqlens_k_dev=torch.zeros(2, dtype=torch.int64)),
+        dict(seqlens_k_dev=torch.zeros(3, dtype=torch.int32)),
+        dict(cos_cache=cos.half(), sin_cache=cos.half()),
+        dict(cos_cache=torch.ones(9, 4), sin_cache=torch.ones(9, 4)),
+        dict(cos_cache=cos, sin_cache=torch.ones(8, 2)),
+        dict(cos_cache=cos),
+    ]
+    for kw in bad_calls:
+        dev = kw.pop("seqlens_k_dev", good)
+        with pytest.raises(g.GQAError) as e:
+            g.gqa_attention_decode(q, kn, kn, kc, vc, lens, dev, stream=0, **kw)
+        assert e.value.status == g.GQA_ERR_INVALID_ARG, kw
+        with pytest.raises(g.GQAError):
+            g.gqa_append_kv(kn, kn, kc, vc, lens, dev, stream=0, **kw)
