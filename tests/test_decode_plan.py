@@ -83,7 +83,19 @@ def worker_range(a, b, ub):
     return owner(a, x0), owner(a, x0 + nb - 1)
 
 
+def check_owner(a):
+    # owner(x) is the inverse of the slice bounds for every block
+    if a["total"] == 0:
+        return
+    starts = np.array([w * a["total"] // a["workers"] for w in range(a["workers"] + 1)])
+    assert starts[-1] == a["total"] and (np.diff(starts) > 0).all()
+    xs = np.arange(a["total"])
+    want = np.searchsorted(starts, xs, side="right") - 1
+    assert (np.array([owner(a, int(x)) for x in xs]) == want).all()
+
+
 def run_plan(a):
+    check_owner(a)
     nunits = a["B"] * a["units"]
     gslots, gwrote = {}, {}
     for wg in range(-(-a["workers"] // WAVES)):
