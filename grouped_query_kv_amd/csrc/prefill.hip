@@ -82,7 +82,7 @@ constexpr int kBK = 64;                       // keys per tile
 #define GQA_PREFILL_PLAN_PCT 100              // split plan: workgroups per 100 CUs
 #endif
 #ifndef GQA_PREFILL_READ_AHEAD
-#define GQA_PREFILL_READ_AHEAD 8              // LDS operand reads issued ahead of their product
+#define GQA_PREFILL_READ_AHEAD 4              // LDS operand reads issued ahead of their product
 #endif
 constexpr int kWaves = 8;                     // two groups of four (one wave of each per SIMD)
 constexpr int kThreads = 64 * kWaves;
