@@ -90,10 +90,9 @@ struct DecodeArgs {
   const float* sinv;
   float* partials;
   int* counters;
-  uint16_t* halo_k;                     // fused eviction: next-block first rows, [B, Hkv, hb, D]
-  uint16_t* halo_v;
+  uint16_t* halo_k;                     // fused eviction: one row per worker, [workers, D]: the
+  uint16_t* halo_v;                     //   source row after its slice that the next slice overwrites
   int shift;                            // fused eviction on: full sequences drop their oldest row
-  int hb;                               // halo rows per unit (blocks of the buffer)
   int B, H, Hkv, G, M, W;
   int cap;                              // rows an evicting sequence keeps: M - 1, or W - 1 (greedy)
   int rot, rot_rows, interleaved;
@@ -280,8 +279,8 @@ struct Q4 {
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <bool kBias>
-__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end,
-                             bool spare = false) {
+__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, int worker,
+                             bool slice_end, bool spare = false) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
   // fused eviction: key `row` is buffer row row + d. The first row of the
   // next block's sources is overwritten by that block's shifted stores. When
@@ -292,7 +291,7 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   int src = row + k.d;
   const bool halo = k.d && slice_end && n == kKeys - 1 && k.i + 1 < k.nb;
   src = src < a.M ? src : row;
-  const int64_t hrow = ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD + 8 * q4;
+  const int64_t hrow = int64_t(worker) * kD + 8 * q4;      // the slice's halo row
   const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
   const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * kD + 8 * q4;
   // a spare load (the pipeline's refill past the slice's last block) reads
@@ -672,7 +671,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (S < E) {
     Blk cur = locate(a, S, sr, lane);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
-    KV rc = load_kv<kBias>(a, cur, n, q4, S + 1 >= E);
+    KV rc = load_kv<kBias>(a, cur, n, q4, worker, S + 1 >= E);
     Acc s;
     acc_reset(s);
     bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
@@ -683,7 +682,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // spare ones. Q rows are loaded when their unit starts (a small,
     // cache-resident read).
     Blk nxt = S + 1 < E ? next_block(a, cur, sr) : cur;        // block x + 1
-    KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
+    KV r1 = load_kv<kBias>(a, nxt, n, q4, worker, S + 2 >= E);
     Blk ahead = S + 2 < E ? next_block(a, nxt, sr) : nxt;       // block x + 2
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
@@ -691,7 +690,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
+      r_fill = load_kv<kBias>(a, ahead, n, q4, worker, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
       compute<T, kBias>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
@@ -793,13 +792,22 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     }
   }
   if (nglob == 0) return;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial stores have landed
+  // release/acquire handoff: the workgroup barrier orders every thread's
+  // partial stores before the count; the counting thread's increment
+  // releases them at agent scope (every increment of a counter continues
+  // the release sequence of the earlier ones), and the thread whose
+  // increment completes the count acquires at agent scope before the
+  // barrier that carries it to the whole workgroup. Only that workgroup pays
+  // for the acquire (an L2 invalidate, which would otherwise also drop lines
+  // the other workgroups on its XCD still read).
   __syncthreads();
   if (tid < nglob) {
     // counted in; the workgroup that completes the count merges
     const int prev = __hip_atomic_fetch_add(a.counters + (tid ? gunit1 : gunit0), 1,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh_flag[tid] = prev == (tid ? gneed1 : gneed0);
+                                            __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (tid ? gneed1 : gneed0);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sh_flag[tid] = last;
   }
   __syncthreads();
   float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
@@ -831,8 +839,7 @@ __global__ void __launch_bounds__(64) shift_halo_kernel(DecodeArgs a) {
   const bool vside = lane >= 16;
   const int part = lane & 15;
   const uint16_t* src = (vside ? k.vc : k.kc) + int64_t(k.kb + kKeys - 1 + k.d) * kD;
-  uint16_t* dst = (vside ? a.halo_v : a.halo_k) +
-                  ((int64_t(k.b) * a.Hkv + k.g) * a.hb + k.i) * kD;
+  uint16_t* dst = (vside ? a.halo_v : a.halo_k) + int64_t(w) * kD;
   *reinterpret_cast<uint4*>(dst + 8 * part) = *reinterpret_cast<const uint4*>(src + 8 * part);
 }
 
@@ -864,9 +871,8 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scratch);
   a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + lay.counters);
   a.shift = fuse_evict ? 1 : 0;
-  a.hb = ceil_div(p.M, kKeys);
   a.halo_k = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.decode_halo);
-  a.halo_v = a.halo_k + int64_t(p.B) * p.Hkv * a.hb * kD;
+  a.halo_v = a.halo_k + int64_t(kDecodeMaxWorkers) * kD;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window; a.cap = p.cap;
   a.n_hg = ceil_div(p.G, kDecodeMaxHG);
   a.hg_size = ceil_div(p.G, a.n_hg);

@@ -94,6 +94,12 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
     if (!k_new || !v_new || !k_cache || !v_cache)
       return fail(GQA_ERR_INVALID_ARG, "a K/V pointer is NULL");
     if (entry != kAppend && (!q || !out)) return fail(GQA_ERR_INVALID_ARG, "q or out is NULL");
+    const uintptr_t bits = uintptr_t(k_new) | uintptr_t(v_new) | uintptr_t(k_cache) |
+                           uintptr_t(v_cache) |
+                           (entry != kAppend ? uintptr_t(q) | uintptr_t(out) : uintptr_t(0));
+    if (bits & (kTensorAlign - 1))
+      return fail(GQA_ERR_INVALID_ARG, "q, k_new, v_new, the caches and out must be %d-byte aligned",
+                  kTensorAlign);
   }
   const bool windowed = W > 0 && entry != kAppend;
   const bool greedy = o->greedy_eviction != 0 && entry != kAppend;
@@ -214,23 +220,10 @@ gqa_status windowed_chunk(const Problem& P, int max_drop, void* ws, const Worksp
   return GQA_OK;
 }
 
-// The whole op for one call. S == 1 takes the split-KV decode route.
-gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options* opts,
-                         const void* q, const void* k_new, const void* v_new, void* k_cache,
-                         void* v_cache, const int32_t* lens_host, const int32_t* lens_dev,
-                         void* out, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = '\0';
-  Problem P;
-  bool needs_evict;
-  int max_drop;
-  gqa_status st = validate(entry, shape, opts, q, k_new, v_new, k_cache, v_cache, lens_host,
-                           lens_dev, out, &P, &needs_evict, &max_drop);
-  if (st != GQA_OK) return st;
-  WorkspaceLayout lay;
-  st = check_workspace(shape, P.window, ws, ws_bytes, &lay);
-  if (st != GQA_OK) return st;
-  if (P.B == 0) return GQA_OK;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+// The kernels of one validated call, on the workspace `ws` carved as `lay`.
+// S == 1 takes the split-KV decode route.
+gqa_status execute(const Problem& P, bool needs_evict, int max_drop, void* ws,
+                   const WorkspaceLayout& lay, hipStream_t hs) {
   hipError_t e;
   if (needs_evict && P.S > 1) return windowed_chunk(P, max_drop, ws, lay, hs);
   const bool fast_decode = P.S == 1 && decode_fast_supported(P);
@@ -247,9 +240,33 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
   }
   e = launch_append(P, evicted_lengths, hs);
   if (e != hipSuccess) return hip_fail(e, "append");
-  e = attend(P, ws, lay, hs);
+  // After an eviction the MFMA kernel still finds each sequence's keys (it
+  // applies the same kept-rows rule), but a bias column is then the buffer
+  // row plus the dropped count, which its aligned four-column bias loads
+  // cannot follow: such calls take the plain kernel.
+  e = (needs_evict && P.bias) ? launch_attention_simple(P, hs) : attend(P, ws, lay, hs);
   if (e != hipSuccess) return hip_fail(e, "attention");
   return GQA_OK;
+}
+
+// The whole op for one call: validation and the workspace check first (no
+// device call before both pass), then the kernels.
+gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options* opts,
+                         const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* lens_host, const int32_t* lens_dev,
+                         void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = '\0';
+  Problem P;
+  bool needs_evict;
+  int max_drop;
+  gqa_status st = validate(entry, shape, opts, q, k_new, v_new, k_cache, v_cache, lens_host,
+                           lens_dev, out, &P, &needs_evict, &max_drop);
+  if (st != GQA_OK) return st;
+  WorkspaceLayout lay;
+  st = check_workspace(shape, P.window, ws, ws_bytes, &lay);
+  if (st != GQA_OK) return st;
+  if (P.B == 0) return GQA_OK;
+  return execute(P, needs_evict, max_drop, ws, lay, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -277,12 +294,14 @@ WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   const EvictGeometry eg = evict_geometry((int)row_bytes);
   const int64_t chunks = (M + eg.chunk_rows - 1) / eg.chunk_rows;
   const int64_t halo = B * Hkv * 2 * chunks * kEvictHaloMax * row_bytes;
-  // fused-eviction halo rows (decode): [2][B, Hkv, ceil(M / 16), D] in the dtype
+  // fused-eviction halo rows (decode): one K and one V row per worker, in the dtype
   int64_t dhalo = 0;
-  if (D == 128 && s.dtype != GQA_FP32) dhalo = 2 * B * Hkv * ((M + 15) / 16) * D * 2;
-  // prefill split partials: [row blocks, splits] slots (only when splitting)
+  if (D == 128 && s.dtype != GQA_FP32) dhalo = 2 * int64_t(kDecodeMaxWorkers) * D * 2;
+  // prefill split partials: [row blocks, splits] slots (only when splitting;
+  // a one-token shape that the split-KV decode serves never runs the prefill)
   int64_t pf_items = 0, pf_partial = 0;
-  if (D == 128 && s.dtype != GQA_FP32 && s.new_tokens > 0) {
+  const bool decode_only = s.new_tokens == 1 && B <= kDecodeArgBatch;
+  if (D == 128 && s.dtype != GQA_FP32 && s.new_tokens > 0 && !decode_only) {
     if (prefill_may_split(B, s.new_tokens, G, Hkv, M)) {
       pf_items = ((s.new_tokens * G + kPrefillWgRows - 1) / kPrefillWgRows) * B * Hkv;
       // the plan may give one row block up to kPrefillMaxSplits ranges
@@ -297,7 +316,8 @@ WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   l.scratch_bytes = align256(std::max({size_t(halo), align256(size_t(partial)) + size_t(dhalo),
                                        size_t(pf_partial)}));
   l.prefill_counters = l.scratch + l.scratch_bytes;
-  l.total = l.prefill_counters + align256(size_t(pf_items) * sizeof(int32_t));
+  l.prefill_counters_bytes = align256(size_t(pf_items) * sizeof(int32_t));
+  l.total = l.prefill_counters + l.prefill_counters_bytes;
   if (staged) {
     l.stage_rows = int(M);
     l.stage_bytes = align256(size_t(B * Hkv * M * row_bytes));
@@ -383,6 +403,8 @@ gqa_status gqa_attention_present(const gqa_shape* shape, const gqa_options* opts
                 "past and present share a buffer only as a whole (same K and V, same rows)");
   if (!same && max_len > 0 && (!past_key || !past_value))
     return fail(GQA_ERR_INVALID_ARG, "past_key or past_value is NULL");
+  if (!same && ((uintptr_t(past_key) | uintptr_t(past_value)) & (kTensorAlign - 1)))
+    return fail(GQA_ERR_INVALID_ARG, "past_key and past_value must be %d-byte aligned", kTensorAlign);
   WorkspaceLayout lay;
   st = check_workspace(shape, P.window, workspace, workspace_bytes, &lay);
   if (st != GQA_OK) return st;
@@ -415,6 +437,8 @@ gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming, void* k_ca
   for (int b = 0; b < B; ++b)
     max_drop = std::max<int64_t>(max_drop, int64_t(seqlens_k_host[b]) + incoming - M);
   if (max_drop > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "cache is NULL");
+  if (max_drop > 0 && ((uintptr_t(k_cache) | uintptr_t(v_cache)) & (kTensorAlign - 1)))
+    return fail(GQA_ERR_INVALID_ARG, "the caches must be %d-byte aligned", kTensorAlign);
   WorkspaceLayout lay;
   st = check_workspace(shape, -1, workspace, workspace_bytes, &lay);
   if (st != GQA_OK) return st;

@@ -55,6 +55,7 @@ struct WorkspaceLayout {
   size_t scratch_bytes;
   size_t decode_halo;     // fused-eviction halo rows, after the decode partials
   size_t prefill_counters;  // int32 [prefill row blocks] split counters (kept zero)
+  size_t prefill_counters_bytes;
   size_t prefill_partials;  // split partials of the prefill kernel (in the scratch area)
   // windowed chunk (S > 1, a window, some sequence evicting): K and V staging
   // frames [B, Hkv, stage_rows, D], stage_rows = M + S, in which attention
@@ -102,11 +103,11 @@ constexpr int kDecodeArgBatch = 64;      // largest batch the fast decode plans 
 // Eviction (parallel form): chunks of kEvictChunkRows rows, one thread per
 // 16-byte column of a chunk; halo copies are used up to kEvictHaloMax
 // dropped rows, the serial form beyond.
-constexpr int kEvictHaloMax = 16;         // largest drop the parallel eviction handles
+constexpr int kEvictHaloMax = 4;          // largest drop the parallel eviction handles
 constexpr int kEvictThreads = 256;
 constexpr int kEvictUnitsPerThread = 16;  // serial eviction: units per thread per pass
 #ifndef GQA_EVICT_CHUNK_ROWS
-#define GQA_EVICT_CHUNK_ROWS 64
+#define GQA_EVICT_CHUNK_ROWS 128
 #endif
 #ifndef GQA_EVICT_ROWS_IN_FLIGHT
 #define GQA_EVICT_ROWS_IN_FLIGHT 8
@@ -115,6 +116,11 @@ constexpr int kEvictChunkRows = GQA_EVICT_CHUNK_ROWS;       // rows per chunk of
 constexpr int kEvictRowsInFlight = GQA_EVICT_ROWS_IN_FLIGHT;  // rows of one column a thread has in flight
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Every tensor the kernels read or write in 16-byte vector units (Q, the new
+// K/V rows, the caches, the output, a separate past) must start at a
+// multiple of this many bytes.
+constexpr int kTensorAlign = 16;
 
 // Rows a sequence of length L keeps before its S new rows: all of them when
 // they fit, else the min(L, max(0, cap - S)) most recent (cap = M keeps the

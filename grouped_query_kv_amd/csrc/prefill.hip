@@ -103,6 +103,7 @@ struct PrefillArgs {
   const float* cosv;
   const float* sinv;
   int B, S, H, Hkv, G, M, W;
+  int cap;            // an evicting sequence keeps min(L, max(0, cap - S)) rows (M, or W when greedy)
   // windowed chunk: keys from each sequence's 64-aligned past length on come
   // from the staging frame (M rows per (b, kv head), row = key), earlier
   // keys from the cache (kv_rows rows per (b, kv head)); without a frame
@@ -517,7 +518,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   } else {
     len_raw = __builtin_amdgcn_readfirstlane(a.lens[b]);
   }
-  const int L = clamp_len(len_raw, 0, a.M - S);
+  // rows kept before the new ones (the append already ran, after any
+  // eviction): the same rule as the eviction kernels
+  const int L = clamp_len(kept_rows(clamp_len(len_raw, 0, a.M), S, a.M, a.cap), 0, a.M - S);
   const int kvalid = L + S;
 
   const int r0 = rb * kWgRows;
@@ -673,13 +676,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(mine + 512 * 64 + tid, rs.m_use, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(mine + 512 * 65 + tid, l_row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial has landed
+    // release/acquire handoff: the workgroup barrier orders every thread's
+    // partial stores before the count; the counting thread's increment
+    // releases them at agent scope (each increment continues the release
+    // sequence of the earlier ones), and the thread whose increment
+    // completes the count acquires at agent scope before the barrier that
+    // carries it to the whole workgroup. Only that workgroup pays for the
+    // acquire (an L2 invalidate, which would also drop K/V lines the other
+    // workgroups on its XCD still read).
     __syncthreads();
     if (tid == 0) {
-      const int prev = __hip_atomic_fetch_add(a.counters + item, 1, __ATOMIC_RELAXED,
+      const int prev = __hip_atomic_fetch_add(a.counters + item, 1, __ATOMIC_RELEASE,
                                               __HIP_MEMORY_SCOPE_AGENT);
       sh_last = prev == nsplit - 1;
-      if (sh_last) __hip_atomic_store(a.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sh_last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(a.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     if (!sh_last) return;
@@ -771,6 +784,7 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
   a.lens = p.lens_dev;
   a.cosv = p.cos; a.sinv = p.sin;
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window;
+  a.cap = p.cap;
   a.k_stage = static_cast<const uint16_t*>(p.stage_k);
   a.v_stage = static_cast<const uint16_t*>(p.stage_v);
   a.kv_rows = p.stage_k ? p.cache_rows : p.M;
@@ -800,7 +814,7 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
     int tmax = 1;
     for (int k = 0; k < a.n_items0; ++k) {
       const int rb = a.n_rb - 1 - k / units, b = (k % units) / p.Hkv;
-      const int L = std::max(0, std::min(p.lens_host[b], p.M - p.S));
+      const int L = std::max(0, std::min(kept_rows_host(p.lens_host[b], p.S, p.M, p.cap), p.M - p.S));
       const int r0 = rb * kWgRows;
       const int ilo = r0 / p.G, ihi = std::min(p.S - 1, (r0 + kWgRows - 1) / p.G);
       const int kstart = p.window > 0 ? std::max(0, L + ilo - p.window + 1) : 0;

@@ -52,9 +52,10 @@
  *      gives its shape) takes bias[b, h, i, j + d_b] for the key at row j
  *      after an eviction of d_b rows, i.e. its column is the key's position
  *      in past ++ new. With a bias the split-KV decode (S = 1, fp16/bf16,
- *      D = 128) and the MFMA prefill (fp16/bf16, D = 128, bias_total a
- *      multiple of 4, bias 8-byte aligned) keep their kernels; other calls
- *      use the plain kernel.
+ *      D = 128, B <= 64) and the MFMA prefill (fp16/bf16, D = 128,
+ *      bias_total a multiple of 4, bias 8-byte aligned) keep their kernels;
+ *      other calls, and one-token calls that evict outside the split-KV
+ *      decode, use the plain kernel.
  *
  * Ownership and threading: every pointer except *_host arguments is device
  * memory owned by the caller. The library never allocates, frees or
@@ -62,6 +63,10 @@
  * the null stream) and the call returns before it completes. The library
  * keeps no state between calls except the error-message buffer, which is
  * thread-local.
+ *
+ * Alignment: q, k_new, v_new, out and the caches (and a separate past) must
+ * start at a multiple of 16 bytes (the kernels move 16-byte units; torch
+ * allocations are 256-byte aligned); otherwise GQA_ERR_INVALID_ARG.
  *
  * Errors: every argument is validated before the first launch, so any
  * status other than GQA_OK and GQA_ERR_HIP guarantees that nothing was

@@ -93,29 +93,3 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what=""):
         bad = np.argwhere(got != want)
         raise AssertionError(f"{what}: {len(bad)} elements differ, first at {tuple(bad[0])}: "
                              f"got {got[tuple(bad[0])]:#x}, want {want[tuple(bad[0])]:#x}")
-
-
-def oracle_sampled(case, rows_by_b):
-    """fp64 outputs for selected query rows (all heads) via the oracle's pieces:
-    rotary, append, and one masked softmax per (b, h) over the selected rows.
-    Valid when no eviction is needed. Returns {b: [len(rows), H*D]}."""
-    B, S, H, Hkv, D = case.batch, case.new_tokens, case.num_heads, case.kv_num_heads, case.head_size
-    G = H // Hkv
-    qr = O.rotated_bits(case, case.q, H)
-    st, kc, vc = O.gqa_append_kv(case)
-    assert st == O.OK
-    sc = O.scale_of(case)
-    res = {}
-    for b, rows in rows_by_b.items():
-        rows = np.asarray(rows)
-        L = int(case.seqlens_k[b])
-        T = L + S
-        full = O.allowed_mask(S, T, L, case.local_window_size)[rows]
-        keys = O.to_f64(kc[b, :, :T], case.dtype)
-        vals = O.to_f64(vc[b, :, :T], case.dtype)
-        qf = O.to_f64(qr[b][:, rows], case.dtype)
-        o = np.zeros((len(rows), H * D))
-        for h in range(H):
-            o[:, h * D:(h + 1) * D] = O.attend_one(qf[h], keys[h // G], vals[h // G], full, sc)
-        res[b] = o
-    return res, kc, vc

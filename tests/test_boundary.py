@@ -304,3 +304,42 @@ def test_binding_checks_lengths_and_rotary_tables(g):
         assert e.value.status == g.GQA_ERR_INVALID_ARG, kw
         with pytest.raises(g.GQAError):
             g.gqa_append_kv(kn, kn, kc, vc, lens, dev, stream=0, **kw)
+
+
+# --------------------------------------------------------------------------
+# alignment: the vector kernels move 16-byte units of every tensor
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("entry", ["append", "prefill", "decode"])
+@pytest.mark.parametrize("which", range(6))
+def test_misaligned_tensors_are_rejected(g, entry, which):
+    # pointer order of the attention calls: q, k_new, v_new, k_cache, v_cache, out
+    ptrs = [FAKE] * 6
+    ptrs[which] = FAKE + 8
+    shape = _shape(g, S=1 if entry == "decode" else 3)
+    opts = g.Options(0.0, -1, None, None, 0, 0)
+    hl = np.zeros(2, np.int32)
+    hp = hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    if entry == "append":
+        if which in (0, 5):          # no q / out in the append half
+            return
+        st = g.lib.gqa_append_kv(ctypes.byref(shape), ctypes.byref(opts), *ptrs[1:5], hp, FAKE, None)
+    else:
+        fn = g.lib.gqa_attention_decode if entry == "decode" else g.lib.gqa_attention_prefill
+        st = fn(ctypes.byref(shape), ctypes.byref(opts), *ptrs[:5], hp, FAKE, ptrs[5], FAKE, 1 << 30,
+                None)
+    assert st == g.GQA_ERR_INVALID_ARG
+    assert b"aligned" in g.lib.gqa_last_error()
+
+
+def test_misaligned_past_and_evict_buffers_are_rejected(g):
+    shape = _shape(g, S=3, M=16)
+    st = _present(g, shape, (5, 2), 8, past_k=FAKE + 0x1004)
+    assert st == g.GQA_ERR_INVALID_ARG and b"aligned" in g.lib.gqa_last_error()
+    after = np.zeros(2, np.int32)
+    hl = np.asarray((16, 3), np.int32)
+    st = g.lib.gqa_evict_window(ctypes.byref(_shape(g, S=0, M=16)), 1, FAKE + 2, FAKE,
+                                hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), FAKE,
+                                after.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), FAKE, 1 << 30,
+                                None)
+    assert st == g.GQA_ERR_INVALID_ARG and b"aligned" in g.lib.gqa_last_error()

@@ -30,8 +30,8 @@ def gpu():
     return torch
 
 
-from gpu_helpers import (DevCase, assert_bits_equal, assert_close, oracle_sampled,  # noqa: E402
-                         out_f64, to_bits, to_dev)
+from gpu_helpers import (DevCase, assert_bits_equal, assert_close, out_f64, to_bits,  # noqa: E402
+                         to_dev)
 
 
 def check_full(case, entry="prefill", what=""):
@@ -286,6 +286,32 @@ def test_attention_bias(spec):
     check_full(case, "decode" if S == 1 else "prefill", f"bias {spec}")
 
 
+# More sequences than the split-KV decode plans (64): one-token calls that
+# evict run the eviction kernel, the append and then the MFMA prefill kernel
+# (which must keep the same rows as the eviction: W - 1 with greedy eviction)
+# or, with a bias, the plain kernel (the bias column of a kept key is its
+# buffer row plus the dropped count).
+MANY = [
+    # dtype, H, Hkv, M, W, greedy, bias kind
+    ("bf16", 8, 2, 96, 64, 1, None),
+    ("fp16", 8, 2, 96, 96, 0, "BH"),
+    ("fp16", 4, 1, 80, 48, 1, "1H"),
+]
+
+
+@pytest.mark.parametrize("spec", MANY, ids=[f"{s[0]}-g{s[5]}-{s[6]}" for s in MANY])
+def test_many_sequences_evicting_decode(spec):
+    dt, H, Hkv, M, W, greedy, kind = spec
+    B = 66
+    lens = [M if i % 3 else (11 * i) % M for i in range(B)]
+    seed = sum(map(ord, repr(spec))) % 1000
+    case = gi.make_case("many", dt, B, 1, H, Hkv, 128, M, lens, seed, window=W)
+    case.greedy_eviction = greedy
+    if kind:
+        _attach_bias(case, kind, 2, np.random.default_rng(seed))
+    check_full(case, "decode", f"{B} sequences evicting {spec}")
+
+
 def test_attention_bias_decode_full_size():
     case = gi.workload("split-kv-decode-fp16")
     _attach_bias(case, "BH", 1, np.random.default_rng(77))
@@ -408,35 +434,20 @@ def test_windowed_chunks_rolling(dt):
         dev.k_cache, dev.v_cache = cache_k, cache_v
 
 
-def test_causal_prefill_full_size_sampled():
-    case = gi.workload("causal-prefill-bf16")
-    rows = {0: [0, 1, 2, 63, 64, 127, 128, 1000, 2047], 1: [5, 511, 512, 2046],
-            2: [0, 2047], 3: [1023, 1024, 1025]}
-    say("[gpu] causal prefill (sampled rows vs oracle, full caches)")
-    want, kc, vc = oracle_sampled(case, rows)
-    dev = DevCase(case)
-    out = dev.run("prefill")
-    gk, gv = dev.caches()
-    assert_bits_equal(gk, kc, "causal prefill k_cache")
-    assert_bits_equal(gv, vc, "causal prefill v_cache")
-    got = out_f64(out, "bf16")
-    worst = max(assert_close(got[b, r], want[b], "bf16", f"causal prefill b={b}") for b, r in rows.items())
-    say(f"[gpu]   max abs error {worst:.3e}")
+def test_causal_prefill_full_size():
+    """The causal prefill workload in full: every output row of every
+    sequence and head (all 32 row blocks of each (sequence, kv head)) against
+    the oracle, and both caches bit for bit."""
+    check_full(gi.workload("causal-prefill-bf16"), "prefill", "causal prefill (every row)")
 
 
-def test_ragged_continuation_full_size_sampled():
+def test_ragged_continuation_full_size():
+    """The ragged continuation workload in full: every output row (each
+    (sequence, kv head) has 128 x 7 query rows in 4 row blocks, whose key
+    ranges the split plan cuts over up to 4 workgroups) against the oracle,
+    and both caches bit for bit."""
     case = gi.workload("ragged-continuation-fp16")
-    rows = {b: [0, 1, 63, 64, 126, 127] for b in range(case.batch)}
-    say(f"[gpu] ragged continuation lens={case.seqlens_k.tolist()}")
-    want, kc, vc = oracle_sampled(case, rows)
-    dev = DevCase(case)
-    out = dev.run("prefill")
-    gk, gv = dev.caches()
-    assert_bits_equal(gk, kc, "ragged continuation k_cache")
-    assert_bits_equal(gv, vc, "ragged continuation v_cache")
-    got = out_f64(out, "fp16")
-    worst = max(assert_close(got[b, r], want[b], "fp16", f"ragged continuation b={b}") for b, r in rows.items())
-    say(f"[gpu]   max abs error {worst:.3e}")
+    check_full(case, "prefill", f"ragged continuation (every row) lens={case.seqlens_k.tolist()}")
 
 
 # --------------------------------------------------------------------------
