@@ -88,6 +88,7 @@ class Case:
     rotary_interleaved: int = 0
     greedy_eviction: int = 0              # 1: evict only on overflow, keep the latest W
     attention_bias: Optional[np.ndarray] = None   # bits [B or 1, H or 1, S, T] or None
+    position_offset: Optional[np.ndarray] = None  # int32 [B]: absolute position of buffer row 0
     seed: int = 0
     extra: dict = dataclasses.field(default_factory=dict)
 
@@ -95,6 +96,8 @@ class Case:
         c = dataclasses.replace(self)
         for f in ("seqlens_k", "q", "k_new", "v_new", "k_cache", "v_cache"):
             setattr(c, f, getattr(self, f).copy())
+        if self.position_offset is not None:
+            c.position_offset = self.position_offset.copy()
         c.extra = dict(self.extra)
         return c
 

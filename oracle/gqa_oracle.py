@@ -44,7 +44,12 @@ Readings where the pages are silent (each also listed in the design notes):
     expression x1*c - x2*s / x2*c + x1*s (both products exact in fp64), then
     rounded to fp32 and to the storage dtype, both nearest-even.
   * rotated Q is rounded to the storage dtype before use, like rotated K.
-  * rotary positions are L_b + i (before any eviction).
+  * rotary positions are offset_b + L_b + i, where L_b is the length before
+    any eviction of the call and offset_b (0 unless given) is the absolute
+    position of buffer row 0: [P2] para 1 puts the positions at arange plus
+    the past length, and once a window has dropped old tokens ([P1]
+    follow-up) the past length alone no longer counts them, so a caller
+    keeping a rolling window passes the dropped count as the offset.
   * with a window, S > 1 and eviction, attention runs over the logical
     sequence before eviction (past ++ new), then the cache is compacted.
 
@@ -117,13 +122,16 @@ def validate(case, entry: str) -> str:
     lens = np.asarray(case.seqlens_k, dtype=np.int64)
     if lens.shape != (B,) or (B and (lens.min() < 0 or lens.max() > M)):
         return INVALID
+    off = position_offsets(case)
+    if off.shape != (B,) or (B and off.min() < 0):
+        return INVALID
     rot = case.cos is not None
     if rot:
         if D % 2 or case.sin is None or case.cos.shape != case.sin.shape:
             return INVALID
         if case.cos.shape[1] != D // 2:
             return INVALID
-        if B and S and int(lens.max()) + S > case.cos.shape[0]:
+        if B and S and int((off + lens).max()) + S > case.cos.shape[0]:
             return INVALID
     bias = getattr(case, "attention_bias", None)
     if bias is not None and entry != "append":
@@ -174,15 +182,27 @@ def _heads_first(bits: np.ndarray, B: int, S: int, nh: int, D: int) -> np.ndarra
     return bits.reshape(B, S, nh, D).transpose(0, 2, 1, 3)
 
 
+def position_offsets(case) -> np.ndarray:
+    """Absolute position of buffer row 0 per sequence (zeros when not given)."""
+    off = getattr(case, "position_offset", None)
+    if off is None:
+        return np.zeros(case.batch, dtype=np.int64)
+    return np.asarray(off, dtype=np.int64)
+
+
 def rotated_bits(case, bits: np.ndarray, nh: int) -> np.ndarray:
-    """Q or K_new in [B, nh, S, D] bits, rotated when the case has tables."""
+    """Q or K_new in [B, nh, S, D] bits, rotated when the case has tables.
+
+    Token i of sequence b sits at position offset_b + L_b + i ([P2] para 1,
+    with the offset of a rolling window; L_b before any eviction)."""
     B, S, D = case.batch, case.new_tokens, case.head_size
     x = _heads_first(bits, B, S, nh, D)
     if case.cos is None:
         return np.ascontiguousarray(x)
+    off = position_offsets(case)
     out = np.empty(x.shape, dtype=bits.dtype)
     for b in range(B):
-        pos = int(case.seqlens_k[b]) + np.arange(S)
+        pos = int(off[b]) + int(case.seqlens_k[b]) + np.arange(S)
         y = rotary_f64(to_f64(x[b], case.dtype), pos, case.cos, case.sin, case.rotary_interleaved)
         out[b] = round_f64_to_dtype(y, case.dtype)
     return out

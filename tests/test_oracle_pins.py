@@ -404,49 +404,101 @@ def test_windowed_decode_equals_full_history_window_attention():
         big.k_cache, big.v_cache, big.seqlens_k = kc2, vc2, l2.astype(np.int32)
 
 
-def test_windowed_chunks_equal_full_history_window_attention():
-    """Chunks of S > 1 tokens into a full W-slot cache (attention before the
-    eviction drops the keys early queries still see) vs the same chunks into a
-    buffer long enough to keep the whole history, with the same window mask.
-    Rotary positions follow the total length on both sides."""
-    rng = np.random.default_rng(9)
-    W, T0, D = 8, 8, 4
+def _rolling_window_vs_history(steps, S_of, W, T0, rng, use_offset=True, D=4):
+    """Chunks into a full W-slot cache (attention before the eviction drops
+    the keys early queries still see) vs the same chunks into a buffer long
+    enough to keep the whole history, with the same window mask and rotary
+    on throughout. The window cache's buffer row 0 holds absolute position
+    total - length, which is its position offset; the history buffer's is 0.
+    Returns the largest output difference and whether every kept row equals
+    the history's row at the same position, bit for bit."""
     small = tiny("fp32", B=2, S=1, H=4, Hkv=2, D=D, M=W, lens=(T0, 3), window=W, seed=2)
     big = small.copy()
-    big.max_seq_len = 96
+    big.max_seq_len = 160
     for name in ("k_cache", "v_cache"):
-        arr = np.zeros((2, 2, 96, D), np.uint32)
+        arr = np.zeros((2, 2, 160, D), np.uint32)
         arr[:, :, :W] = getattr(small, name)
         setattr(big, name, arr)
-    cos, sin = gi.rope_tables(96, D // 2)
+    cos, sin = gi.rope_tables(160, D // 2)
     for c in (small, big):
         c.cos, c.sin = cos, sin
     total = np.array([T0, 3])
-    for step in range(8):
-        S = int(rng.integers(2, W + 1))
+    worst, rows_equal = 0.0, True
+    for step in range(steps):
+        S = S_of(step)
         q = gi.to_bits(rng.standard_normal((2, S, 4 * D)), "fp32")
         k = gi.to_bits(rng.standard_normal((2, S, 2 * D)), "fp32")
         v = gi.to_bits(rng.standard_normal((2, S, 2 * D)), "fp32")
         for c in (small, big):
             c.new_tokens, c.q, c.k_new, c.v_new = S, q, k, v
-        # the small cache's rows start at total - lens: rotary positions must
-        # be the history's, so only compare while nothing was dropped before
-        # this step, or without rotary
-        rot = bool((total == small.seqlens_k).all())
-        for c in (small, big):
-            c.cos, c.sin = (cos, sin) if rot else (None, None)
-        s1, o1, kc1, vc1, l1 = O.gqa_attention(small)
-        s2, o2, kc2, vc2, l2 = O.gqa_attention(big)
+        small.position_offset = (total - small.seqlens_k).astype(np.int32) if use_offset else None
+        entry = "decode" if S == 1 else "prefill"
+        s1, o1, kc1, vc1, l1 = O.gqa_attention(small, entry)
+        s2, o2, kc2, vc2, l2 = O.gqa_attention(big, entry)
         assert s1 == s2 == O.OK
-        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+        worst = max(worst, float(np.abs(o1 - o2).max()))
         total = total + S
         assert l1.tolist() == np.minimum(total, W).tolist()
         for b in range(2):
             n = int(l1[b])
-            assert np.array_equal(kc1[b, :, :n], kc2[b, :, int(l2[b]) - n:int(l2[b])])
-            assert np.array_equal(vc1[b, :, :n], vc2[b, :, int(l2[b]) - n:int(l2[b])])
+            rows_equal &= bool(np.array_equal(kc1[b, :, :n], kc2[b, :, int(l2[b]) - n:int(l2[b])]))
+            rows_equal &= bool(np.array_equal(vc1[b, :, :n], vc2[b, :, int(l2[b]) - n:int(l2[b])]))
         small.k_cache, small.v_cache, small.seqlens_k = kc1, vc1, l1.astype(np.int32)
         big.k_cache, big.v_cache, big.seqlens_k = kc2, vc2, l2.astype(np.int32)
+    return worst, rows_equal
+
+
+def test_windowed_chunks_equal_full_history_window_attention():
+    """Rolling chunks of 2..W tokens into a full window cache, rotary on at
+    every step (absolute positions through the position offset): outputs
+    equal full-history window attention, and the kept rows are the history's
+    newest rows, rotated at the same positions, bit for bit."""
+    rng = np.random.default_rng(9)
+    W = 8
+    worst, rows_equal = _rolling_window_vs_history(8, lambda _: int(rng.integers(2, W + 1)), W, 8,
+                                                   np.random.default_rng(10))
+    assert worst <= 1e-13 and rows_equal
+
+
+def test_windowed_decode_with_rotary_equals_full_history():
+    """One-token steps into a full window cache (one row dropped per step),
+    rotary on: equal to full-history window attention at the same absolute
+    positions."""
+    worst, rows_equal = _rolling_window_vs_history(12, lambda _: 1, 6, 6, np.random.default_rng(12))
+    assert worst <= 1e-13 and rows_equal
+
+
+def test_dropping_the_position_offset_breaks_the_history_equivalence():
+    """Negative control for the two pins above: rotating at L_b + i alone
+    (no offset) once rows have been dropped rotates the new keys at wrong
+    positions, and the comparison with the history catches it."""
+    worst, rows_equal = _rolling_window_vs_history(6, lambda _: 1, 6, 6, np.random.default_rng(12),
+                                                   use_offset=False)
+    assert not rows_equal and worst > 1e-6
+
+
+def test_position_offset_validation():
+    base = tiny("fp16", S=2, M=12, lens=(3, 5), rotary=True, rotary_rows=20)
+    ok = base.copy()
+    ok.position_offset = np.array([0, 13], np.int32)           # 13 + 5 + 2 = 20 rows: fits
+    assert O.validate(ok, "prefill") == O.OK
+    over = base.copy()
+    over.position_offset = np.array([0, 14], np.int32)         # position 20 is past the table
+    assert O.validate(over, "prefill") == O.INVALID
+    neg = base.copy()
+    neg.position_offset = np.array([-1, 0], np.int32)
+    assert O.validate(neg, "prefill") == O.INVALID
+    short = base.copy()
+    short.position_offset = np.array([0], np.int32)            # not one per sequence
+    assert O.validate(short, "prefill") == O.INVALID
+    # an offset moves every rotary position by the same amount: the rotated K
+    # rows of (offset o, past L) are those of (offset 0, past L + o)
+    a = tiny("bf16", B=1, S=3, M=16, lens=(2,), rotary=True, rotary_rows=32, seed=5)
+    a.position_offset = np.array([7], np.int32)
+    b = a.copy()
+    b.position_offset = None
+    b.seqlens_k = np.array([9], np.int32)
+    assert np.array_equal(O.rotated_bits(a, a.k_new, 2), O.rotated_bits(b, b.k_new, 2))
 
 
 def test_present_mode_by_index_code_and_equals_shared_mode():
