@@ -9,7 +9,8 @@ package raises.
 
 The functions carry the C entry points' names:
   gqa_append_kv, gqa_attention_prefill, gqa_attention_decode,
-  gqa_attention_present, gqa_evict_window, gqa_workspace_bytes.
+  gqa_attention_present, gqa_evict_window, gqa_workspace_bytes,
+  gqa_attention_decode_noalloc.
 The attention functions also take separate present_key/present_value
 tensors (past and present in different buffers) and then call
 gqa_attention_present.
@@ -29,7 +30,9 @@ GQA_OK, GQA_ERR_NO_ROOM, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKS
 GQA_FP32, GQA_FP16, GQA_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "ok", 1: "no_room", 2: "invalid_arg", 3: "unsupported", 4: "workspace", 5: "hip"}
 EXPORTED = ("gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill", "gqa_attention_decode",
-            "gqa_attention_present", "gqa_evict_window", "gqa_status_string", "gqa_last_error")
+            "gqa_attention_present", "gqa_evict_window", "gqa_attention_decode_noalloc",
+            "gqa_status_string", "gqa_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20     # GQA_NOALLOC_SCRATCH_BYTES
 
 
 class GQAError(RuntimeError):
@@ -76,6 +79,9 @@ def _load() -> ctypes.CDLL:
                                           ctypes.c_int32, VP, VP, I32P, VP, VP, VP,
                                           ctypes.c_size_t, VP]
     lib.gqa_attention_present.restype = ctypes.c_int
+    lib.gqa_attention_decode_noalloc.argtypes = [P, ctypes.POINTER(Options), VP, VP, VP, VP, VP,
+                                                 I32P, VP, VP, VP]
+    lib.gqa_attention_decode_noalloc.restype = ctypes.c_int
     lib.gqa_evict_window.argtypes = [P, ctypes.c_int32, VP, VP, I32P, VP, I32P, VP, ctypes.c_size_t, VP]
     lib.gqa_evict_window.restype = ctypes.c_int
     lib.gqa_status_string.argtypes = [ctypes.c_int]
@@ -325,6 +331,40 @@ def gqa_attention_decode(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seql
                       seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
                       rotary_interleaved, present_key, present_value, workspace, stream,
                       greedy_eviction, attention_bias)
+
+
+def gqa_attention_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
+                                 out, *, scale=0.0, local_window_size=-1, cos_cache=None,
+                                 sin_cache=None, rotary_interleaved=False, greedy_eviction=False,
+                                 attention_bias=None, stream=None):
+    """gqa_attention_decode on the library's static device scratch: no
+    workspace, and nothing is allocated, here or in the library (`out` must
+    be given). Calls that overlap in time on one GPU race on the scratch."""
+    if out is None:
+        raise GQAError(GQA_ERR_INVALID_ARG, "out must be given (this entry point allocates nothing)")
+    _contig(q, k_new, v_new, k_cache, v_cache, out, cos_cache, sin_cache, attention_bias)
+    if q.dim() != 3 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.dim() != 3:
+        raise GQAError(GQA_ERR_INVALID_ARG, "q must be [B, 1, H*D], k_new/v_new [B, 1, Hkv*D]")
+    B, S, Hkv, M, D = _kv_common(k_new, k_cache, v_cache, None)
+    if int(q.shape[0]) != B or int(q.shape[1]) != S or int(q.shape[2]) % D:
+        raise GQAError(GQA_ERR_INVALID_ARG, "q must be [B, S, H*D] with the cache's D")
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise GQAError(GQA_ERR_INVALID_ARG, "out must match q")
+    if q.dtype != k_cache.dtype or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise GQAError(GQA_ERR_INVALID_ARG, "q, k_new, v_new and the caches must share a dtype")
+    _check_aux(B, D, k_cache.device, seqlens_k_dev, cos_cache, sin_cache, q, k_new, v_new,
+               v_cache, out, attention_bias)
+    if attention_bias is not None and (attention_bias.dtype != q.dtype or attention_bias.dim() != 4
+                                       or int(attention_bias.shape[2]) != S):
+        raise GQAError(GQA_ERR_INVALID_ARG, "attention_bias must be [B or 1, H or 1, S, T] in q's dtype")
+    shape = make_shape(B, S, int(q.shape[2]) // D, Hkv, D, M, dtype_code(q))
+    opts = make_options(scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
+                        greedy_eviction, attention_bias)
+    hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
+    _check(lib.gqa_attention_decode_noalloc(ctypes.byref(shape), ctypes.byref(opts), _ptr(q),
+                                            _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                            hp, _ptr(seqlens_k_dev), _ptr(out), _stream(stream)))
+    return out
 
 
 def gqa_evict_window(k_cache, v_cache, seqlens_k_host, seqlens_k_dev, incoming: int, *,

@@ -220,6 +220,33 @@ gqa_status windowed_chunk(const Problem& P, int max_drop, void* ws, const Worksp
   return GQA_OK;
 }
 
+// The layout of a call moved into the static scratch: counters into the
+// counter area, every other region after it (same order, same sizes).
+gqa_status static_layout(const WorkspaceLayout& lay, WorkspaceLayout* out) {
+  constexpr size_t half = kStaticCounterArea / 2;
+  if (lay.counters_bytes > half || lay.prefill_counters_bytes > half)
+    return fail(GQA_ERR_WORKSPACE, "the call needs %zu + %zu bytes of merge counters, the static "
+                "scratch holds %zu + %zu", lay.counters_bytes, lay.prefill_counters_bytes, half, half);
+  const size_t delta = kStaticCounterArea - lay.scratch;   // lay.scratch == lay.counters_bytes
+  const size_t need = lay.total + delta;
+  if (need > size_t(GQA_NOALLOC_SCRATCH_BYTES))
+    return fail(GQA_ERR_WORKSPACE, "the call needs %zu bytes of scratch, the static scratch holds "
+                "%zu", need, size_t(GQA_NOALLOC_SCRATCH_BYTES));
+  WorkspaceLayout s = lay;
+  s.counters = 0;
+  s.prefill_counters = half;
+  s.scratch += delta;
+  s.decode_halo += delta;
+  s.prefill_partials += delta;
+  if (s.stage_bytes) {
+    s.stage_k += delta;
+    s.stage_v += delta;
+  }
+  s.total = need;
+  *out = s;
+  return GQA_OK;
+}
+
 // The kernels of one validated call, on the workspace `ws` carved as `lay`.
 // S == 1 takes the split-KV decode route.
 gqa_status execute(const Problem& P, bool needs_evict, int max_drop, void* ws,
@@ -250,11 +277,13 @@ gqa_status execute(const Problem& P, bool needs_evict, int max_drop, void* ws,
 }
 
 // The whole op for one call: validation and the workspace check first (no
-// device call before both pass), then the kernels.
+// device call before both pass), then the kernels. With static_scratch the
+// workspace is the current device's static scratch instead of `ws`.
 gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options* opts,
                          const void* q, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, const int32_t* lens_host, const int32_t* lens_dev,
-                         void* out, void* ws, size_t ws_bytes, void* stream) {
+                         void* out, void* ws, size_t ws_bytes, void* stream,
+                         bool static_scratch = false) {
   g_err[0] = '\0';
   Problem P;
   bool needs_evict;
@@ -263,13 +292,39 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
                            lens_dev, out, &P, &needs_evict, &max_drop);
   if (st != GQA_OK) return st;
   WorkspaceLayout lay;
-  st = check_workspace(shape, P.window, ws, ws_bytes, &lay);
+  if (static_scratch) {
+    st = static_layout(workspace_layout(*shape, P.window), &lay);
+  } else {
+    st = check_workspace(shape, P.window, ws, ws_bytes, &lay);
+  }
   if (st != GQA_OK) return st;
   if (P.B == 0) return GQA_OK;
-  return execute(P, needs_evict, max_drop, ws, lay, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (!static_scratch) return execute(P, needs_evict, max_drop, ws, lay, hs);
+  StaticScratch sc;
+  st = static_scratch_begin(&sc);
+  if (st != GQA_OK) return st;
+  if (sc.clear) {
+    const hipError_t e = launch_zero(sc.ptr, kStaticCounterArea, hs);
+    if (e != hipSuccess) {
+      static_scratch_end(sc, GQA_ERR_HIP);
+      return hip_fail(e, "static scratch counter clear");
+    }
+  }
+  st = execute(P, needs_evict, max_drop, sc.ptr, lay, hs);
+  static_scratch_end(sc, st);
+  return st;
 }
 
 }  // namespace
+
+gqa_status set_error(gqa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
 
 WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   WorkspaceLayout l{};
@@ -469,5 +524,14 @@ const char* gqa_status_string(gqa_status s) {
 }
 
 const char* gqa_last_error(void) { return g_err; }
+
+gqa_status gqa_attention_decode_noalloc(const gqa_shape* shape, const gqa_options* opts,
+                                        const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache,
+                                        const int32_t* seqlens_k_host,
+                                        const int32_t* seqlens_k_dev, void* out, void* stream) {
+  return run_attention(kDecode, shape, opts, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
+                       seqlens_k_dev, out, nullptr, 0, stream, true);
+}
 
 }  // extern "C"

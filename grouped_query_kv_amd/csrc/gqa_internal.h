@@ -147,6 +147,35 @@ inline EvictGeometry evict_geometry(int row_bytes) {
 // S > 1 the layout includes the staging frames.
 WorkspaceLayout workspace_layout(const gqa_shape& s, int window);
 
+// The device scratch of gqa_attention_decode_noalloc: a static array of
+// GQA_NOALLOC_SCRATCH_BYTES per GPU. Its first kStaticCounterArea bytes hold
+// only merge counters (decode counters from 0, prefill split counters from
+// kStaticCounterArea / 2), zeroed once per device and left at zero by every
+// successful call; the other regions of a call's layout start at
+// kStaticCounterArea.
+constexpr size_t kStaticCounterArea = size_t(64) << 10;
+
+// The current device's static scratch for one call: its device address and
+// whether its counter area must be zeroed first (the device's first call,
+// or the first after a call that failed in a launch).
+struct StaticScratch {
+  int device = -1;
+  void* ptr = nullptr;
+  bool clear = false;
+};
+// Look up (once per device, with hipGetSymbolAddress) the scratch of the
+// current device. GQA_ERR_HIP if the device or the symbol is unavailable.
+gqa_status static_scratch_begin(StaticScratch* sc);
+// After the call's launches: a call that zeroed the counters leaves them
+// zero for the next one; a call that failed in a launch marks them dirty.
+void static_scratch_end(const StaticScratch& sc, gqa_status st);
+
+// Zero `bytes` (a multiple of 16) at `p` with a fill kernel on `st`.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+// Record a failure message for gqa_last_error() (printf-style).
+gqa_status set_error(gqa_status s, const char* fmt, ...);
+
 // Rows of the staging frame the windowed chunk path fills before attention:
 // key tiles of the attention kernels start at multiples of this, so every
 // row of a visited tile holds a real key.

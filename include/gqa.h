@@ -247,6 +247,31 @@ gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming,
                             int32_t* seqlens_after_host,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch behind gqa_attention_decode_noalloc
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define GQA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * gqa_attention_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, semantics, errors and
+ * kernels as gqa_attention_decode; the workspace is a static device array of
+ * GQA_NOALLOC_SCRATCH_BYTES on the current device, and nothing is allocated
+ * or freed. A call whose workspace (gqa_workspace_bytes of the shape, plus
+ * 64 KiB of merge counters) does not fit returns GQA_ERR_WORKSPACE before any
+ * launch: the decode workloads of up to 64 sequences with 8 KV heads and
+ * 4096-row fp16/bf16 buffers fit. Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that overlap in time on
+ * one GPU (two streams, two host threads) race and give undefined results.
+ * The first call on a device, and the first after a GQA_ERR_HIP, zeroes the
+ * array's counter area with a small kernel on `stream`.
+ */
+gqa_status gqa_attention_decode_noalloc(const gqa_shape* shape, const gqa_options* opts,
+                                        const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache,
+                                        const int32_t* seqlens_k_host,
+                                        const int32_t* seqlens_k_dev, void* out, void* stream);
+
 /* Static description of a status code. */
 const char* gqa_status_string(gqa_status status);
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(g):
     names = declared_functions()
     assert set(names) == {"gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill",
                           "gqa_attention_decode", "gqa_attention_present", "gqa_evict_window",
-                          "gqa_status_string", "gqa_last_error"}
+                          "gqa_attention_decode_noalloc", "gqa_status_string", "gqa_last_error"}
     assert set(names) == set(g.EXPORTED)
     lib = ctypes.CDLL(g.LIB_PATH)
     for n in names:
@@ -343,3 +343,45 @@ def test_misaligned_past_and_evict_buffers_are_rejected(g):
                                 after.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), FAKE, 1 << 30,
                                 None)
     assert st == g.GQA_ERR_INVALID_ARG and b"aligned" in g.lib.gqa_last_error()
+
+
+# --------------------------------------------------------------------------
+# the entry point without a workspace: validated before any device call
+# --------------------------------------------------------------------------
+
+def _noalloc(g, shape, lens, opts=None):
+    opts = opts or g.Options(0.0, -1, None, None, 0, 0)
+    hl = np.asarray(lens, np.int32)
+    return g.lib.gqa_attention_decode_noalloc(ctypes.byref(shape), ctypes.byref(opts), FAKE, FAKE,
+                                              FAKE, FAKE, FAKE,
+                                              hl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                              FAKE, FAKE, None)
+
+
+def test_noalloc_validates_like_decode(g):
+    assert _noalloc(g, _shape(g, S=2), (0, 0)) == g.GQA_ERR_INVALID_ARG       # one token only
+    assert _noalloc(g, _shape(g, S=1, M=16), (16, 0)) == g.GQA_ERR_NO_ROOM
+    assert _noalloc(g, _shape(g, S=1, D=257), (0, 0)) == g.GQA_ERR_INVALID_ARG
+    assert _noalloc(g, _shape(g, B=0, S=1), ()) == g.GQA_OK                   # nothing to do
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(g):
+    # a shape whose workspace exceeds the static scratch is refused with a
+    # message naming both sizes, before any device call
+    big = g.Shape(64, 1, 256, 32, 128, 8192, g.GQA_FP16)
+    need = g.lib.gqa_workspace_bytes(ctypes.byref(big), None)
+    assert need > g.NOALLOC_SCRATCH_BYTES
+    st = _noalloc(g, big, [0] * 64)
+    assert st == g.GQA_ERR_WORKSPACE
+    assert b"static scratch" in g.lib.gqa_last_error()
+
+
+@pytest.mark.parametrize("B,H,Hkv,M,dt,W", [(16, 32, 8, 4096, 1, -1), (8, 32, 8, 4096, 2, 4096),
+                                           (64, 32, 8, 4096, 1, -1)])
+def test_decode_workloads_fit_the_static_scratch(g, B, H, Hkv, M, dt, W):
+    # the split-KV and window decode workloads (and 64 sequences of 4096 rows)
+    # need less workspace than the static scratch holds, counters apart
+    shape = g.Shape(B, 1, H, Hkv, 128, M, dt)
+    opts = g.Options(0.0, W, None, None, 0, 0)
+    need = g.lib.gqa_workspace_bytes(ctypes.byref(shape), ctypes.byref(opts))
+    assert need + (64 << 10) <= g.NOALLOC_SCRATCH_BYTES
