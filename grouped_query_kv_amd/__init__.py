@@ -57,7 +57,8 @@ class Options(ctypes.Structure):
                 ("rotary_rows", ctypes.c_int32), ("rotary_interleaved", ctypes.c_int32),
                 ("greedy_eviction", ctypes.c_int32),
                 ("attention_bias", ctypes.c_void_p), ("bias_batch", ctypes.c_int32),
-                ("bias_heads", ctypes.c_int32), ("bias_total", ctypes.c_int32)]
+                ("bias_heads", ctypes.c_int32), ("bias_total", ctypes.c_int32),
+                ("position_offset_host", ctypes.c_void_p), ("position_offset_dev", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -179,16 +180,46 @@ def make_shape(B, S, H, Hkv, D, M, dtype) -> Shape:
 
 
 def make_options(scale=0.0, local_window_size=-1, cos_cache=None, sin_cache=None,
-                 rotary_interleaved=False, greedy_eviction=False, attention_bias=None) -> Options:
+                 rotary_interleaved=False, greedy_eviction=False, attention_bias=None,
+                 offsets=None) -> Options:
+    """`offsets`: None, or the (host array, device tensor) pair that
+    _position_offsets returns."""
     rows = int(cos_cache.shape[0]) if cos_cache is not None else 0
     bb = bh = bt = 0
     if attention_bias is not None:
         if attention_bias.dim() != 4:
             raise GQAError(GQA_ERR_INVALID_ARG, "attention_bias must be [B or 1, H or 1, S, T]")
         bb, bh, bt = (int(attention_bias.shape[i]) for i in (0, 1, 3))
+    oh = od = None
+    if offsets is not None:
+        oh, od = offsets[0].ctypes.data, _ptr(offsets[1])
     return Options(float(scale), int(local_window_size), _ptr(cos_cache), _ptr(sin_cache), rows,
                    int(bool(rotary_interleaved)), int(bool(greedy_eviction)), _ptr(attention_bias),
-                   bb, bh, bt)
+                   bb, bh, bt, oh, od)
+
+
+def _position_offsets(position_offset, position_offset_dev, B: int, device, allocate: bool = True):
+    """Host int32 [B] copy (kept alive by the caller through the call) and
+    the device tensor of the per-sequence position offsets, or None.
+
+    `position_offset` is the host copy (array-like or CPU tensor); the device
+    copy is `position_offset_dev` when given, else (allocate=True) a new
+    tensor made from the host copy."""
+    if position_offset is None:
+        if position_offset_dev is not None:
+            raise GQAError(GQA_ERR_INVALID_ARG, "position_offset_dev needs its host copy position_offset")
+        return None
+    host, _ = _host_lengths(position_offset, B)
+    if position_offset_dev is None:
+        if not allocate:
+            raise GQAError(GQA_ERR_INVALID_ARG, "give position_offset_dev (this entry point allocates nothing)")
+        position_offset_dev = _torch().from_numpy(host.copy()).to(device)
+    torch = _torch()
+    if (position_offset_dev.dtype != torch.int32 or position_offset_dev.numel() != B
+            or not position_offset_dev.is_contiguous() or position_offset_dev.device != device):
+        raise GQAError(GQA_ERR_INVALID_ARG,
+                       f"position_offset_dev must be a contiguous int32 tensor of {B} on {device}")
+    return host, position_offset_dev
 
 
 _workspaces = {}
@@ -227,7 +258,8 @@ def _kv_common(k_new, k_cache, v_cache, num_heads):
 
 def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev, *,
                   cos_cache=None, sin_cache=None, rotary_interleaved=False,
-                  present_key=None, present_value=None, stream=None):
+                  present_key=None, present_value=None, stream=None, position_offset=None,
+                  position_offset_dev=None):
     """Append S new rows per sequence at seqlens_k (rotary on K if tables given)."""
     _same_buffer(k_cache, present_key, "key")
     _same_buffer(v_cache, present_value, "value")
@@ -237,7 +269,8 @@ def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
     B, S, Hkv, M, D = _kv_common(k_new, k_cache, v_cache, None)
     _check_aux(B, D, k_cache.device, seqlens_k_dev, cos_cache, sin_cache, k_new, v_new, v_cache)
     shape = make_shape(B, S, Hkv, Hkv, D, M, dtype_code(k_cache))
-    opts = make_options(0.0, -1, cos_cache, sin_cache, rotary_interleaved)
+    offs = _position_offsets(position_offset, position_offset_dev, B, k_cache.device)
+    opts = make_options(0.0, -1, cos_cache, sin_cache, rotary_interleaved, offsets=offs)
     hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
     _check(lib.gqa_append_kv(ctypes.byref(shape), ctypes.byref(opts), _ptr(k_new), _ptr(v_new),
                              _ptr(k_cache), _ptr(v_cache), hp, _ptr(seqlens_k_dev), _stream(stream)))
@@ -246,7 +279,7 @@ def gqa_append_kv(k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
 def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev, out,
                scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
                present_key, present_value, workspace, stream, greedy_eviction=False,
-               attention_bias=None):
+               attention_bias=None, position_offset=None, position_offset_dev=None):
     past_k = past_v = None
     past_rows = 0
     if (present_key is None) != (present_value is None):
@@ -283,8 +316,9 @@ def _attention(fn, q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_
         if (attention_bias.dtype != q.dtype or attention_bias.dim() != 4
                 or int(attention_bias.shape[2]) != S):
             raise GQAError(GQA_ERR_INVALID_ARG, "attention_bias must be [B or 1, H or 1, S, T] in q's dtype")
+    offs = _position_offsets(position_offset, position_offset_dev, B, k_cache.device)
     opts = make_options(scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
-                        greedy_eviction, attention_bias)
+                        greedy_eviction, attention_bias, offs)
     hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
     if workspace is None:
         ws, nbytes = workspace_for(shape, q.device, opts)
@@ -309,7 +343,8 @@ def gqa_attention_prefill(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seq
                           out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
                           sin_cache=None, rotary_interleaved=False, present_key=None,
                           present_value=None, workspace=None, stream=None, greedy_eviction=False,
-                          attention_bias=None):
+                          attention_bias=None, position_offset=None,
+                          position_offset_dev=None):
     """The whole op for S >= 1 new tokens; returns out [B, S, H*D].
 
     With present_key/present_value in buffers other than k_cache/v_cache,
@@ -318,25 +353,29 @@ def gqa_attention_prefill(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seq
     return _attention(lib.gqa_attention_prefill, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
                       seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
                       rotary_interleaved, present_key, present_value, workspace, stream,
-                      greedy_eviction, attention_bias)
+                      greedy_eviction, attention_bias, position_offset,
+                      position_offset_dev)
 
 
 def gqa_attention_decode(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
                          out=None, *, scale=0.0, local_window_size=-1, cos_cache=None,
                          sin_cache=None, rotary_interleaved=False, present_key=None,
                          present_value=None, workspace=None, stream=None, greedy_eviction=False,
-                         attention_bias=None):
+                         attention_bias=None, position_offset=None,
+                         position_offset_dev=None):
     """The whole op for one new token per sequence; returns out [B, 1, H*D]."""
     return _attention(lib.gqa_attention_decode, q, k_new, v_new, k_cache, v_cache, seqlens_k_host,
                       seqlens_k_dev, out, scale, local_window_size, cos_cache, sin_cache,
                       rotary_interleaved, present_key, present_value, workspace, stream,
-                      greedy_eviction, attention_bias)
+                      greedy_eviction, attention_bias, position_offset,
+                      position_offset_dev)
 
 
 def gqa_attention_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seqlens_k_host, seqlens_k_dev,
                                  out, *, scale=0.0, local_window_size=-1, cos_cache=None,
                                  sin_cache=None, rotary_interleaved=False, greedy_eviction=False,
-                                 attention_bias=None, stream=None):
+                                 attention_bias=None, stream=None, position_offset=None,
+                                 position_offset_dev=None):
     """gqa_attention_decode on the library's static device scratch: no
     workspace, and nothing is allocated, here or in the library (`out` must
     be given). Calls that overlap in time on one GPU race on the scratch."""
@@ -358,8 +397,10 @@ def gqa_attention_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seqlens_k_ho
                                        or int(attention_bias.shape[2]) != S):
         raise GQAError(GQA_ERR_INVALID_ARG, "attention_bias must be [B or 1, H or 1, S, T] in q's dtype")
     shape = make_shape(B, S, int(q.shape[2]) // D, Hkv, D, M, dtype_code(q))
+    offs = _position_offsets(position_offset, position_offset_dev, B, k_cache.device,
+                             allocate=False)
     opts = make_options(scale, local_window_size, cos_cache, sin_cache, rotary_interleaved,
-                        greedy_eviction, attention_bias)
+                        greedy_eviction, attention_bias, offs)
     hl, hp = _host_lengths(seqlens_k_host, B)  # keep hl alive through the call
     _check(lib.gqa_attention_decode_noalloc(ctypes.byref(shape), ctypes.byref(opts), _ptr(q),
                                             _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),

@@ -10,6 +10,12 @@
 namespace gqa {
 namespace {
 
+// Rotary position of sequence b's first new token: the absolute position of
+// buffer row 0 (0 without offsets) plus the past length before any eviction.
+__device__ inline int rotary_base(const int32_t* lens, const int32_t* offs, int b, int M) {
+  return clamp_len(lens[b], 0, M) + (offs ? offs[b] : 0);
+}
+
 // Destination row of sequence b's first new token. With a window (cap > 0)
 // the buffer was just compacted, so the append starts at the rows it kept.
 __device__ inline int dest_base(const int32_t* lens, int b, int S, int M, int cap) {
@@ -43,8 +49,8 @@ __global__ void __launch_bounds__(256) copy_rows_kernel(const U* __restrict__ sr
 template <class T>
 __global__ void __launch_bounds__(256) rotary_rows_kernel(
     const typename T::bits* __restrict__ src, typename T::bits* __restrict__ dst,
-    const int32_t* __restrict__ lens, int B, int S, int Hkv, int D, int M,
-    const float* __restrict__ cosv, const float* __restrict__ sinv, int rot_rows,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ offs, int B, int S, int Hkv,
+    int D, int M, const float* __restrict__ cosv, const float* __restrict__ sinv, int rot_rows,
     int interleaved, int cap) {
   const int half = D / 2;
   const int64_t total = int64_t(B) * S * Hkv * half;
@@ -55,7 +61,7 @@ __global__ void __launch_bounds__(256) rotary_rows_kernel(
     const int g = int(r % Hkv); r /= Hkv;
     const int i = int(r % S);
     const int b = int(r / S);
-    const int pos = clamp_len(clamp_len(lens[b], 0, M) + i, 0, rot_rows - 1);
+    const int pos = clamp_len(rotary_base(lens, offs, b, M) + i, 0, rot_rows - 1);
     const int e1 = interleaved ? 2 * j : j;
     const int e2 = interleaved ? 2 * j + 1 : j + half;
     const int64_t s0 = ((int64_t(b) * S + i) * Hkv + g) * D;
@@ -109,9 +115,9 @@ template <class T>
 __global__ void __launch_bounds__(256) append_rows_vec_kernel(
     const uint16_t* __restrict__ k_src, uint16_t* __restrict__ k_dst,
     const uint16_t* __restrict__ v_src, uint16_t* __restrict__ v_dst,
-    const int32_t* __restrict__ lens, int B, int S, int Hkv, int D, int M,
-    const float* __restrict__ cosv, const float* __restrict__ sinv, int rot, int rot_rows,
-    int interleaved, int cap) {
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ offs, int B, int S, int Hkv,
+    int D, int M, const float* __restrict__ cosv, const float* __restrict__ sinv, int rot,
+    int rot_rows, int interleaved, int cap) {
   const int half = D / 2;
   const int cpr = D / 16;                         // threads per row: 16 elements each
   const int64_t total = int64_t(B) * S * Hkv * cpr;
@@ -134,7 +140,7 @@ __global__ void __launch_bounds__(256) append_rows_vec_kernel(
     const uint4 vx = *reinterpret_cast<const uint4*>(vs + o1);
     const uint4 vy = *reinterpret_cast<const uint4*>(vs + o2);
     if (rot) {
-      const int pos = clamp_len(clamp_len(lens[b], 0, M) + i, 0, rot_rows - 1);
+      const int pos = clamp_len(rotary_base(lens, offs, b, M) + i, 0, rot_rows - 1);
       const float* cr = cosv + int64_t(pos) * half + 8 * ch;   // pairs 8 ch .. 8 ch + 7
       const float* sr = sinv + int64_t(pos) * half + 8 * ch;
       const float4 c0 = *reinterpret_cast<const float4*>(cr);
@@ -194,7 +200,7 @@ hipError_t rotary_rows(const Problem& p, bool evicted, hipStream_t st) {
   const int64_t total = int64_t(p.B) * p.S * p.Hkv * (p.D / 2);
   hipLaunchKernelGGL(rotary_rows_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
                      static_cast<const Bits*>(p.k_new), static_cast<Bits*>(p.k_cache),
-                     p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,
+                     p.lens_dev, p.off_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot_rows,
                      p.interleaved, evicted ? p.cap : 0);
   return hipGetLastError();
 }
@@ -205,7 +211,7 @@ hipError_t append_rows_vec(const Problem& p, bool evicted, hipStream_t st) {
   hipLaunchKernelGGL(append_rows_vec_kernel<T>, dim3(grid_for(total)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(p.k_new), static_cast<uint16_t*>(p.k_cache),
                      static_cast<const uint16_t*>(p.v_new), static_cast<uint16_t*>(p.v_cache),
-                     p.lens_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot, p.rot_rows,
+                     p.lens_dev, p.off_dev, p.B, p.S, p.Hkv, p.D, p.M, p.cos, p.sin, p.rot, p.rot_rows,
                      p.interleaved, evicted ? p.cap : 0);
   return hipGetLastError();
 }

@@ -19,6 +19,7 @@ struct SimpleArgs {
   const void* v_cache;
   void* out;
   const int32_t* lens;
+  const int32_t* offs;   // absolute position of buffer row 0 (nullptr: 0)
   const float* cosv;
   const float* sinv;
   int B, S, H, Hkv, G, D, M, W;
@@ -49,7 +50,7 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(SimpleArgs a) {
   const Bits* qrow = static_cast<const Bits*>(a.q) + ((int64_t(b) * a.S + i) * a.H + h) * D;
   if (a.rot) {
     const int half = D / 2;
-    const int pos = clamp_len(L + i, 0, a.rot_rows - 1);
+    const int pos = clamp_len(L + (a.offs ? a.offs[b] : 0) + i, 0, a.rot_rows - 1);
     for (int j = lane; j < half; j += 64) {
       const int e1 = a.interleaved ? 2 * j : j;
       const int e2 = a.interleaved ? 2 * j + 1 : j + half;
@@ -114,7 +115,7 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(SimpleArgs a) {
 hipError_t launch_attention_simple(const Problem& p, hipStream_t st) {
   SimpleArgs a;
   a.q = p.q; a.k_cache = p.k_cache; a.v_cache = p.v_cache; a.out = p.out;
-  a.lens = p.lens_dev; a.cosv = p.cos; a.sinv = p.sin;
+  a.lens = p.lens_dev; a.offs = p.off_dev; a.cosv = p.cos; a.sinv = p.sin;
   a.B = p.B; a.S = p.S; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.D = p.D; a.M = p.M;
   a.W = p.window; a.cap = p.cap; a.rot = p.rot; a.rot_rows = p.rot_rows; a.interleaved = p.interleaved;
   a.scale_log2 = p.scale * kLog2e;

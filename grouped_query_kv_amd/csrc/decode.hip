@@ -104,6 +104,7 @@ struct DecodeArgs {
   const uint16_t* bias;                 // additive bias (b, h, column) at b bias_bs + h bias_hs + column
   int64_t bias_bs, bias_hs;
   int32_t hl[kDecodeArgBatch];          // past lengths
+  int32_t ro[kDecodeArgBatch];          // absolute position of buffer row 0 (rotary only)
   int32_t pb[kDecodeArgBatch + 1];      // first global block of sequence b (all its units)
 };
 
@@ -152,7 +153,7 @@ struct Blk {
   int b, g, ub, i, nb;
   int d;                   // fused eviction: key r is read from buffer row r + d
   int coff;                // bias column of key r: r + coff (its position before any eviction)
-  int L;                   // past length (the new token's rotary position)
+  int L;                   // rotary position of the new token: offset_b + past length
 };
 
 __device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) {
@@ -167,7 +168,7 @@ __device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) 
   k.kb = s.kstart + kKeys * k.i;
   k.d = s.d;
   k.coff = s.L - s.Lp;
-  k.L = s.L;
+  k.L = a.rot ? s.L + a.ro[k.b] : s.L;
 }
 
 __device__ inline Blk locate(const DecodeArgs& a, int64_t x, const SeqRegs& sr, int lane) {
@@ -886,6 +887,7 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
     const int kend = L + 1;
     const int kstart = p.window > 0 ? (kend - p.window > 0 ? kend - p.window : 0) : 0;
     a.hl[b] = p.lens_host[b];
+    a.ro[b] = p.off_host ? p.off_host[b] : 0;
     a.pb[b] = int32_t(total);
     total += int64_t((kend - kstart + kKeys - 1) / kKeys) * units_per_seq;
   }

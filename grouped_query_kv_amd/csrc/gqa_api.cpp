@@ -79,15 +79,24 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
   st = check_lengths(s, lens_host, lens_dev);
   if (st != GQA_OK) return st;
   const bool rot = o->cos_cache != nullptr || o->sin_cache != nullptr;
-  int maxlen = 0;
-  for (int b = 0; b < B; ++b) maxlen = std::max(maxlen, lens_host[b]);
+  const bool offsets = o->position_offset_host != nullptr || o->position_offset_dev != nullptr;
+  if (offsets && B > 0 && (!o->position_offset_host || !o->position_offset_dev))
+    return fail(GQA_ERR_INVALID_ARG,
+                "position_offset_host and position_offset_dev must be given together");
+  int64_t maxpos = 0;            // largest offset_b + L_b
+  for (int b = 0; b < B; ++b) {
+    const int64_t off = offsets ? o->position_offset_host[b] : 0;
+    if (off < 0)
+      return fail(GQA_ERR_INVALID_ARG, "position_offset[%d] = %lld < 0", b, (long long)off);
+    maxpos = std::max(maxpos, off + lens_host[b]);
+  }
   if (rot) {
     if (!o->cos_cache || !o->sin_cache)
       return fail(GQA_ERR_INVALID_ARG, "cos_cache and sin_cache must be given together");
     if (D % 2) return fail(GQA_ERR_INVALID_ARG, "rotary needs an even head_size (got %d)", D);
-    if (B > 0 && S > 0 && (int64_t)maxlen + S > (int64_t)o->rotary_rows)
-      return fail(GQA_ERR_INVALID_ARG, "rotary table has %d rows, positions reach %d",
-                  o->rotary_rows, maxlen + S - 1);
+    if (B > 0 && S > 0 && maxpos + S > (int64_t)o->rotary_rows)
+      return fail(GQA_ERR_INVALID_ARG, "rotary table has %d rows, positions reach %lld",
+                  o->rotary_rows, (long long)(maxpos + S - 1));
   }
   const bool work = B > 0 && S > 0;
   if (work) {
@@ -143,6 +152,8 @@ gqa_status validate(Entry entry, const gqa_shape* s, const gqa_options* o, const
   P.scale = o->scale != 0.0f ? o->scale : 1.0f / sqrtf((float)D);
   P.rot = rot; P.cos = o->cos_cache; P.sin = o->sin_cache; P.rot_rows = o->rotary_rows;
   P.interleaved = o->rotary_interleaved != 0;
+  P.off_host = offsets && B > 0 ? o->position_offset_host : nullptr;
+  P.off_dev = offsets && B > 0 ? o->position_offset_dev : nullptr;
   P.q = q; P.k_new = k_new; P.v_new = v_new; P.k_cache = k_cache; P.v_cache = v_cache;
   P.out = out; P.lens_dev = lens_dev; P.lens_host = lens_host;
   return GQA_OK;

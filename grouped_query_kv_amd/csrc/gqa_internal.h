@@ -23,6 +23,11 @@ struct Problem {
   const float* sin;
   int rot_rows;
   int interleaved;
+  // absolute position of each sequence's buffer row 0 (nullptr: 0); rotary
+  // positions are offset_b + L_b + i (host copy for planning, device copy
+  // for kernels that cannot take it in their arguments)
+  const int32_t* off_host = nullptr;
+  const int32_t* off_dev = nullptr;
   // tensors
   const void* q;
   const void* k_new;

@@ -126,6 +126,8 @@ struct PrefillArgs {
   float bias_mul;         // log2(e) / scale_log2 = 1 / |scale|: a bias in units of the raw scores
   int hl_ok;          // past lengths below are valid (B <= kPrefillArgBatch)
   int hl[kPrefillArgBatch];   // past lengths from the host (the same values as lens)
+  const int32_t* offs;        // absolute position of buffer row 0 (nullptr: 0), device
+  int ho[kPrefillArgBatch];   // the same from the host, valid with hl_ok
 };
 
 // The cos/sin values one lane needs for its row's 8 B-operand chunks; chunk
@@ -570,7 +572,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
     if (a.rot) {
-      const int pos = clamp_len(len_raw + my_i, 0, a.rot_rows - 1);
+      int off = 0;
+      if (a.hl_ok) {
+        off = a.ho[b];
+        asm volatile("" : "+s"(off));
+      } else if (a.offs) {
+        off = __builtin_amdgcn_readfirstlane(a.offs[b]);
+      }
+      const int pos = clamp_len(len_raw + off + my_i, 0, a.rot_rows - 1);
       RotVals rv;
       load_rot(rv, a.cosv + int64_t(pos) * (kD / 2), a.sinv + int64_t(pos) * (kD / 2), c,
                a.interleaved);
@@ -796,8 +805,12 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
   a.bias_bs = p.bias_bs; a.bias_hs = p.bias_hs; a.bias_T = p.bias_T;
   a.bias_mul = kLog2e / a.scale_log2;
   a.hl_ok = p.lens_host != nullptr && p.B <= kPrefillArgBatch;
+  a.offs = p.off_dev;
   if (a.hl_ok)
-    for (int b = 0; b < p.B; ++b) a.hl[b] = p.lens_host[b];
+    for (int b = 0; b < p.B; ++b) {
+      a.hl[b] = p.lens_host[b];
+      a.ho[b] = p.off_host ? p.off_host[b] : 0;
+    }
   a.n_items0 = a.n_rb * p.B * p.Hkv;
   if (a.n_items0 == 0) return hipSuccess;
   int blocks = a.n_items0;

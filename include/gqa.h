@@ -33,7 +33,8 @@
  *
  * Semantics of one attention call (prefill or decode):
  *   1. rotary (if cos/sin given) on Q (H heads) and K (Hkv heads) at
- *      positions L_b + i; pairs (j, j + D/2), or (2j, 2j+1) when
+ *      positions offset_b + L_b + i (offset_b = position_offset[b], 0 when
+ *      not given, L_b before any eviction); pairs (j, j + D/2), or (2j, 2j+1) when
  *      rotary_interleaved; each rotated value is the fp64 expression
  *      x1*c - x2*s (resp. x2*c + x1*s) rounded to fp32 then to dtype,
  *      both nearest-even (exact products, so the cache is reproducible
@@ -133,6 +134,15 @@ typedef struct gqa_options {
   int32_t bias_total;          /* T >= max_b (L_b + S): column j is the key at
                                   position j of past ++ new (before any
                                   eviction of this call) */
+  const int32_t* position_offset_host;  /* NULL: 0 for every sequence; else
+                                  [B] host: absolute position of sequence b's
+                                  buffer row 0 (>= 0); rotary positions are
+                                  offset_b + L_b + i, and offset_b + L_b + S
+                                  <= rotary_rows. A caller keeping a rolling
+                                  window adds each call's dropped count
+                                  (L_b + S - new length) to offset_b */
+  const int32_t* position_offset_dev;   /* the same values on the device;
+                                  given together with the host copy */
 } gqa_options;
 
 /*

@@ -44,6 +44,10 @@ class DevCase:
         self.bias = None
         if getattr(case, "attention_bias", None) is not None:
             self.bias = to_dev(case.attention_bias, dt, device)
+        self.off_host = self.off_dev = None
+        if getattr(case, "position_offset", None) is not None:
+            self.off_host = np.asarray(case.position_offset, np.int32).copy()
+            self.off_dev = torch.from_numpy(self.off_host.copy()).to(device)
         self.cos = self.sin = None
         if case.cos is not None:
             self.cos = torch.from_numpy(case.cos).to(device)
@@ -54,6 +58,11 @@ class DevCase:
         self.lens_host = np.asarray(lens, np.int32).copy()
         self.lens_dev = torch.from_numpy(self.lens_host.copy()).to(self.k_cache.device)
 
+    def set_offsets(self, offsets):
+        import torch
+        self.off_host = np.asarray(offsets, np.int32).copy()
+        self.off_dev = torch.from_numpy(self.off_host.copy()).to(self.k_cache.device)
+
     def run(self, entry="prefill", out=None, workspace=None):
         import grouped_query_kv_amd as gqa
         c = self.case
@@ -62,14 +71,16 @@ class DevCase:
                   self.lens_dev, out, scale=c.scale, local_window_size=c.local_window_size,
                   cos_cache=self.cos, sin_cache=self.sin, rotary_interleaved=c.rotary_interleaved,
                   workspace=workspace, greedy_eviction=bool(c.greedy_eviction),
-                  attention_bias=self.bias)
+                  attention_bias=self.bias, position_offset=self.off_host,
+                  position_offset_dev=self.off_dev)
 
     def append(self):
         import grouped_query_kv_amd as gqa
         c = self.case
         gqa.gqa_append_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.lens_host,
                           self.lens_dev, cos_cache=self.cos, sin_cache=self.sin,
-                          rotary_interleaved=c.rotary_interleaved)
+                          rotary_interleaved=c.rotary_interleaved, position_offset=self.off_host,
+                          position_offset_dev=self.off_dev)
 
     def caches(self):
         return to_bits(self.k_cache), to_bits(self.v_cache)

@@ -385,3 +385,40 @@ def test_decode_workloads_fit_the_static_scratch(g, B, H, Hkv, M, dt, W):
     opts = g.Options(0.0, W, None, None, 0, 0)
     need = g.lib.gqa_workspace_bytes(ctypes.byref(shape), ctypes.byref(opts))
     assert need + (64 << 10) <= g.NOALLOC_SCRATCH_BYTES
+
+
+# --------------------------------------------------------------------------
+# position offsets: validated against the rotary table before any launch
+# --------------------------------------------------------------------------
+
+def _with_offsets(g, host, dev=FAKE, rows=16, rot=True):
+    o = g.Options(0.0, -1, FAKE if rot else None, FAKE if rot else None, rows, 0)
+    keep = None
+    if host is not None:
+        keep = np.asarray(host, np.int32)
+        o.position_offset_host = keep.ctypes.data
+    o.position_offset_dev = dev
+    return o, keep
+
+
+@pytest.mark.parametrize("host,dev,lens,msg", [
+    ([0, 0], None, (0, 0), b"position_offset"),     # host copy without the device copy
+    (None, FAKE, (0, 0), b"position_offset"),       # device copy without the host copy
+    ([-1, 0], FAKE, (0, 0), b"position_offset"),    # negative
+    ([0, 11], FAKE, (2, 3), b"rotary table"),       # 11 + 3 + 3 = 17 > 16 table rows
+])
+def test_position_offset_validation(g, host, dev, lens, msg):
+    # (10 + 3 + 3 = 16 rows would fit; the oracle test below checks that
+    # boundary, since a valid call here would launch on dummy pointers)
+    o, keep = _with_offsets(g, host, dev)
+    st = _call(g, "prefill", _shape(g, S=3), o, lens=lens, ws=FAKE)
+    assert st == g.GQA_ERR_INVALID_ARG, g.lib.gqa_last_error()
+    assert msg in g.lib.gqa_last_error()
+
+
+def test_position_offset_rule_matches_oracle():
+    c = gi.make_case("x", "fp16", 2, 3, 4, 2, 8, 16, [2, 3], 0, rotary=True, rotary_rows=16)
+    c.position_offset = np.array([0, 10], np.int32)
+    assert O.validate(c, "prefill") == O.OK
+    c.position_offset = np.array([0, 11], np.int32)
+    assert O.validate(c, "prefill") == O.INVALID

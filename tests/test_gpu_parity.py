@@ -322,16 +322,20 @@ def test_attention_bias_decode_full_size():
 # the halves: append and eviction on their own
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dt,D,rot", [("fp16", 128, False), ("bf16", 64, True), ("fp32", 8, True),
-                                      ("fp16", 6, False)])
-def test_append_by_index_code(dt, D, rot):
+@pytest.mark.parametrize("dt,D,rot,offsets", [("fp16", 128, False, None), ("bf16", 64, True, None),
+                                              ("fp32", 8, True, None), ("fp16", 6, False, None),
+                                              ("bf16", 128, True, [9, 0, 24]),
+                                              ("fp32", 8, True, [3, 1, 2])])
+def test_append_by_index_code(dt, D, rot, offsets):
     B, S, Hkv, M = 3, 5, 2, 40
     case = gi.make_case("append", dt, B, S, 2 * Hkv, Hkv, D, M, [0, 17, 35], 3, rotary=rot,
-                        rotary_rows=M)
+                        rotary_rows=M + 24)
+    if offsets is not None:
+        case.position_offset = np.array(offsets, np.int32)
     code = np.arange(B * S * Hkv * D, dtype=np.float64).reshape(B, S, Hkv * D) % 1000
     case.k_new = gi.to_bits(code, dt)
     case.v_new = gi.to_bits(-code, dt)
-    say(f"[gpu] append {dt} D={D} rot={rot}")
+    say(f"[gpu] append {dt} D={D} rot={rot} offsets={offsets}")
     st, kc, vc = O.gqa_append_kv(case)
     dev = DevCase(case)
     dev.append()
@@ -406,7 +410,9 @@ def test_windowed_chunks_rolling(dt):
     B, H, Hkv, D, M = 4, 16, 4, 128, 1024
     lens = [1024, 1000, 600, 1024]
     case = gi.make_case("chunks", dt, B, 96, H, Hkv, D, M, lens, 12, window=M, rotary=True,
-                        rotary_rows=M + 4 * 128)
+                        rotary_rows=M + 4 * 128 + 300)
+    # buffer row 0 holds absolute position 300 + (rows the windows dropped before)
+    case.position_offset = np.array([300, 0, 17, 5], np.int32)
     dev = DevCase(case)
     ptr = dev.k_cache.data_ptr()
     for step in range(3):
@@ -427,9 +433,65 @@ def test_windowed_chunks_rolling(dt):
         nxt.q = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, H * D)), dt)
         nxt.k_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
         nxt.v_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        # the rows this step dropped move the absolute position of row 0
+        nxt.position_offset = (case.position_offset + case.seqlens_k + S - after).astype(np.int32)
         nxt.k_cache, nxt.v_cache, nxt.seqlens_k = kc, vc, after.astype(np.int32)
         case = nxt
         cache_k, cache_v = dev.k_cache, dev.v_cache
+        dev = DevCase(case)
+        dev.k_cache, dev.v_cache = cache_k, cache_v
+
+
+POSITION_OFFSETS = [
+    # dtype, B, H, Hkv, D, M, W, lens, chunk sizes per step, greedy
+    ("bf16", 3, 16, 4, 128, 256, 256, [256, 256, 100], [1, 1, 1, 1], 0),       # fused eviction decode
+    ("fp16", 2, 8, 2, 128, 300, 200, [300, 280], [1, 1, 1], 1),                # greedy, eviction kernel
+    ("fp16", 2, 28, 4, 128, 512, 512, [512, 400], [64, 1, 33, 1], 0),         # chunks and decodes
+    ("fp32", 2, 4, 2, 8, 40, 40, [40, 33], [1, 7, 1], 0),                      # plain kernel
+    ("bf16", 66, 4, 2, 128, 64, 64, [64 if i % 2 else (7 * i) % 60 for i in range(66)], [3, 1], 0),
+]
+
+
+@pytest.mark.parametrize("spec", POSITION_OFFSETS,
+                         ids=[f"{s[0]}-B{s[1]}-{i}" for i, s in enumerate(POSITION_OFFSETS)])
+def test_rolling_window_with_rotary_position_offsets(spec):
+    """Rolling steps into full window caches with rotary on throughout: row 0
+    of each buffer holds absolute position offset_b, which grows by the rows
+    each step drops, so new tokens keep rotating at their positions in the
+    whole history ([P2] para 1 positions with the sliding-window follow-up's
+    eviction). Every step against the oracle on the previous oracle state;
+    66 sequences take the prefill kernel's device-read offsets."""
+    dt, B, H, Hkv, D, M, W, lens, chunks, greedy = spec
+    seed = sum(map(ord, repr(spec))) % 1000
+    rng = np.random.default_rng(seed)
+    case = gi.make_case("offsets", dt, B, chunks[0], H, Hkv, D, M, lens, seed, window=W,
+                        rotary=True, rotary_rows=2000)
+    case.greedy_eviction = greedy
+    case.position_offset = rng.integers(0, 500, B).astype(np.int32)
+    dev = DevCase(case)
+    cache_k, cache_v = dev.k_cache, dev.v_cache
+    for step, S in enumerate(chunks):
+        entry = "decode" if S == 1 else "prefill"
+        say(f"[gpu] offsets {spec[:7]} step {step}: S={S} lens={case.seqlens_k.tolist()[:6]} "
+            f"offsets={case.position_offset.tolist()[:6]}")
+        st, want, kc, vc, after = O.gqa_attention(case, entry)
+        assert st == O.OK
+        out = dev.run(entry)
+        gk, gv = dev.caches()
+        assert_bits_equal(gk, kc, f"offsets step {step} k_cache")
+        assert_bits_equal(gv, vc, f"offsets step {step} v_cache")
+        err = assert_close(out_f64(out, dt), want, dt, f"offsets step {step}")
+        say(f"[gpu]   max abs error {err:.3e}")
+        if step + 1 == len(chunks):
+            break
+        nxt = case.copy()
+        nxt.new_tokens = chunks[step + 1]
+        nxt.q = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, H * D)), dt)
+        nxt.k_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        nxt.v_new = gi.to_bits(rng.standard_normal((B, nxt.new_tokens, Hkv * D)), dt)
+        nxt.position_offset = (case.position_offset + case.seqlens_k + S - after).astype(np.int32)
+        nxt.k_cache, nxt.v_cache, nxt.seqlens_k = kc, vc, after.astype(np.int32)
+        case = nxt
         dev = DevCase(case)
         dev.k_cache, dev.v_cache = cache_k, cache_v
 
@@ -627,6 +689,10 @@ def _random_case(k):
         Hb = G * Hkv if rng.random() < 0.5 else 1
         case.attention_bias = gi.to_bits(rng.standard_normal((Bb, Hb, S, T)), dt)
     present_rows = int(max(lens)) + int(rng.integers(0, 8)) if rng.random() < 0.25 else None
+    orng = np.random.default_rng(5000 + k)     # own generator: the draws above stay as they were
+    if rot and orng.random() < 0.5:
+        case.position_offset = orng.integers(0, 40, B).astype(np.int32)
+        case.cos, case.sin = gi.rope_tables(M + S + 40, D // 2)
     return case, present_rows
 
 
@@ -639,6 +705,7 @@ def test_random_feature_combinations(k):
             f"Hkv={case.kv_num_heads} D={case.head_size} M={case.max_seq_len} W={case.local_window_size} "
             f"greedy={case.greedy_eviction} rot={case.cos is not None} "
             f"bias={None if case.attention_bias is None else case.attention_bias.shape} "
+            f"offsets={None if case.position_offset is None else case.position_offset.tolist()} "
             f"present={present_rows} lens={list(case.seqlens_k)}")
     if present_rows is None:
         check_full(case, entry, desc)
@@ -657,7 +724,8 @@ def test_random_feature_combinations(k):
              dev.lens_host, dev.lens_dev, scale=case.scale, local_window_size=case.local_window_size,
              cos_cache=dev.cos, sin_cache=dev.sin, rotary_interleaved=case.rotary_interleaved,
              present_key=dev.k_cache, present_value=dev.v_cache,
-             greedy_eviction=bool(case.greedy_eviction), attention_bias=dev.bias)
+             greedy_eviction=bool(case.greedy_eviction), attention_bias=dev.bias,
+             position_offset=dev.off_host, position_offset_dev=dev.off_dev)
     gk, gv = dev.caches()
     assert_bits_equal(gk, kc, f"{desc} present k")
     assert_bits_equal(gv, vc, f"{desc} present v")
