@@ -304,13 +304,40 @@ def device_info(torch):
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(case, budget_s=12.0):
-    from oracle import gqa_oracle as O
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        blas = 1
+        return 1
+
+
+def cpu_baseline_prefill(case, nb=1):
+    """The fp64 oracle on the first `nb` sequences of the causal prefill
+    (all heads, all 2048 new tokens): TFLOP/s over the causal pairs it
+    computes (the oracle itself works on the dense masked matrix)."""
+    from oracle import gqa_oracle as O
+    sub = case.copy()
+    sub.batch = nb
+    for f in ("seqlens_k", "q", "k_new", "v_new", "k_cache", "v_cache"):
+        setattr(sub, f, getattr(case, f)[:nb].copy())
+    t0 = time.perf_counter()
+    st, out, *_ = O.gqa_attention(sub, "prefill")
+    el = time.perf_counter() - t0
+    assert st == O.OK
+    fl = prefill_flops(sub)
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, causal prefill of the first {nb} of {case.batch} "
+                       f"sequences (S=2048, 32 heads, rotary), one run of {el:.1f} s, "
+                       f"{fl:.3e} causal-pair flop; {len(os.sched_getaffinity(0))} host cores "
+                       f"visible, {blas_threads()} BLAS threads; "
+                       f"{platform.processor() or platform.machine()}")}
+
+
+def cpu_baseline(case, budget_s=12.0):
+    from oracle import gqa_oracle as O
+    blas = blas_threads()
     nb = 4
     sub = case.copy()
     sub.batch = nb
@@ -427,13 +454,26 @@ def main():
         st = stats(d, p_)
         att = decode_bytes(win, [4095] * 8, window=4096)
         shift = 8 * 8 * 4095 * 128 * 2 * 2 * 2      # read + write of every kept row, K and V
+        del sets
+        torch.cuda.empty_cache()
+        # attention alone: the same shapes one row short of full (4095 past
+        # rows), so the step appends at row 4095 and attends over 4096 keys
+        # without moving anything
+        att_case = gi.workload("window-decode-bf16")
+        att_case.seqlens_k = np.full(8, 4095, np.int32)
+        w2, st2 = run_leg(torch, "window decode, attention only", att_case, decode_call(gqa),
+                          args.steps, args.warmup)
         extra["window_decode"] = {
             "workload": "bf16 sliding-window decode B=8 H=32 Hkv=8 D=128 M=W=4096, full cache",
             "step_gbs_vs_fused_minimum": (att + shift // 2) / (st["mean_ms"] * 1e-3) / 1e9,
             "step_bytes_unfused": att + shift, "attention_bytes": att,
-            "ms_per_call_wall": w, **st}
-        del sets
-        torch.cuda.empty_cache()
+            "ms_per_call_wall": w, **st,
+            "attention_only": {
+                "workload": "the same shapes with 4095 past rows: append at row 4095, attend over "
+                            "4096 keys, no eviction",
+                "gbs": att / (st2["mean_ms"] * 1e-3) / 1e9,
+                "frac_hbm_peak": att / (st2["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "ms_per_call_wall": w2, **st2}}
 
     if "chunks" in which:
         # chunks of 128 tokens into the full window caches: attention over
@@ -522,6 +562,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
         cpu = cpu_baseline(dec)
+        if "causal_prefill" in extra:
+            log("[bench] CPU baseline of the causal prefill (oracle)")
+            extra["causal_prefill"]["cpu_baseline"] = cpu_baseline_prefill(
+                gi.workload("causal-prefill-bf16"))
 
     line = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

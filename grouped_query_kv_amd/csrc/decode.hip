@@ -153,7 +153,7 @@ struct Blk {
   int b, g, ub, i, nb;
   int d;                   // fused eviction: key r is read from buffer row r + d
   int coff;                // bias column of key r: r + coff (its position before any eviction)
-  int L;                   // rotary position of the new token: offset_b + past length
+  int L;                   // past length (with the sequence's position offset: the rotary position)
 };
 
 __device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) {
@@ -168,7 +168,7 @@ __device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) 
   k.kb = s.kstart + kKeys * k.i;
   k.d = s.d;
   k.coff = s.L - s.Lp;
-  k.L = a.rot ? s.L + a.ro[k.b] : s.L;
+  k.L = s.L;
 }
 
 __device__ inline Blk locate(const DecodeArgs& a, int64_t x, const SeqRegs& sr, int lane) {
@@ -280,8 +280,8 @@ struct Q4 {
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <bool kBias>
-__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, int worker,
-                             bool slice_end, bool spare = false) {
+__device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end,
+                             bool spare = false) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
   // fused eviction: key `row` is buffer row row + d. The first row of the
   // next block's sources is overwritten by that block's shifted stores. When
@@ -292,7 +292,10 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, i
   int src = row + k.d;
   const bool halo = k.d && slice_end && n == kKeys - 1 && k.i + 1 < k.nb;
   src = src < a.M ? src : row;
-  const int64_t hrow = int64_t(worker) * kD + 8 * q4;      // the slice's halo row
+  // the slice's halo row, at its wave's index in the launch (recomputed
+  // here rather than kept live through the stream)
+  const int worker = int(blockIdx.x) * kDecodeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t hrow = int64_t(worker) * kD + 8 * q4;
   const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
   const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * kD + 8 * q4;
   // a spare load (the pipeline's refill past the slice's last block) reads
@@ -369,7 +372,7 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
     const uint16_t* vn = a.v_new + kvrow;
     r.k0 = ld16(kn); r.k1 = ld16(kn + 32); r.k2 = ld16(kn + 64); r.k3 = ld16(kn + 96);
     if (a.rot) {
-      const int pos = clamp_len(k.L, 0, a.rot_rows - 1);
+      const int pos = clamp_len(k.L + a.ro[k.b], 0, a.rot_rows - 1);
       rotate4<T>(r.k0, r.k1, r.k2, r.k3, q4, a.cosv + int64_t(pos) * (kD / 2),
                  a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
     }
@@ -549,7 +552,7 @@ __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, 
   const int hg = k.ub % a.n_hg;
   const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
   if (a.rot) {
-    const int pos = clamp_len(k.L, 0, a.rot_rows - 1);
+    const int pos = clamp_len(k.L + a.ro[k.b], 0, a.rot_rows - 1);
     rotate4<T>(q.c0, q.c1, q.c2, q.c3, q4, a.cosv + int64_t(pos) * (kD / 2),
                a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
   }
@@ -672,7 +675,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   if (S < E) {
     Blk cur = locate(a, S, sr, lane);
     Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
-    KV rc = load_kv<kBias>(a, cur, n, q4, worker, S + 1 >= E);
+    KV rc = load_kv<kBias>(a, cur, n, q4, S + 1 >= E);
     Acc s;
     acc_reset(s);
     bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
@@ -683,7 +686,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // spare ones. Q rows are loaded when their unit starts (a small,
     // cache-resident read).
     Blk nxt = S + 1 < E ? next_block(a, cur, sr) : cur;        // block x + 1
-    KV r1 = load_kv<kBias>(a, nxt, n, q4, worker, S + 2 >= E);
+    KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
     Blk ahead = S + 2 < E ? next_block(a, nxt, sr) : nxt;       // block x + 2
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
@@ -691,7 +694,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv<kBias>(a, ahead, n, q4, worker, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
+      r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
       compute<T, kBias>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
