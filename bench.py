@@ -47,11 +47,11 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "0d68b7a1d322793e6ac15af377cc66d82f90816fa976746d60d8ff99c0b9787b",
+                "9fccd59c2fc68d4a0fa7de9eead22f318d67013df0441f63cc7579957d8128d6",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "99ab9293511c96fd9c6ed6c19350b91f1b11766870f6c5957417cdc6bbd1ec4e"},
-    "fetch_kib": 74156.510, "write_kib": 1050.281,
-    "fetch_scale": 524288.0 / 262156.825, "write_scale": 1.0,
+                "6260f8ffec745efa6e63541d2973d809e78a61e935af173068a60613b61419cb"},
+    "fetch_kib": 74132.510, "write_kib": 1050.281,
+    "fetch_scale": 524288.0 / 262157.15, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
 MIN_ROTATION_BYTES = 1 << 30
