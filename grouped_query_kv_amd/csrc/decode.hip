@@ -562,14 +562,36 @@ __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, 
   return q;
 }
 
+// A workgroup's table entry: a unit one of its waves holds only in part
+// (from the start of its slice, or to its end), with what its combine and
+// merge need. Written at the start of the slice, read after it.
+enum { kEntUnit, kEntB, kEntH0, kEntHeads, kEntWFirst, kEntWLast, kEntInts = 8 };
+
+struct EntInfo {
+  int unit, b, h0, nheads, w_first, w_last;
+};
+
+// One LDS round trip; every lane reads the same words (wave-uniform values).
+__device__ inline EntInfo read_entry(const int* ent) {
+  const int4 x = *reinterpret_cast<const int4*>(ent);
+  const int2 y = *reinterpret_cast<const int2*>(ent + 4);
+  EntInfo u;
+  u.unit = __builtin_amdgcn_readfirstlane(x.x);
+  u.b = __builtin_amdgcn_readfirstlane(x.y);
+  u.h0 = __builtin_amdgcn_readfirstlane(x.z);
+  u.nheads = __builtin_amdgcn_readfirstlane(x.w);
+  u.w_first = __builtin_amdgcn_readfirstlane(y.x);
+  u.w_last = __builtin_amdgcn_readfirstlane(y.y);
+  return u;
+}
+
 // Merge the workgroup partials of a unit (slots wg_first + unit .. wg_last +
 // unit) by log-sum-exp, write the output and reset the unit's counter. All
 // threads of the workgroup; `lds` holds 2 kMergeMax x 16 floats.
 template <class T>
-__device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds,
-                                  const SeqRegs& sr) {
+__device__ inline void merge_unit(const DecodeArgs& a, const EntInfo& u, float* lds) {
   const int tid = threadIdx.x;
-  const UnitInfo u = unit_info(a, b, ub, sr);
+  const int b = u.b;
   const int wg_first = u.w_first / kDecodeWaves, wg_last = u.w_last / kDecodeWaves;
   const int count = wg_last - wg_first + 1;
   const float* base = a.partials + int64_t(wg_first + u.unit) * kSlotFloats;
@@ -642,13 +664,29 @@ __device__ inline void merge_unit(const DecodeArgs& a, int b, int ub, float* lds
   if (tid == 0) __hip_atomic_store(a.counters + u.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Entry `ent` of this wave: unit of block k when `on`, else empty.
+__device__ inline void set_entry(const DecodeArgs& a, int* ent, bool on, const Blk& k,
+                                 const SeqRegs& sr, int lane) {
+  if (on) {
+    const UnitInfo u = unit_info(a, k.b, k.ub, sr);
+    if (lane == 0) {
+      ent[kEntUnit] = u.unit; ent[kEntB] = k.b; ent[kEntH0] = u.h0; ent[kEntHeads] = u.nheads;
+      ent[kEntWFirst] = u.w_first; ent[kEntWLast] = u.w_last;
+    }
+  } else if (lane == 0) {
+    ent[kEntUnit] = -1;
+  }
+}
+
 // One launch: workgroups of kDecodeWaves waves; every wave of the grid
 // streams its own slice (see the top of the file), then the workgroup
 // combines the partials its waves left.
 template <class T, bool kBias>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
-  __shared__ int sh_tab[kDecodeWaves][2][2];        // per wave, slot: (b, ub) or b = -1
+  // per wave, entries 2 wv (its first unit, partial in slot 0) and 2 wv + 1
+  // (its last unit, partial in slot 1)
+  __shared__ __attribute__((aligned(16))) int sh_ent[2 * kDecodeWaves][kEntInts];
   __shared__ int sh_flag[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -659,7 +697,6 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   float* slot0 = reinterpret_cast<float*>(lds + wv * kWaveLds);
   float* slot1 = reinterpret_cast<float*>(lds + wv * kWaveLds + kSlotBytes);
   unsigned char* vt = lds + wv * kWaveLds + kSlotBytes;     // the V tile while streaming
-  if (lane < 4) sh_tab[wv][lane >> 1][lane & 1] = -1;
   const SeqRegs sr = load_seq_regs(a, lane);
 
   int64_t S = 0, E = 0;
@@ -672,9 +709,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       E = (int64_t(worker + 1) * a.total) / a.workers;
     }
   }
-  if (S < E) {
+  if (S >= E) {
+    set_entry(a, sh_ent[2 * wv], false, Blk{}, sr, lane);
+    set_entry(a, sh_ent[2 * wv + 1], false, Blk{}, sr, lane);
+  } else {
     Blk cur = locate(a, S, sr, lane);
-    Q4 qv = finish_q<T>(load_q_raw(a, cur, lane), a, cur, lane);
+    const Q4 qraw = load_q_raw(a, cur, lane);
     KV rc = load_kv<kBias>(a, cur, n, q4, S + 1 >= E);
     Acc s;
     acc_reset(s);
@@ -689,6 +729,20 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
     Blk ahead = S + 2 < E ? next_block(a, nxt, sr) : nxt;       // block x + 2
 
+    // While the first loads are in flight: this wave's table entries. Its
+    // first unit leaves a partial (slot 0) if it began in an earlier slice
+    // and ends inside this one; its last unit (slot 1) if it goes on past
+    // the slice, or if it is also the first and began earlier. The
+    // segment-closing code below writes exactly these slots.
+    {
+      const Blk lb = S + 1 < E ? locate(a, E - 1, sr, lane) : cur;
+      const bool same = lb.b == cur.b && lb.ub == cur.ub;
+      const bool open_end = lb.i + 1 < lb.nb;
+      set_entry(a, sh_ent[2 * wv], cur.i > 0 && !same, cur, sr, lane);
+      set_entry(a, sh_ent[2 * wv + 1], same ? (cur.i > 0 || open_end) : open_end, lb, sr, lane);
+    }
+    Q4 qv = finish_q<T>(qraw, a, cur, lane);
+
     // one block: issue the loads of x + 2, compute x, close the segment at a
     // unit end or at the slice end. Returns false after the slice's last block.
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
@@ -701,10 +755,6 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
         if (shared) {
           // the slice's last segment goes to slot 1 (over the V tile, free now)
           finish_segment<T>(a, s, cur, true, last ? slot1 : slot0, lane);
-          if (lane == 0) {
-            sh_tab[wv][last ? 1 : 0][0] = cur.b;
-            sh_tab[wv][last ? 1 : 0][1] = cur.ub;
-          }
         } else {
           finish_segment<T>(a, s, cur, false, slot0, lane);
         }
@@ -727,45 +777,47 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- combine the partials of each cut unit in slice order. The table
-  // is read once (one LDS round trip); entries of a unit are consecutive in
-  // slice order (empty entries between them are skipped). ----
-  // every lane reads the same entries: mark them wave-uniform, so that the
-  // per-sequence arguments they index are scalar reads, not vector loads
-  // from the argument block that wait a full memory round trip
-  int tb[2 * kDecodeWaves], tu[2 * kDecodeWaves];
+  // ---- combine the partials of each cut unit. Entries of a unit are
+  // consecutive in slice order (empty entries between them are skipped).
+  // This runs once per workgroup after its slowest wave, so it is kept to
+  // scalar masks and the reads each unit needs: the entries were filled in
+  // at the start of the slices. ----
+  int key[2 * kDecodeWaves];                  // unit of each entry, -1 if empty
 #pragma unroll
-  for (int f = 0; f < 2 * kDecodeWaves; ++f) {
-    tb[f] = __builtin_amdgcn_readfirstlane(sh_tab[f >> 1][f & 1][0]);
-    tu[f] = __builtin_amdgcn_readfirstlane(sh_tab[f >> 1][f & 1][1]);
+  for (int f = 0; f < 2 * kDecodeWaves; ++f) key[f] = __builtin_amdgcn_readfirstlane(sh_ent[f][kEntUnit]);
+  uint32_t firsts = 0;                        // first entry of each unit
+  {
+    int lastk = -1;
+#pragma unroll
+    for (int f = 0; f < 2 * kDecodeWaves; ++f) {
+      if (key[f] >= 0 && key[f] != lastk) firsts |= 1u << f;
+      lastk = key[f] >= 0 ? key[f] : lastk;
+    }
   }
-  int nglob = 0, gb0 = 0, gub0 = 0, gb1 = 0, gub1 = 0;
-  int gunit0 = 0, gunit1 = 0, gneed0 = 0, gneed1 = 0;   // counter index, earlier arrivals
-  int prev_b = -1, prev_ub = -1;
+  int nglob = 0, gent0 = 0, gent1 = 0;        // entries of the units counted in (at most two)
+  while (firsts) {
+    const int e = __builtin_ctz(firsts);
+    firsts &= firsts - 1;
+    const EntInfo u = read_entry(sh_ent[e]);
+    uint32_t um = 0;                          // this unit's entries
 #pragma unroll
-  for (int e = 0; e < 2 * kDecodeWaves; ++e) {
-    const int b = tb[e], ub = tu[e];
-    if (b < 0 || (b == prev_b && ub == prev_ub)) continue;   // empty, or not a unit's first entry
-    prev_b = b; prev_ub = ub;
-    const UnitInfo u = unit_info(a, b, ub, sr);
+    for (int f = 0; f < 2 * kDecodeWaves; ++f) um |= (key[f] == u.unit ? 1u : 0u) << f;
     const bool inside = u.w_first >= wg * kDecodeWaves && u.w_last < (wg + 1) * kDecodeWaves;
     float* gslot = a.partials + int64_t(wg + u.unit) * kSlotFloats;
     for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
       const int h = idx / kD, d = idx % kD;
-      // every entry of this unit: its m, l and o, loaded together
       float m[2 * kDecodeWaves], l[2 * kDecodeWaves], o[2 * kDecodeWaves];
 #pragma unroll
       for (int f = 0; f < 2 * kDecodeWaves; ++f) {
-        // loaded unconditionally (every slot lies inside the workgroup's LDS)
-        // and selected after: no branch per entry, all reads in flight at once
-        const bool mine = f >= e && tb[f] == b && tu[f] == ub;
-        const float* sl = reinterpret_cast<const float*>(lds + (f >> 1) * kWaveLds + (f & 1) * kSlotBytes);
-        const float mv = sl[kDecodeMaxHG * kD + h];
-        const float lv = sl[kDecodeMaxHG * kD + kDecodeMaxHG + h];
-        const float ov = sl[h * kD + d];
-        m[f] = mine ? mv : -INFINITY;
-        l[f] = mine ? lv : 0.f;
-        o[f] = mine ? ov : 0.f;
+        m[f] = -INFINITY;
+        l[f] = 0.f;
+        o[f] = 0.f;
+        if (um & (1u << f)) {                 // wave-uniform
+          const float* sl = reinterpret_cast<const float*>(lds + (f >> 1) * kWaveLds + (f & 1) * kSlotBytes);
+          m[f] = sl[kDecodeMaxHG * kD + h];
+          l[f] = sl[kDecodeMaxHG * kD + kDecodeMaxHG + h];
+          o[f] = sl[h * kD + d];
+        }
       }
       float M = -INFINITY;
 #pragma unroll
@@ -778,7 +830,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
         O = fmaf(o[f], wgt, O);
       }
       if (inside) {
-        store_out<T>(a, b, u.h0 + h, d, O / L);
+        store_out<T>(a, u.b, u.h0 + h, d, O / L);
       } else {
         __hip_atomic_store(gslot + h * kD + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) {
@@ -789,9 +841,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       }
     }
     if (!inside) {
-      const int need = u.w_last / kDecodeWaves - u.w_first / kDecodeWaves;
-      if (nglob == 0) { gb0 = b; gub0 = ub; gunit0 = u.unit; gneed0 = need; }
-      else { gb1 = b; gub1 = ub; gunit1 = u.unit; gneed1 = need; }
+      if (nglob == 0) gent0 = e;
+      else gent1 = e;
       ++nglob;
     }
   }
@@ -807,16 +858,19 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (tid < nglob) {
     // counted in; the workgroup that completes the count merges
-    const int prev = __hip_atomic_fetch_add(a.counters + (tid ? gunit1 : gunit0), 1,
-                                            __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == (tid ? gneed1 : gneed0);
+    const int* ent = sh_ent[tid ? gent1 : gent0];
+    const int need = ent[kEntWLast] / kDecodeWaves - ent[kEntWFirst] / kDecodeWaves;
+    const int prev = __hip_atomic_fetch_add(a.counters + ent[kEntUnit], 1, __ATOMIC_RELEASE,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == need;
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     sh_flag[tid] = last;
   }
   __syncthreads();
   float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
-  if (sh_flag[0]) merge_unit<T>(a, gb0, gub0, mlds, sr);
-  if (nglob > 1 && sh_flag[1]) merge_unit<T>(a, gb1, gub1, mlds, sr);
+#pragma unroll 1
+  for (int j = 0; j < nglob; ++j)                     // one copy of the merge code
+    if (sh_flag[j]) merge_unit<T>(a, read_entry(sh_ent[j ? gent1 : gent0]), mlds);
 }
 
 // Fused eviction, before the decode kernel: for the last block i of every
