@@ -165,38 +165,46 @@ __device__ __forceinline__ float rot_entry(const RotVals& r, int i, bool sine) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
-// Rotate one row's 8 B-operand chunks in place with the loaded values.
+// Rotate one row's 8 B-operand chunks in place with the loaded values, in
+// fp32: each output is a fused multiply-add on the rounded other product,
+// then nearest-even to the dtype. Q only enters the scores, so this
+// rounding (at most one fp32 ulp from the exact expression before the
+// dtype rounding) shows only in the outputs, which are held to their
+// tolerance; K rows written to the cache use the exact rule of
+// rotate_pair. The fp64 form here was about a third of each workgroup's
+// start (fp64 conversions run at a quarter of the fp32 rate).
 template <class T>
-__device__ __forceinline__ void apply_rot(uint4 (&qv)[8], const RotVals& r, int interleaved) {
+__device__ __forceinline__ void apply_rot_q(uint4 (&qv)[8], const RotVals& r, int interleaved) {
   using Bits = typename T::bits;
-  auto get = [&](int ks, int e) -> Bits {
-    const uint32_t w = (&qv[ks].x)[e >> 1];
-    return Bits((w >> (16 * (e & 1))) & 0xFFFFu);
-  };
-  auto put = [&](int ks, int e, Bits v) {
-    uint32_t& w = (&qv[ks].x)[e >> 1];
-    const int sh = 16 * (e & 1);
-    w = (w & ~(0xFFFFu << sh)) | (uint32_t(v) << sh);
-  };
+  auto lo = [](uint32_t w) { return T::to_float(Bits(w & 0xFFFFu)); };
+  auto hi = [](uint32_t w) { return T::to_float(Bits(w >> 16)); };
   if (!interleaved) {
+    // pairs (chunk ks element e, chunk ks + 4 element e): two per word
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Bits x = get(ks, e), y = get(ks + 4, e);
-        rotate_pair<T>(x, y, rot_entry(r, 8 * ks + e, false), rot_entry(r, 8 * ks + e, true));
-        put(ks, e, x);
-        put(ks + 4, e, y);
+      for (int j = 0; j < 4; ++j) {
+        uint32_t& wx = (&qv[ks].x)[j];
+        uint32_t& wy = (&qv[ks + 4].x)[j];
+        const float c0 = rot_entry(r, 8 * ks + 2 * j, false), s0 = rot_entry(r, 8 * ks + 2 * j, true);
+        const float c1 = rot_entry(r, 8 * ks + 2 * j + 1, false);
+        const float s1 = rot_entry(r, 8 * ks + 2 * j + 1, true);
+        const float x0 = lo(wx), x1 = hi(wx), y0 = lo(wy), y1 = hi(wy);
+        const float ys0 = y0 * s0, ys1 = y1 * s1, xs0 = x0 * s0, xs1 = x1 * s1;
+        wx = Mma32<T>::pack2(fmaf(x0, c0, -ys0), fmaf(x1, c1, -ys1));
+        wy = Mma32<T>::pack2(fmaf(y0, c0, xs0), fmaf(y1, c1, xs1));
       }
   } else {
+    // pairs are the two elements of a word
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        Bits x = get(ks, e), y = get(ks, e + 1);
-        rotate_pair<T>(x, y, rot_entry(r, 4 * ks + e / 2, false), rot_entry(r, 4 * ks + e / 2, true));
-        put(ks, e, x);
-        put(ks, e + 1, y);
+      for (int j = 0; j < 4; ++j) {
+        uint32_t& w = (&qv[ks].x)[j];
+        const float cc = rot_entry(r, 4 * ks + j, false), ss = rot_entry(r, 4 * ks + j, true);
+        const float x = lo(w), y = hi(w);
+        const float ys = y * ss, xs = x * ss;
+        w = Mma32<T>::pack2(fmaf(x, cc, -ys), fmaf(y, cc, xs));
       }
   }
 }
@@ -583,7 +591,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       RotVals rv;
       load_rot(rv, a.cosv + int64_t(pos) * (kD / 2), a.sinv + int64_t(pos) * (kD / 2), c,
                a.interleaved);
-      apply_rot<T>(qv, rv, a.interleaved);
+      apply_rot_q<T>(qv, rv, a.interleaved);
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -738,19 +746,44 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                           wj, o[dt][v]);
     }
   }
-  if (!row_ok) return;
-  const float inv = 1.f / l_row;
-  uint16_t* orow = a.out + ((int64_t(b) * S + my_i) * a.H + my_h) * kD;
+  // ---- the output. A lane holds dims 32 dt + 8 v4 + 4 c .. + 3 of its row,
+  // so storing from registers writes 16-byte pieces of 32 rows per
+  // instruction; instead the wave's 32 rows go through its own 8 KB of LDS
+  // (the tiles are free: every wave has passed the last tile's barrier) and
+  // each store instruction writes four whole 256-byte rows. Chunks are
+  // XOR-swizzled by row, so the 8-byte writes and the 16-byte reads are
+  // free of bank conflicts. ----
+  const float inv = row_ok ? 1.f / l_row : 0.f;
+  unsigned char* stage = (wave < 2 ? k_even : wave < 4 ? k_odd : wave < 6 ? v_even : v_odd) +
+                         (wave & 1) * (kTileBytes / 2);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      const int d = 32 * dt + 8 * v4 + 4 * c;
       uint2 w;
       w.x = Mma32<T>::pack2(o[dt][4 * v4] * inv, o[dt][4 * v4 + 1] * inv);
       w.y = Mma32<T>::pack2(o[dt][4 * v4 + 2] * inv, o[dt][4 * v4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + d) = w;
+      *reinterpret_cast<uint2*>(stage + col * 256 + (((4 * dt + v4) ^ (col & 15)) << 4) + 8 * c) = w;
     }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // lane: row 4 k + lane / 16 of the wave, chunk lane % 16
+  const int ch = lane & 15;
+  int out_i = (wr0 + (lane >> 4)) / G;
+  int out_j = wr0 + (lane >> 4) - out_i * G;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int rr = 4 * k + (lane >> 4);
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * 256 + ((ch ^ (rr & 15)) << 4));
+    if (wr0 + rr < nrows)
+      *reinterpret_cast<uint4*>(a.out + ((int64_t(b) * S + out_i) * a.H + g * G + out_j) * kD + 8 * ch) = v;
+    out_j += 4;
+    while (out_j >= G) {
+      out_j -= G;
+      ++out_i;
+    }
+  }
   };
 
   row_block(a.n_rb - 1 - item / units);      // longest row blocks first
