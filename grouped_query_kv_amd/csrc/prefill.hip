@@ -713,6 +713,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
     if (!sh_last) return;
+    // the other splits' partials from memory, this split's own from its
+    // registers (the values it stored), all weighed in split order
     float mj[kPrefillMaxSplits], lj[kPrefillMaxSplits];
     float M = -INFINITY;
 #pragma unroll
@@ -721,30 +723,43 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       lj[j] = 0.f;
       if (j < nsplit) {
         const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
-        mj[j] = __hip_atomic_load(sj + 512 * 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lj[j] = __hip_atomic_load(sj + 512 * 65 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mj[j] = j == split ? rs.m_use
+                           : __hip_atomic_load(sj + 512 * 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lj[j] = j == split ? l_row
+                           : __hip_atomic_load(sj + 512 * 65 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (lj[j] > 0.f) M = fmaxf(M, mj[j]);   // a split that saw no key of the row adds nothing
       }
     }
-    l_row = 0.f;
+    float l_acc = 0.f;
+    f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+      for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
 #pragma unroll
     for (int j = 0; j < kPrefillMaxSplits; ++j) {
       if (j >= nsplit) break;
       const float wj = lj[j] > 0.f ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
-      l_row = fmaf(lj[j], wj, l_row);
+      l_acc = fmaf(lj[j], wj, l_acc);
       const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
+      if (j == split) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          o[dt][v] = fmaf(__hip_atomic_load(sj + (wave * 64 + dt * 16 + v) * 64 + lane,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                          wj, o[dt][v]);
+          for (int v = 0; v < 16; ++v) acc[dt][v] = fmaf(o[dt][v], wj, acc[dt][v]);
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            acc[dt][v] = fmaf(__hip_atomic_load(sj + (wave * 64 + dt * 16 + v) * 64 + lane,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                              wj, acc[dt][v]);
+      }
     }
+    l_row = l_acc;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = acc[dt];
   }
   // ---- the output. A lane holds dims 32 dt + 8 v4 + 4 c .. + 3 of its row,
   // so storing from registers writes 16-byte pieces of 32 rows per
