@@ -911,12 +911,15 @@ bool decode_fused_evict_supported(const Problem& p) {
 }
 
 bool decode_fast_supported(const Problem& p) {
-  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.S == 1 &&
-         p.B <= kDecodeArgBatch;
+  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.S == 1;
 }
 
-hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
-                              hipStream_t st, bool fuse_evict) {
+namespace {
+
+// One launch over at most kDecodeArgBatch sequences (their plan travels in
+// the kernel arguments).
+hipError_t launch_decode_batch(const Problem& p, void* ws, const WorkspaceLayout& lay,
+                               hipStream_t st, bool fuse_evict) {
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(p.q);
   a.k_new = static_cast<const uint16_t*>(p.k_new);
@@ -978,6 +981,38 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
   else
     hipLaunchKernelGGL((decode_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Batches of more than kDecodeArgBatch sequences run as consecutive launches
+// over groups of kDecodeArgBatch sequences (sequences are independent; the
+// launches share the workspace in stream order, and each leaves the merge
+// counters at zero for the next).
+hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
+                              hipStream_t st, bool fuse_evict) {
+  if (p.B <= kDecodeArgBatch) return launch_decode_batch(p, ws, lay, st, fuse_evict);
+  for (int b0 = 0; b0 < p.B; b0 += kDecodeArgBatch) {
+    Problem c = p;
+    c.B = p.B - b0 < kDecodeArgBatch ? p.B - b0 : kDecodeArgBatch;
+    const int64_t qrow = int64_t(b0) * p.H * p.D;             // [B, 1, H, D] (S == 1)
+    const int64_t kvrow = int64_t(b0) * p.Hkv * p.D;          // [B, 1, Hkv, D]
+    const int64_t crow = int64_t(b0) * p.Hkv * p.M * p.D;     // [B, Hkv, M, D]
+    c.q = static_cast<const uint16_t*>(p.q) + qrow;
+    c.out = static_cast<uint16_t*>(p.out) + qrow;
+    c.k_new = static_cast<const uint16_t*>(p.k_new) + kvrow;
+    c.v_new = static_cast<const uint16_t*>(p.v_new) + kvrow;
+    c.k_cache = static_cast<uint16_t*>(p.k_cache) + crow;
+    c.v_cache = static_cast<uint16_t*>(p.v_cache) + crow;
+    c.lens_host = p.lens_host + b0;
+    c.lens_dev = p.lens_dev ? p.lens_dev + b0 : nullptr;
+    c.off_host = p.off_host ? p.off_host + b0 : nullptr;
+    c.off_dev = p.off_dev ? p.off_dev + b0 : nullptr;
+    if (p.bias) c.bias = static_cast<const uint16_t*>(p.bias) + b0 * p.bias_bs;
+    const hipError_t e = launch_decode_batch(c, ws, lay, st, fuse_evict);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gqa

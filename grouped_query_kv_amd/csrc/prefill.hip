@@ -8,7 +8,7 @@
 // Per 64-key tile (the gemm0 -> softmax -> gemm1 chain of the "KV Cache"
 // discussion's worked example, on gfx950 MFMA 32x32x16):
 //   S^T = K Q^T   A = K rows from LDS, B = Q^T held in registers (rotated
-//                 on load under the fp64 rule when rotary is on);
+//                 on load in fp32 when rotary is on);
 //                 lane (row, half) gets 32 keys of its row;
 //   online softmax per row, in registers (one cross-lane step);
 //   O^T += V^T P^T  A = V^T through transposing LDS reads, B = P^T straight

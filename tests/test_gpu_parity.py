@@ -286,11 +286,11 @@ def test_attention_bias(spec):
     check_full(case, "decode" if S == 1 else "prefill", f"bias {spec}")
 
 
-# More sequences than the split-KV decode plans (64): one-token calls that
-# evict run the eviction kernel, the append and then the MFMA prefill kernel
-# (which must keep the same rows as the eviction: W - 1 with greedy eviction)
-# or, with a bias, the plain kernel (the bias column of a kept key is its
-# buffer row plus the dropped count).
+# More sequences than one split-KV decode launch plans (64): one-token calls
+# that evict run the eviction (fused when the window covers the buffer) and
+# then the split-KV decode in launches of 64 sequences, which must keep the
+# same rows as the eviction (W - 1 with greedy eviction) and read the bias
+# column of a kept key at its buffer row plus the dropped count.
 MANY = [
     # dtype, H, Hkv, M, W, greedy, bias kind
     ("bf16", 8, 2, 96, 64, 1, None),
@@ -310,6 +310,26 @@ def test_many_sequences_evicting_decode(spec):
     if kind:
         _attach_bias(case, kind, 2, np.random.default_rng(seed))
     check_full(case, "decode", f"{B} sequences evicting {spec}")
+
+
+@pytest.mark.parametrize("spec", [
+    # dtype, B, H, Hkv, M, W, rotary: more than 64 sequences run the split-KV
+    # decode as consecutive launches of 64 (here 64 + 64 + 2, and 64 + 6 with
+    # the fused eviction of a full window)
+    ("fp16", 130, 8, 2, 256, -1, True),
+    ("bf16", 70, 8, 8, 128, 128, False),
+], ids=["fp16-B130", "bf16-B70-window"])
+def test_decode_more_than_64_sequences(spec):
+    dt, B, H, Hkv, M, W, rot = spec
+    seed = sum(map(ord, repr(spec))) % 1000
+    rng = np.random.default_rng(seed)
+    if W > 0:
+        lens = [M if i % 4 else int(rng.integers(0, M)) for i in range(B)]
+    else:
+        lens = rng.integers(0, M, B).tolist()
+    case = gi.make_case("many-decode", dt, B, 1, H, Hkv, 128, M, lens, seed, window=W, rotary=rot,
+                        rotary_rows=2 * M)
+    check_full(case, "decode", f"decode {B} sequences {spec}")
 
 
 def test_attention_bias_decode_full_size():
