@@ -47,7 +47,7 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "df8d380e05ae388bacc3966e646c0f9315e5785adf1a68c87ba02d9429dc1a3b",
+                "ecd8264505a23b2272825ee7fa5c506f9cc4ce33ecd4c9e03497d6f3fa1fccc1",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
                 "6260f8ffec745efa6e63541d2973d809e78a61e935af173068a60613b61419cb"},
     "fetch_kib": 73845.260, "write_kib": 1050.291,
