@@ -422,6 +422,68 @@ def test_window_decode_rolling_steps():
     assert e.value.status == gqa.GQA_ERR_NO_ROOM
 
 
+@pytest.mark.parametrize("dt,M,lens,S,greedy", [
+    ("bf16", 1024, [1024, 1000, 1024], 40, 0),   # split key ranges: partial slots poisoned too
+    ("fp16", 256, [256, 199, 131], 37, 1),       # greedy: only the first overflows
+])
+def test_windowed_chunk_poisoned_workspace(dt, M, lens, S, greedy):
+    """A windowed chunk (S > 1 into full W-slot caches) whose workspace holds
+    NaN bits in every byte except the merge counters (which the library keeps
+    at zero between calls). The staging frames then hold NaN in the rows past
+    each sequence's L + S up to the end of its last 64-key tile, and in every
+    row no step writes: outputs and caches must still match the oracle, so the
+    prefill's tile loads stop at the valid length and nothing reads a row the
+    call did not write."""
+    import torch
+    from test_prefill_plan import align256, cdiv, layout, lib_workspace
+    B, H, Hkv, D = 3, 8, 2, 128
+    case = gi.make_case("poisoned-workspace", dt, B, S, H, Hkv, D, M, lens, 41 + S, window=M,
+                        rotary=True, rotary_rows=M + S)
+    case.greedy_eviction = greedy
+    total, _, (c_off, c_bytes), _ = layout(B, S, H, Hkv, D, M, 2, M)
+    assert total == lib_workspace(B, S, H, Hkv, M, M, {"fp16": 1, "bf16": 2}[dt])
+    ws = torch.full((total,), 0xFF, dtype=torch.uint8, device="cuda")   # 0xFFFF: NaN in fp16, bf16
+    ws[:align256(B * Hkv * cdiv(H // Hkv, 16) * 4)] = 0                  # decode merge counters
+    ws[c_off:c_off + c_bytes] = 0                                        # prefill split counters
+    say(f"[gpu] poisoned workspace {dt} lens={lens} S={S} greedy={greedy}: {total} bytes")
+    st, want, kc, vc, _ = O.gqa_attention(case, "prefill")
+    assert st == O.OK
+    dev = DevCase(case)
+    out = dev.run("prefill", workspace=ws)
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "poisoned workspace k_cache")
+    assert_bits_equal(gv, vc, "poisoned workspace v_cache")
+    err = assert_close(out_f64(out, dt), want, dt, "poisoned workspace")
+    say(f"[gpu]   max abs error {err:.3e}")
+
+
+@pytest.mark.parametrize("dt,W", [("fp16", -1), ("bf16", 512)])
+def test_decode_poisoned_workspace(dt, W):
+    """The split-KV decode (with a window: full caches, so the fused eviction
+    and its halo rows run too) on a workspace that holds NaN bits everywhere
+    but the merge counters: the cross-workgroup merge reads only partials this
+    call wrote."""
+    import torch
+    from test_prefill_plan import align256, cdiv, lib_workspace
+    B, H, Hkv, D, M = 16, 32, 8, 128, 512
+    lens = [M if W > 0 else M - 1] * 8 + list(range(37, M, 60))   # no window: room for one
+    case = gi.make_case("poisoned-decode", dt, B, 1, H, Hkv, D, M, lens, 77, window=W,
+                        rotary=True, rotary_rows=M + 1)
+    total = lib_workspace(B, 1, H, Hkv, M, W, {"fp16": 1, "bf16": 2}[dt])
+    ws = torch.full((total,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[:align256(B * Hkv * cdiv(H // Hkv, 16) * 4)] = 0                  # decode merge counters
+    say(f"[gpu] poisoned workspace decode {dt} W={W}: {total} bytes")
+    st, want, kc, vc, _ = O.gqa_attention(case, "decode")
+    assert st == O.OK
+    dev = DevCase(case)
+    out = dev.run("decode", workspace=ws)
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, "poisoned decode k_cache")
+    assert_bits_equal(gv, vc, "poisoned decode v_cache")
+    err = assert_close(out_f64(out, dt), want, dt, "poisoned decode")
+    say(f"[gpu]   max abs error {err:.3e}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 def test_windowed_chunks_rolling(dt):
     """Chunks of S > 1 tokens into full W-slot caches, continued in place on

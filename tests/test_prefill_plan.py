@@ -63,7 +63,7 @@ def layout(B, S, H, Hkv, D, M, dt_bytes, window):
     halo = B * Hkv * 2 * cdiv(M, EVICT_CHUNK_ROWS) * EVICT_HALO_MAX * row_bytes
     dhalo = 2 * DECODE_WG * DECODE_WAVES * D * 2 if fast else 0
     pf_items = pf_partial = 0
-    decode_only = S == 1 and B <= DECODE_ARG_BATCH
+    decode_only = S == 1
     if fast and S > 0 and not decode_only and may_split(B, S, G, Hkv, M):
         pf_items = cdiv(S * G, WG_ROWS) * B * Hkv
         pf_partial = pf_items * MAX_SPLITS * SLOT_FLOATS * 4
