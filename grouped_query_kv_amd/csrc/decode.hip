@@ -76,6 +76,7 @@ constexpr int kSlotBytes = kSlotFloats * 4;
 // per wave in LDS: partial slot 0, then an area holding the V tile while
 // streaming and partial slot 1 at the end
 constexpr int kWaveLds = 2 * kSlotBytes;
+static_assert(kVTileBytes <= kSlotBytes, "the V tile lives in partial slot 1 while streaming");
 constexpr float kRescaleSlack = 8.f;           // binary orders the reference max may lag
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -298,6 +299,16 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   const int64_t hrow = int64_t(worker) * kD + 8 * q4;
   const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
   const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * kD + 8 * q4;
+  if (k.Lp < k.kb + kKeys) {
+    // the block of the new token: that key's K and V rows come from k_new
+    // and v_new (the cache row is written when the block is computed), in
+    // flight with the rest of the block
+    if (row == k.Lp) {
+      const int64_t kvrow = (int64_t(k.b) * a.Hkv + k.g) * kD + 8 * q4;
+      kp = a.k_new + kvrow;
+      vp = a.v_new + kvrow;
+    }
+  }
   // a spare load (the pipeline's refill past the slice's last block) reads
   // the first 128 Q elements instead: one cache line for the wave, not a
   // second copy of the last block, and the wait counts stay those of a full
@@ -354,7 +365,7 @@ __device__ inline uint32_t pack2(float x, float y) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <class T, bool kBias>
+template <class T, bool kBias, bool kRot>
 __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
                                const DecodeArgs& a, int lane, unsigned char* vt) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -364,19 +375,14 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
     r.v0 = z; r.v1 = z; r.v2 = z; r.v3 = z;
   }
   if (k.Lp >= k.kb && k.Lp < k.kb + kKeys && n == k.Lp - k.kb) {
-    // the new token: its K row (rotated from k_new) and V row (from v_new)
-    // replace the loaded ones and go into the cache; the head group 0 unit of
-    // the kv head writes them
-    const int64_t kvrow = (int64_t(k.b) * a.Hkv + k.g) * kD + 8 * q4;
-    const uint16_t* kn = a.k_new + kvrow;
-    const uint16_t* vn = a.v_new + kvrow;
-    r.k0 = ld16(kn); r.k1 = ld16(kn + 32); r.k2 = ld16(kn + 64); r.k3 = ld16(kn + 96);
-    if (a.rot) {
+    // the new token: its K row (loaded from k_new, rotated here) and V row
+    // (from v_new) go into the cache; the head group 0 unit of the kv head
+    // writes them
+    if (kRot && a.rot) {
       const int pos = clamp_len(k.L + a.ro[k.b], 0, a.rot_rows - 1);
       rotate4<T>(r.k0, r.k1, r.k2, r.k3, q4, a.cosv + int64_t(pos) * (kD / 2),
                  a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
     }
-    r.v0 = ld16(vn); r.v1 = ld16(vn + 32); r.v2 = ld16(vn + 64); r.v3 = ld16(vn + 96);
     if (k.ub % a.n_hg == 0) {
       const int64_t crow = ((int64_t(k.b) * a.Hkv + k.g) * a.M + k.Lp) * kD + 8 * q4;
       uint4* kc = reinterpret_cast<uint4*>(a.k_cache + crow);
@@ -546,12 +552,12 @@ __device__ inline uint4 mask4(uint4 c, uint32_t m) {
 
 // Rotate Q at position L_b and zero the padding heads (a mask, no select of
 // aggregates: the rows stay in registers).
-template <class T>
+template <class T, bool kRot>
 __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, int lane) {
   const int n = lane & 15, q4 = lane >> 4;
   const int hg = k.ub % a.n_hg;
   const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
-  if (a.rot) {
+  if (kRot && a.rot) {
     const int pos = clamp_len(k.L + a.ro[k.b], 0, a.rot_rows - 1);
     rotate4<T>(q.c0, q.c1, q.c2, q.c3, q4, a.cosv + int64_t(pos) * (kD / 2),
                a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
@@ -681,7 +687,7 @@ __device__ inline void set_entry(const DecodeArgs& a, int* ent, bool on, const B
 // One launch: workgroups of kDecodeWaves waves; every wave of the grid
 // streams its own slice (see the top of the file), then the workgroup
 // combines the partials its waves left.
-template <class T, bool kBias>
+template <class T, bool kBias, bool kRot>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
   // per wave, entries 2 wv (its first unit, partial in slot 0) and 2 wv + 1
@@ -741,7 +747,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       set_entry(a, sh_ent[2 * wv], cur.i > 0 && !same, cur, sr, lane);
       set_entry(a, sh_ent[2 * wv + 1], same ? (cur.i > 0 || open_end) : open_end, lb, sr, lane);
     }
-    Q4 qv = finish_q<T>(qraw, a, cur, lane);
+    Q4 qv = finish_q<T, kRot>(qraw, a, cur, lane);
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
     // unit end or at the slice end. Returns false after the slice's last block.
@@ -749,7 +755,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
       r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
-      compute<T, kBias>(s, r_cur, qv, cur, a, lane, vt);
+      compute<T, kBias, kRot>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
         if (shared) {
@@ -761,7 +767,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
         if (last) return false;
         acc_reset(s);
         seg_shared = false;
-        qv = finish_q<T>(load_q_raw(a, nxt, lane), a, nxt, lane);
+        qv = finish_q<T, kRot>(load_q_raw(a, nxt, lane), a, nxt, lane);
       }
       cur = nxt;
       nxt = ahead;
@@ -971,15 +977,21 @@ hipError_t launch_decode_batch(const Problem& p, void* ws, const WorkspaceLayout
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // rotary gets kernels of its own: without the rotation code the streaming
+  // loop needs fewer registers
   const bool fp16 = p.dtype == GQA_FP16;
-  if (p.bias && fp16)
-    hipLaunchKernelGGL((decode_kernel<F16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else if (p.bias)
-    hipLaunchKernelGGL((decode_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else if (fp16)
-    hipLaunchKernelGGL((decode_kernel<F16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+  const dim3 grid(blocks), wg(kThreads);
+  if (a.rot) {
+    if (p.bias && fp16) hipLaunchKernelGGL((decode_kernel<F16, true, true>), grid, wg, 0, st, a);
+    else if (p.bias) hipLaunchKernelGGL((decode_kernel<BF16, true, true>), grid, wg, 0, st, a);
+    else if (fp16) hipLaunchKernelGGL((decode_kernel<F16, false, true>), grid, wg, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<BF16, false, true>), grid, wg, 0, st, a);
+  } else {
+    if (p.bias && fp16) hipLaunchKernelGGL((decode_kernel<F16, true, false>), grid, wg, 0, st, a);
+    else if (p.bias) hipLaunchKernelGGL((decode_kernel<BF16, true, false>), grid, wg, 0, st, a);
+    else if (fp16) hipLaunchKernelGGL((decode_kernel<F16, false, false>), grid, wg, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<BF16, false, false>), grid, wg, 0, st, a);
+  }
   return hipGetLastError();
 }
 
