@@ -227,6 +227,24 @@ def stats(dev, per):
             "per_call_event_p90_ms": float(a[int(0.9 * (len(a) - 1))])}
 
 
+def read_yardstick(torch, gqa, nbytes, steps, warmup, decode_ms):
+    """A plain streaming read (gqa_stream_read, the decode's launch shape) of
+    the decode's byte count, rotating over buffers that together exceed the
+    last-level cache like the decode's input sets: the time any kernel that
+    reads those bytes once can reach here, and the decode's time against it."""
+    nbytes16 = (nbytes + 15) // 16 * 16
+    n = max(4, math.ceil(MIN_ROTATION_BYTES / nbytes16))
+    bufs = [torch.ones(nbytes16, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    log(f"[bench] read yardstick: {n} buffers of {nbytes16} bytes")
+    _, dev, per = time_calls(torch, bufs, lambda b: gqa.gqa_stream_read(b), steps, warmup)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes16, "us": dev * 1e3, "gbs": nbytes16 / (dev * 1e-3) / 1e9,
+            "frac_hbm_peak": nbytes16 / (dev * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decode_time_over_read_time": decode_ms / dev,
+            "per_call_event_median_us": float(np.median(per)) * 1e3}
+
+
 def decode_call(gqa):
     def call(s):
         c = s.case
@@ -412,6 +430,8 @@ def main():
     value = dec_bytes / (wall * 1e-3) / 1e9
     del sets
     torch.cuda.empty_cache()
+    yardstick = read_yardstick(torch, gqa, dec_bytes, args.steps, args.warmup,
+                               st_dec["mean_ms"])
     device = device_info(torch)
 
     extra = {}
@@ -580,6 +600,7 @@ def main():
                      "kernel": "decode call (all launches of gqa_attention_decode)",
                      "bytes_per_call": dec_bytes, **st_dec},
         "cpu_baseline": cpu,
+        "hbm_read_yardstick": yardstick,
         "device": device,
         **extra,
     }

@@ -31,7 +31,7 @@ GQA_FP32, GQA_FP16, GQA_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "ok", 1: "no_room", 2: "invalid_arg", 3: "unsupported", 4: "workspace", 5: "hip"}
 EXPORTED = ("gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill", "gqa_attention_decode",
             "gqa_attention_present", "gqa_evict_window", "gqa_attention_decode_noalloc",
-            "gqa_status_string", "gqa_last_error")
+            "gqa_stream_read", "gqa_status_string", "gqa_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20     # GQA_NOALLOC_SCRATCH_BYTES
 
 
@@ -85,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attention_decode_noalloc.restype = ctypes.c_int
     lib.gqa_evict_window.argtypes = [P, ctypes.c_int32, VP, VP, I32P, VP, I32P, VP, ctypes.c_size_t, VP]
     lib.gqa_evict_window.restype = ctypes.c_int
+    lib.gqa_stream_read.argtypes = [VP, ctypes.c_size_t, VP]
+    lib.gqa_stream_read.restype = ctypes.c_int
     lib.gqa_status_string.argtypes = [ctypes.c_int]
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_last_error.argtypes = []
@@ -406,6 +408,13 @@ def gqa_attention_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seqlens_k_ho
                                             _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                             hp, _ptr(seqlens_k_dev), _ptr(out), _stream(stream)))
     return out
+
+
+def gqa_stream_read(buf, *, stream=None):
+    """Enqueue one plain streaming read of the whole (contiguous) device tensor
+    `buf`: the yardstick for the memory-bound kernels, not part of the op."""
+    _contig(buf)
+    _check(lib.gqa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)))
 
 
 def gqa_evict_window(k_cache, v_cache, seqlens_k_host, seqlens_k_dev, incoming: int, *,

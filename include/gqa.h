@@ -281,6 +281,19 @@ gqa_status gqa_attention_decode_noalloc(const gqa_shape* shape, const gqa_option
                                         const int32_t* seqlens_k_host,
                                         const int32_t* seqlens_k_dev, void* out, void* stream);
 
+/*
+ * A plain streaming read of `bytes` bytes at `src` (device memory, 16-byte
+ * aligned; bytes a positive multiple of 16), enqueued on `stream`. Not part
+ * of the operation: the yardstick the memory-bound kernels are measured
+ * against (the benchmark times it on buffers of the split-KV decode's byte
+ * count that are not cache-resident). It reads the buffer once, with the
+ * split-KV decode's launch shape (one workgroup of eight waves per CU, each
+ * wave a contiguous slice, 16-byte loads, four in flight per lane), and
+ * writes nothing the caller reads. Errors: GQA_ERR_INVALID_ARG before any
+ * launch; GQA_ERR_HIP if the launch fails.
+ */
+gqa_status gqa_stream_read(const void* src, size_t bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gqa_status_string(gqa_status status);
 

@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol(g):
     names = declared_functions()
     assert set(names) == {"gqa_workspace_bytes", "gqa_append_kv", "gqa_attention_prefill",
                           "gqa_attention_decode", "gqa_attention_present", "gqa_evict_window",
-                          "gqa_attention_decode_noalloc", "gqa_status_string", "gqa_last_error"}
+                          "gqa_attention_decode_noalloc", "gqa_stream_read", "gqa_status_string",
+                          "gqa_last_error"}
     assert set(names) == set(g.EXPORTED)
     lib = ctypes.CDLL(g.LIB_PATH)
     for n in names:
@@ -422,3 +423,11 @@ def test_position_offset_rule_matches_oracle():
     assert O.validate(c, "prefill") == O.OK
     c.position_offset = np.array([0, 11], np.int32)
     assert O.validate(c, "prefill") == O.INVALID
+
+
+def test_stream_read_rejects_bad_arguments(g):
+    """The read yardstick validates before any launch (no GPU needed)."""
+    for ptr, nbytes in ((None, 1024), (16, 0), (16, 1000), (8, 1024)):
+        st = g.lib.gqa_stream_read(ptr, nbytes, None)
+        assert st == g.GQA_ERR_INVALID_ARG, (ptr, nbytes, st)
+        assert b"gqa_stream_read" in g.lib.gqa_last_error()

@@ -813,3 +813,15 @@ def test_random_feature_combinations(k):
     assert_bits_equal(gv, vc, f"{desc} present v")
     err = assert_close(out_f64(out, case.dtype), want, case.dtype, desc)
     say(f"[gpu]   max abs error {err:.3e}")
+
+
+def test_stream_read_yardstick_runs():
+    """The read yardstick (not part of the op) runs on a device buffer and
+    leaves it as it was."""
+    import torch
+    import grouped_query_kv_amd as gqa
+    buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda")
+    before = buf.clone()
+    gqa.gqa_stream_read(buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
