@@ -326,10 +326,15 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
   }
   // NaN-propagating maximum: unlike fmaxf it needs no quieting of each
   // operand, so the chain folds into one three-input max per two scores
-  float tmax = __builtin_elementwise_maximum(s[0][0], s[1][0]);
+  // four independent chains, then a tree: short dependency paths
+  float mc[4];
 #pragma unroll
-  for (int v = 1; v < 16; ++v)
-    tmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(tmax, s[0][v]), s[1][v]);
+  for (int c4 = 0; c4 < 4; ++c4) mc[c4] = __builtin_elementwise_maximum(s[0][c4], s[1][c4]);
+#pragma unroll
+  for (int v = 4; v < 16; ++v)
+    mc[v & 3] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mc[v & 3], s[0][v]), s[1][v]);
+  float tmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mc[0], mc[1]),
+                                             __builtin_elementwise_maximum(mc[2], mc[3]));
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
                                                      false, false);
@@ -349,6 +354,7 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
     rs.m_use = use_new;
   }
   const float mu = rs.m_use;
+  float lp[4] = {0.f, 0.f, 0.f, 0.f};   // the tile's row sum in four chains
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     uint32_t w[4];
@@ -358,10 +364,11 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][v], cs, -mu));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][v + 1], cs, -mu));
       w[e] = Mma32<T>::pack2(p0, p1);
-      rs.l = Mma32<T>::dot_ones(w[e], rs.l);
+      lp[e] = Mma32<T>::dot_ones(w[e], lp[e]);
     }
     pk[u] = make_uint4(w[0], w[1], w[2], w[3]);
   }
+  rs.l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
 }
 
 // S^T (64 keys) = K Q^T for the lane's row; A = K rows (key 32 h + col,
