@@ -47,10 +47,10 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GP
 # on; any change to them makes the figure null until the passes are repeated.
 DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
-                "2e3ce1359ed8c44397be43948ff3589866b7257eb88ced84ec55069ff60d3999",
+                "18888959ac127026e4519d190334f2a6a4eca49f9babe47caf957e46958b39df",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "6260f8ffec745efa6e63541d2973d809e78a61e935af173068a60613b61419cb"},
-    "fetch_kib": 73694.058, "write_kib": 1050.325,
+                "9375556f61ec86da828769c99791203ec998440fccd61fa074bbbf7e60d46258"},
+    "fetch_kib": 73702.938, "write_kib": 1050.305,
     "fetch_scale": 524288.0 / 262157.088, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}

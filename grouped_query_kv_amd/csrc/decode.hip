@@ -66,7 +66,10 @@ template <> struct Mma<BF16> {
   }
 };
 
-constexpr int kD = 128;
+// Head sizes 128 and 64 (template parameter D). Partial slots and the V
+// tile are laid out for the larger one: a head of D = 64 uses the first
+// half of each 128-float head row of a slot and of each 256-byte tile row.
+constexpr int kD = 128;                           // slot and tile row capacity
 constexpr int kKeys = 16;                         // keys per block
 constexpr int kVTileBytes = kKeys * kD * 2;       // per-wave V tile, 16 rows x 256 B
 constexpr int kSlotFloats = kDecodeMaxHG * (kD + 2);
@@ -157,10 +160,11 @@ struct Blk {
   int L;                   // past length (with the sequence's position offset: the rotary position)
 };
 
+template <int D>
 __device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) {
   const Seq s = seq_of(a, k.b, sr);
   k.g = k.ub / a.n_hg;
-  const int64_t base = (int64_t(k.b) * a.Hkv + k.g) * a.M * kD;
+  const int64_t base = (int64_t(k.b) * a.Hkv + k.g) * a.M * D;
   k.kc = a.k_cache + base;
   k.vc = a.v_cache + base;
   k.kend = s.kend;
@@ -172,6 +176,7 @@ __device__ inline void set_unit(Blk& k, const DecodeArgs& a, const SeqRegs& sr) 
   k.L = s.L;
 }
 
+template <int D>
 __device__ inline Blk locate(const DecodeArgs& a, int64_t x, const SeqRegs& sr, int lane) {
   Blk k;
   // the lane whose sequence holds block x (none past the end: sequence 0)
@@ -186,10 +191,11 @@ __device__ inline Blk locate(const DecodeArgs& a, int64_t x, const SeqRegs& sr, 
   k.ub = k.ub < units ? (k.ub > 0 ? k.ub : 0) : units - 1;
   k.i = off - k.ub * nb;
   k.i = k.i < nb ? (k.i > 0 ? k.i : 0) : (nb > 0 ? nb - 1 : 0);
-  set_unit(k, a, sr);
+  set_unit<D>(k, a, sr);
   return k;
 }
 
+template <int D>
 __device__ inline Blk next_block(const DecodeArgs& a, const Blk& c, const SeqRegs& sr) {
   Blk k = c;
   if (++k.i < k.nb) {
@@ -201,7 +207,7 @@ __device__ inline Blk next_block(const DecodeArgs& a, const Blk& c, const SeqReg
     k.ub = 0;
     ++k.b;
   }
-  set_unit(k, a, sr);
+  set_unit<D>(k, a, sr);
   return k;
 }
 
@@ -245,17 +251,28 @@ __device__ inline void rot_inter_chunk(uint4& c, int j0, const float* cosr, cons
   rot_inter_word<T>(c.w, j0 + 3, cosr, sinr);
 }
 
-template <class T>
+// The lane's D / 32 chunks (c2, c3 only for D = 128); `cosr`/`sinr` point
+// at the position's D / 2 table entries.
+template <class T, int D>
 __device__ inline void rotate4(uint4& c0, uint4& c1, uint4& c2, uint4& c3, int q4,
                                const float* cosr, const float* sinr, int interleaved) {
-  if (!interleaved) {
-    rot_half_chunks<T>(c0, c2, 8 * q4, cosr, sinr);          // dims 8 q4 + e with + 64
-    rot_half_chunks<T>(c1, c3, 32 + 8 * q4, cosr, sinr);
+  if (D == 128) {
+    if (!interleaved) {
+      rot_half_chunks<T>(c0, c2, 8 * q4, cosr, sinr);          // dims 8 q4 + e with + 64
+      rot_half_chunks<T>(c1, c3, 32 + 8 * q4, cosr, sinr);
+    } else {
+      rot_inter_chunk<T>(c0, 4 * q4, cosr, sinr);               // pair index (32 i + 8 q4 + e) / 2
+      rot_inter_chunk<T>(c1, 16 + 4 * q4, cosr, sinr);
+      rot_inter_chunk<T>(c2, 32 + 4 * q4, cosr, sinr);
+      rot_inter_chunk<T>(c3, 48 + 4 * q4, cosr, sinr);
+    }
   } else {
-    rot_inter_chunk<T>(c0, 4 * q4, cosr, sinr);               // pair index (32 i + 8 q4 + e) / 2
-    rot_inter_chunk<T>(c1, 16 + 4 * q4, cosr, sinr);
-    rot_inter_chunk<T>(c2, 32 + 4 * q4, cosr, sinr);
-    rot_inter_chunk<T>(c3, 48 + 4 * q4, cosr, sinr);
+    if (!interleaved) {
+      rot_half_chunks<T>(c0, c1, 8 * q4, cosr, sinr);          // dims 8 q4 + e with + 32
+    } else {
+      rot_inter_chunk<T>(c0, 4 * q4, cosr, sinr);
+      rot_inter_chunk<T>(c1, 16 + 4 * q4, cosr, sinr);
+    }
   }
 }
 
@@ -280,7 +297,7 @@ struct Q4 {
 
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <bool kBias>
+template <bool kBias, int D>
 __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, bool slice_end,
                              bool spare = false) {
   const int row = k.kb + n < k.kend ? k.kb + n : k.kb;
@@ -296,15 +313,15 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   // the slice's halo row, at its wave's index in the launch (recomputed
   // here rather than kept live through the stream)
   const int worker = int(blockIdx.x) * kDecodeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t hrow = int64_t(worker) * kD + 8 * q4;
-  const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * kD + 8 * q4;
-  const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * kD + 8 * q4;
+  const int64_t hrow = int64_t(worker) * D + 8 * q4;
+  const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * D + 8 * q4;
+  const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * D + 8 * q4;
   if (k.Lp < k.kb + kKeys) {
     // the block of the new token: that key's K and V rows come from k_new
     // and v_new (the cache row is written when the block is computed), in
     // flight with the rest of the block
     if (row == k.Lp) {
-      const int64_t kvrow = (int64_t(k.b) * a.Hkv + k.g) * kD + 8 * q4;
+      const int64_t kvrow = (int64_t(k.b) * a.Hkv + k.g) * D + 8 * q4;
       kp = a.k_new + kvrow;
       vp = a.v_new + kvrow;
     }
@@ -316,8 +333,14 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   // The bias kernel, at its register limit, measured slower with it.
   if (!kBias && spare) { kp = a.q + 8 * q4; vp = kp; }
   KV r;
-  r.k0 = ld16(kp); r.k1 = ld16(kp + 32); r.k2 = ld16(kp + 64); r.k3 = ld16(kp + 96);
-  r.v0 = ld16(vp); r.v1 = ld16(vp + 32); r.v2 = ld16(vp + 64); r.v3 = ld16(vp + 96);
+  r.k0 = ld16(kp); r.k1 = ld16(kp + 32);
+  r.v0 = ld16(vp); r.v1 = ld16(vp + 32);
+  if (D == 128) {
+    r.k2 = ld16(kp + 64); r.k3 = ld16(kp + 96);
+    r.v2 = ld16(vp + 64); r.v3 = ld16(vp + 96);
+  } else {
+    r.k2 = r.k3 = r.v2 = r.v3 = make_uint4(0, 0, 0, 0);   // no such dims
+  }
   if (kBias) {
     // head column n of the unit (padding columns reuse head h0; their
     // scores are never written out), keys kb + 4 q4 + e clamped to the
@@ -365,7 +388,7 @@ __device__ inline uint32_t pack2(float x, float y) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <class T, bool kBias, bool kRot>
+template <class T, bool kBias, bool kRot, int D>
 __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
                                const DecodeArgs& a, int lane, unsigned char* vt) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -380,40 +403,52 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
     // writes them
     if (kRot && a.rot) {
       const int pos = clamp_len(k.L + a.ro[k.b], 0, a.rot_rows - 1);
-      rotate4<T>(r.k0, r.k1, r.k2, r.k3, q4, a.cosv + int64_t(pos) * (kD / 2),
-                 a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
+      rotate4<T, D>(r.k0, r.k1, r.k2, r.k3, q4, a.cosv + int64_t(pos) * (D / 2),
+                    a.sinv + int64_t(pos) * (D / 2), a.interleaved);
     }
     if (k.ub % a.n_hg == 0) {
-      const int64_t crow = ((int64_t(k.b) * a.Hkv + k.g) * a.M + k.Lp) * kD + 8 * q4;
+      const int64_t crow = ((int64_t(k.b) * a.Hkv + k.g) * a.M + k.Lp) * D + 8 * q4;
       uint4* kc = reinterpret_cast<uint4*>(a.k_cache + crow);
       uint4* vc = reinterpret_cast<uint4*>(a.v_cache + crow);
-      kc[0] = r.k0; kc[4] = r.k1; kc[8] = r.k2; kc[12] = r.k3;
-      vc[0] = r.v0; vc[4] = r.v1; vc[8] = r.v2; vc[12] = r.v3;
+      kc[0] = r.k0; kc[4] = r.k1;
+      vc[0] = r.v0; vc[4] = r.v1;
+      if (D == 128) {
+        kc[8] = r.k2; kc[12] = r.k3;
+        vc[8] = r.v2; vc[12] = r.v3;
+      }
     }
   }
   if (k.d && k.ub % a.n_hg == 0 && k.kb + n < k.kend) {
     // fused eviction: key kb + n now lives in buffer row kb + n (its source
     // rows of this block are already in registers; the row this overwrites
     // for the previous block was read from the halo copy)
-    const int64_t crow = int64_t(k.kb + n) * kD + 8 * q4;
+    const int64_t crow = int64_t(k.kb + n) * D + 8 * q4;
     uint4* kc = reinterpret_cast<uint4*>(const_cast<uint16_t*>(k.kc) + crow);
     uint4* vc = reinterpret_cast<uint4*>(const_cast<uint16_t*>(k.vc) + crow);
-    kc[0] = r.k0; kc[4] = r.k1; kc[8] = r.k2; kc[12] = r.k3;
-    vc[0] = r.v0; vc[4] = r.v1; vc[8] = r.v2; vc[12] = r.v3;
+    kc[0] = r.k0; kc[4] = r.k1;
+    vc[0] = r.v0; vc[4] = r.v1;
+    if (D == 128) {
+      kc[8] = r.k2; kc[12] = r.k3;
+      vc[8] = r.v2; vc[12] = r.v3;
+    }
   }
   // ---- V rows into the tile ----
   {
     unsigned char* row = vt + n * 256;
     *reinterpret_cast<uint4*>(row + 16 * vchunk(n, q4)) = r.v0;
     *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 4 + q4)) = r.v1;
-    *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 8 + q4)) = r.v2;
-    *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 12 + q4)) = r.v3;
+    if (D == 128) {
+      *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 8 + q4)) = r.v2;
+      *reinterpret_cast<uint4*>(row + 16 * vchunk(n, 12 + q4)) = r.v3;
+    }
   }
   // ---- S^T = K Q^T: lane gets keys 4 q4 + rr of head column n ----
   f32x4 acc = Mma<T>::qk(r.k0, qv.c0, f32x4{0.f, 0.f, 0.f, 0.f});
   acc = Mma<T>::qk(r.k1, qv.c1, acc);
-  acc = Mma<T>::qk(r.k2, qv.c2, acc);
-  acc = Mma<T>::qk(r.k3, qv.c3, acc);
+  if (D == 128) {
+    acc = Mma<T>::qk(r.k2, qv.c2, acc);
+    acc = Mma<T>::qk(r.k3, qv.c3, acc);
+  }
   float sv[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -433,7 +468,7 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
     const float alpha = exp2f(s.m_use - use);
     s.l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) s.o[dt] *= alpha;
+    for (int dt = 0; dt < D / 16; ++dt) s.o[dt] *= alpha;
     s.m_run = mn;
     s.m_use = use;
   }
@@ -454,7 +489,7 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
   const int trow = 4 * q4 + (n >> 2);
   const unsigned char* tbase = vt + trow * 256 + 8 * ((n & 3) & 1);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
+  for (int dt = 0; dt < D / 16; ++dt) {
     const int c = 2 * dt + ((n & 3) >> 1);
     const s16x4 x =
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tbase + 16 * vchunk(trow, c)));
@@ -489,9 +524,9 @@ __device__ inline UnitInfo unit_info(const DecodeArgs& a, int b, int ub, const S
   return u;
 }
 
-template <class T>
+template <class T, int D>
 __device__ inline void store_out(const DecodeArgs& a, int b, int h, int d, float v) {
-  reinterpret_cast<typename T::bits*>(a.out)[(int64_t(b) * a.H + h) * kD + d] = T::from_float(v);
+  reinterpret_cast<typename T::bits*>(a.out)[(int64_t(b) * a.H + h) * D + d] = T::from_float(v);
 }
 
 __device__ inline float ld_agent(const float* p) {
@@ -501,7 +536,7 @@ __device__ inline float ld_agent(const float* p) {
 // End of one unit segment of this wave: normalise and write the output (the
 // wave saw the whole unit) or put the unnormalised partial (o, m, l) into the
 // wave's LDS slot. Lane (n, q4) holds head column n, dims 16 dt + 4 q4 + r.
-template <class T>
+template <class T, int D>
 __device__ inline void finish_segment(const DecodeArgs& a, const Acc& s, const Blk& k, bool shared,
                                       float* slot, int lane) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -515,9 +550,9 @@ __device__ inline void finish_segment(const DecodeArgs& a, const Acc& s, const B
   if (!shared) {
     const float inv = 1.f / l;
     using Bits = typename T::bits;
-    Bits* orow = reinterpret_cast<Bits*>(a.out) + (int64_t(k.b) * a.H + h0 + n) * kD + 4 * q4;
+    Bits* orow = reinterpret_cast<Bits*>(a.out) + (int64_t(k.b) * a.H + h0 + n) * D + 4 * q4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
       uint2 w;
       w.x = pack2<T>(s.o[dt][0] * inv, s.o[dt][1] * inv);
       w.y = pack2<T>(s.o[dt][2] * inv, s.o[dt][3] * inv);
@@ -526,7 +561,7 @@ __device__ inline void finish_segment(const DecodeArgs& a, const Acc& s, const B
     return;
   }
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < D / 16; ++dt)
     *reinterpret_cast<f32x4*>(slot + n * kD + 16 * dt + 4 * q4) = s.o[dt];
   if (q4 == 0) {
     slot[kDecodeMaxHG * kD + n] = s.m_use;
@@ -535,14 +570,20 @@ __device__ inline void finish_segment(const DecodeArgs& a, const Acc& s, const B
 }
 
 // Raw Q rows of block k's unit: lane (n, q4) holds head n's dims 32 i + 8 q4.
+template <int D>
 __device__ inline Q4 load_q_raw(const DecodeArgs& a, const Blk& k, int lane) {
   const int n = lane & 15, q4 = lane >> 4;
   const int hg = k.ub % a.n_hg;
   const int h0 = k.g * a.G + hg * a.hg_size;
   const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
-  const uint16_t* qrow = a.q + (int64_t(k.b) * a.H + h0 + (n < nheads ? n : 0)) * kD + 8 * q4;
+  const uint16_t* qrow = a.q + (int64_t(k.b) * a.H + h0 + (n < nheads ? n : 0)) * D + 8 * q4;
   Q4 q;
-  q.c0 = ld16(qrow); q.c1 = ld16(qrow + 32); q.c2 = ld16(qrow + 64); q.c3 = ld16(qrow + 96);
+  q.c0 = ld16(qrow); q.c1 = ld16(qrow + 32);
+  if (D == 128) {
+    q.c2 = ld16(qrow + 64); q.c3 = ld16(qrow + 96);
+  } else {
+    q.c2 = q.c3 = make_uint4(0, 0, 0, 0);
+  }
   return q;
 }
 
@@ -552,15 +593,15 @@ __device__ inline uint4 mask4(uint4 c, uint32_t m) {
 
 // Rotate Q at position L_b and zero the padding heads (a mask, no select of
 // aggregates: the rows stay in registers).
-template <class T, bool kRot>
+template <class T, bool kRot, int D>
 __device__ __forceinline__ Q4 finish_q(Q4 q, const DecodeArgs& a, const Blk& k, int lane) {
   const int n = lane & 15, q4 = lane >> 4;
   const int hg = k.ub % a.n_hg;
   const int nheads = min(a.hg_size, a.G - hg * a.hg_size);
   if (kRot && a.rot) {
     const int pos = clamp_len(k.L + a.ro[k.b], 0, a.rot_rows - 1);
-    rotate4<T>(q.c0, q.c1, q.c2, q.c3, q4, a.cosv + int64_t(pos) * (kD / 2),
-               a.sinv + int64_t(pos) * (kD / 2), a.interleaved);
+    rotate4<T, D>(q.c0, q.c1, q.c2, q.c3, q4, a.cosv + int64_t(pos) * (D / 2),
+                  a.sinv + int64_t(pos) * (D / 2), a.interleaved);
   }
   const uint32_t keep = n < nheads ? 0xFFFFFFFFu : 0u;
   q.c0 = mask4(q.c0, keep); q.c1 = mask4(q.c1, keep);
@@ -594,7 +635,7 @@ __device__ inline EntInfo read_entry(const int* ent) {
 // Merge the workgroup partials of a unit (slots wg_first + unit .. wg_last +
 // unit) by log-sum-exp, write the output and reset the unit's counter. All
 // threads of the workgroup; `lds` holds 2 kMergeMax x 16 floats.
-template <class T>
+template <class T, int D>
 __device__ inline void merge_unit(const DecodeArgs& a, const EntInfo& u, float* lds) {
   const int tid = threadIdx.x;
   const int b = u.b;
@@ -604,8 +645,8 @@ __device__ inline void merge_unit(const DecodeArgs& a, const EntInfo& u, float* 
   if (count <= 4) {
     // usual case: every thread loads m, l and o of all partials for its
     // output at once (one memory round trip), no LDS pass
-    for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
-      const int h = idx / kD, d = idx % kD;
+    for (int idx = tid; idx < u.nheads * D; idx += kThreads) {
+      const int h = idx / D, d = idx % D;
       float m[4], l[4], o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -624,7 +665,7 @@ __device__ inline void merge_unit(const DecodeArgs& a, const EntInfo& u, float* 
         L = fmaf(l[j], w, L);
         O = fmaf(o[j], w, O);
       }
-      store_out<T>(a, b, u.h0 + h, d, O / L);
+      store_out<T, D>(a, b, u.h0 + h, d, O / L);
     }
     __syncthreads();
     if (tid == 0) __hip_atomic_store(a.counters + u.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -652,8 +693,8 @@ __device__ inline void merge_unit(const DecodeArgs& a, const EntInfo& u, float* 
     for (int j = 0; j < count; ++j) wm[j * 16 + tid] *= inv;
   }
   __syncthreads();
-  for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
-    const int h = idx / kD, d = idx % kD;
+  for (int idx = tid; idx < u.nheads * D; idx += kThreads) {
+    const int h = idx / D, d = idx % D;
     float acc = 0.f;
     for (int j0 = 0; j0 < count; j0 += 8) {
       float x[8];
@@ -664,7 +705,7 @@ __device__ inline void merge_unit(const DecodeArgs& a, const EntInfo& u, float* 
       for (int j = 0; j < 8; ++j)
         if (j0 + j < count) acc = fmaf(x[j], wm[(j0 + j) * 16 + h], acc);
     }
-    store_out<T>(a, b, u.h0 + h, d, acc);
+    store_out<T, D>(a, b, u.h0 + h, d, acc);
   }
   __syncthreads();
   if (tid == 0) __hip_atomic_store(a.counters + u.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -687,7 +728,7 @@ __device__ inline void set_entry(const DecodeArgs& a, int* ent, bool on, const B
 // One launch: workgroups of kDecodeWaves waves; every wave of the grid
 // streams its own slice (see the top of the file), then the workgroup
 // combines the partials its waves left.
-template <class T, bool kBias, bool kRot>
+template <class T, bool kBias, bool kRot, int D>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kDecodeWaves * kWaveLds];
   // per wave, entries 2 wv (its first unit, partial in slot 0) and 2 wv + 1
@@ -719,9 +760,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     set_entry(a, sh_ent[2 * wv], false, Blk{}, sr, lane);
     set_entry(a, sh_ent[2 * wv + 1], false, Blk{}, sr, lane);
   } else {
-    Blk cur = locate(a, S, sr, lane);
-    const Q4 qraw = load_q_raw(a, cur, lane);
-    KV rc = load_kv<kBias>(a, cur, n, q4, S + 1 >= E);
+    Blk cur = locate<D>(a, S, sr, lane);
+    const Q4 qraw = load_q_raw<D>(a, cur, lane);
+    KV rc = load_kv<kBias, D>(a, cur, n, q4, S + 1 >= E);
     Acc s;
     acc_reset(s);
     bool seg_shared = cur.i > 0;          // the unit began in an earlier slice
@@ -731,9 +772,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // next (x + 2), clamped to the slice's last block; past it the loads are
     // spare ones. Q rows are loaded when their unit starts (a small,
     // cache-resident read).
-    Blk nxt = S + 1 < E ? next_block(a, cur, sr) : cur;        // block x + 1
-    KV r1 = load_kv<kBias>(a, nxt, n, q4, S + 2 >= E);
-    Blk ahead = S + 2 < E ? next_block(a, nxt, sr) : nxt;       // block x + 2
+    Blk nxt = S + 1 < E ? next_block<D>(a, cur, sr) : cur;        // block x + 1
+    KV r1 = load_kv<kBias, D>(a, nxt, n, q4, S + 2 >= E);
+    Blk ahead = S + 2 < E ? next_block<D>(a, nxt, sr) : nxt;       // block x + 2
 
     // While the first loads are in flight: this wave's table entries. Its
     // first unit leaves a partial (slot 0) if it began in an earlier slice
@@ -741,37 +782,37 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     // the slice, or if it is also the first and began earlier. The
     // segment-closing code below writes exactly these slots.
     {
-      const Blk lb = S + 1 < E ? locate(a, E - 1, sr, lane) : cur;
+      const Blk lb = S + 1 < E ? locate<D>(a, E - 1, sr, lane) : cur;
       const bool same = lb.b == cur.b && lb.ub == cur.ub;
       const bool open_end = lb.i + 1 < lb.nb;
       set_entry(a, sh_ent[2 * wv], cur.i > 0 && !same, cur, sr, lane);
       set_entry(a, sh_ent[2 * wv + 1], same ? (cur.i > 0 || open_end) : open_end, lb, sr, lane);
     }
-    Q4 qv = finish_q<T, kRot>(qraw, a, cur, lane);
+    Q4 qv = finish_q<T, kRot, D>(qraw, a, cur, lane);
 
     // one block: issue the loads of x + 2, compute x, close the segment at a
     // unit end or at the slice end. Returns false after the slice's last block.
     auto step = [&](int64_t x, KV& r_cur, KV& r_fill) -> bool {
       const bool last = x + 1 >= E;
       const bool unit_end = cur.i + 1 >= cur.nb;
-      r_fill = load_kv<kBias>(a, ahead, n, q4, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
-      compute<T, kBias, kRot>(s, r_cur, qv, cur, a, lane, vt);
+      r_fill = load_kv<kBias, D>(a, ahead, n, q4, x + 3 >= E, x + 2 >= E);   // ahead = min(x + 2, E - 1)
+      compute<T, kBias, kRot, D>(s, r_cur, qv, cur, a, lane, vt);
       if (unit_end || last) {
         const bool shared = seg_shared || !unit_end;
         if (shared) {
           // the slice's last segment goes to slot 1 (over the V tile, free now)
-          finish_segment<T>(a, s, cur, true, last ? slot1 : slot0, lane);
+          finish_segment<T, D>(a, s, cur, true, last ? slot1 : slot0, lane);
         } else {
-          finish_segment<T>(a, s, cur, false, slot0, lane);
+          finish_segment<T, D>(a, s, cur, false, slot0, lane);
         }
         if (last) return false;
         acc_reset(s);
         seg_shared = false;
-        qv = finish_q<T, kRot>(load_q_raw(a, nxt, lane), a, nxt, lane);
+        qv = finish_q<T, kRot, D>(load_q_raw<D>(a, nxt, lane), a, nxt, lane);
       }
       cur = nxt;
       nxt = ahead;
-      ahead = x + 3 < E ? next_block(a, ahead, sr) : ahead;
+      ahead = x + 3 < E ? next_block<D>(a, ahead, sr) : ahead;
       return true;
     };
     KV r2;
@@ -810,8 +851,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
     for (int f = 0; f < 2 * kDecodeWaves; ++f) um |= (key[f] == u.unit ? 1u : 0u) << f;
     const bool inside = u.w_first >= wg * kDecodeWaves && u.w_last < (wg + 1) * kDecodeWaves;
     float* gslot = a.partials + int64_t(wg + u.unit) * kSlotFloats;
-    for (int idx = tid; idx < u.nheads * kD; idx += kThreads) {
-      const int h = idx / kD, d = idx % kD;
+    for (int idx = tid; idx < u.nheads * D; idx += kThreads) {
+      const int h = idx / D, d = idx % D;
       float m[2 * kDecodeWaves], l[2 * kDecodeWaves], o[2 * kDecodeWaves];
 #pragma unroll
       for (int f = 0; f < 2 * kDecodeWaves; ++f) {
@@ -836,7 +877,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
         O = fmaf(o[f], wgt, O);
       }
       if (inside) {
-        store_out<T>(a, u.b, u.h0 + h, d, O / L);
+        store_out<T, D>(a, u.b, u.h0 + h, d, O / L);
       } else {
         __hip_atomic_store(gslot + h * kD + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) {
@@ -876,13 +917,14 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   float* mlds = reinterpret_cast<float*>(lds);       // the slots are read: reuse
 #pragma unroll 1
   for (int j = 0; j < nglob; ++j)                     // one copy of the merge code
-    if (sh_flag[j]) merge_unit<T>(a, read_entry(sh_ent[j ? gent1 : gent0]), mlds);
+    if (sh_flag[j]) merge_unit<T, D>(a, read_entry(sh_ent[j ? gent1 : gent0]), mlds);
 }
 
 // Fused eviction, before the decode kernel: for the last block i of every
 // worker's slice whose unit goes on into the next worker's slice, copy the
 // first source row of block i + 1 (key 16 i + 15's source), which block
 // i + 1's shifted stores, made by another wave, may overwrite first.
+template <int D>
 __global__ void __launch_bounds__(64) shift_halo_kernel(DecodeArgs a) {
   // one wave per worker (its plan values stay scalar): lanes 0-15 copy the K
   // row, lanes 16-31 the V row, 16 bytes each
@@ -898,12 +940,12 @@ __global__ void __launch_bounds__(64) shift_halo_kernel(DecodeArgs a) {
   if (S >= E) return;
   // all 64 lanes take part in the lookup (one lane per sequence)
   const SeqRegs sr = load_seq_regs(a, lane);
-  const Blk k = locate(a, E - 1, sr, lane);
-  if (lane >= 32 || !k.d || k.i + 1 >= k.nb) return;
-  const bool vside = lane >= 16;
+  const Blk k = locate<D>(a, E - 1, sr, lane);
   const int part = lane & 15;
-  const uint16_t* src = (vside ? k.vc : k.kc) + int64_t(k.kb + kKeys - 1 + k.d) * kD;
-  uint16_t* dst = (vside ? a.halo_v : a.halo_k) + int64_t(w) * kD;
+  if (lane >= 32 || !k.d || k.i + 1 >= k.nb || 8 * part >= D) return;
+  const bool vside = lane >= 16;
+  const uint16_t* src = (vside ? k.vc : k.kc) + int64_t(k.kb + kKeys - 1 + k.d) * D;
+  uint16_t* dst = (vside ? a.halo_v : a.halo_k) + int64_t(w) * D;
   *reinterpret_cast<uint4*>(dst + 8 * part) = *reinterpret_cast<const uint4*>(src + 8 * part);
 }
 
@@ -917,10 +959,36 @@ bool decode_fused_evict_supported(const Problem& p) {
 }
 
 bool decode_fast_supported(const Problem& p) {
-  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.S == 1;
+  return (p.D == 128 || p.D == 64) && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.S == 1;
 }
 
 namespace {
+
+// One instantiation per dtype, bias, rotary and head size.
+template <int D>
+hipError_t launch_decode_kernel(const Problem& p, const DecodeArgs& a, dim3 grid, dim3 wg,
+                                hipStream_t st) {
+  if (a.shift) {
+    hipLaunchKernelGGL(shift_halo_kernel<D>, dim3(a.workers), dim3(64), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // rotary gets kernels of its own: without the rotation code the streaming
+  // loop needs fewer registers
+  const bool fp16 = p.dtype == GQA_FP16;
+  if (a.rot) {
+    if (p.bias && fp16) hipLaunchKernelGGL((decode_kernel<F16, true, true, D>), grid, wg, 0, st, a);
+    else if (p.bias) hipLaunchKernelGGL((decode_kernel<BF16, true, true, D>), grid, wg, 0, st, a);
+    else if (fp16) hipLaunchKernelGGL((decode_kernel<F16, false, true, D>), grid, wg, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<BF16, false, true, D>), grid, wg, 0, st, a);
+  } else {
+    if (p.bias && fp16) hipLaunchKernelGGL((decode_kernel<F16, true, false, D>), grid, wg, 0, st, a);
+    else if (p.bias) hipLaunchKernelGGL((decode_kernel<BF16, true, false, D>), grid, wg, 0, st, a);
+    else if (fp16) hipLaunchKernelGGL((decode_kernel<F16, false, false, D>), grid, wg, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<BF16, false, false, D>), grid, wg, 0, st, a);
+  }
+  return hipGetLastError();
+}
 
 // One launch over at most kDecodeArgBatch sequences (their plan travels in
 // the kernel arguments).
@@ -939,7 +1007,7 @@ hipError_t launch_decode_batch(const Problem& p, void* ws, const WorkspaceLayout
   a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + lay.counters);
   a.shift = fuse_evict ? 1 : 0;
   a.halo_k = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.decode_halo);
-  a.halo_v = a.halo_k + int64_t(kDecodeMaxWorkers) * kD;
+  a.halo_v = a.halo_k + int64_t(kDecodeMaxWorkers) * p.D;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window; a.cap = p.cap;
   a.n_hg = ceil_div(p.G, kDecodeMaxHG);
   a.hg_size = ceil_div(p.G, a.n_hg);
@@ -972,27 +1040,9 @@ hipError_t launch_decode_batch(const Problem& p, void* ws, const WorkspaceLayout
   a.workers = int(workers);
   a.fits32 = (total + 1) * workers < (int64_t(1) << 32) ? 1 : 0;
   const int blocks = int((workers + kDecodeWaves - 1) / kDecodeWaves);
-  if (a.shift) {
-    hipLaunchKernelGGL(shift_halo_kernel, dim3(a.workers), dim3(64), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // rotary gets kernels of its own: without the rotation code the streaming
-  // loop needs fewer registers
-  const bool fp16 = p.dtype == GQA_FP16;
   const dim3 grid(blocks), wg(kThreads);
-  if (a.rot) {
-    if (p.bias && fp16) hipLaunchKernelGGL((decode_kernel<F16, true, true>), grid, wg, 0, st, a);
-    else if (p.bias) hipLaunchKernelGGL((decode_kernel<BF16, true, true>), grid, wg, 0, st, a);
-    else if (fp16) hipLaunchKernelGGL((decode_kernel<F16, false, true>), grid, wg, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<BF16, false, true>), grid, wg, 0, st, a);
-  } else {
-    if (p.bias && fp16) hipLaunchKernelGGL((decode_kernel<F16, true, false>), grid, wg, 0, st, a);
-    else if (p.bias) hipLaunchKernelGGL((decode_kernel<BF16, true, false>), grid, wg, 0, st, a);
-    else if (fp16) hipLaunchKernelGGL((decode_kernel<F16, false, false>), grid, wg, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<BF16, false, false>), grid, wg, 0, st, a);
-  }
-  return hipGetLastError();
+  return p.D == 128 ? launch_decode_kernel<128>(p, a, grid, wg, st)
+                    : launch_decode_kernel<64>(p, a, grid, wg, st);
 }
 
 }  // namespace

@@ -352,9 +352,11 @@ WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   l.counters_bytes = align256(size_t(B * Hkv * hg) * sizeof(int32_t));
   // decode partials: one slot of [HG_max, D + 2] fp32 per (workgroup, unit)
   // pair that can meet: at most (workgroups + units) slots
+  // (slots are laid out for head size 128, which D = 64 shares)
   int64_t partial = 0;
-  if (D == 128 && s.dtype != GQA_FP32)
-    partial = (kDecodeMaxWorkgroups + B * Hkv * hg) * int64_t(kDecodeMaxHG) * (D + 2) * 4;
+  const bool fast_decode = (D == 128 || D == 64) && s.dtype != GQA_FP32;
+  if (fast_decode)
+    partial = (kDecodeMaxWorkgroups + B * Hkv * hg) * int64_t(kDecodeMaxHG) * (128 + 2) * 4;
   // eviction halos: [B, Hkv, 2, chunks, halo rows, row bytes]
   const int64_t row_bytes = D * (s.dtype == GQA_FP32 ? 4 : 2);
   const EvictGeometry eg = evict_geometry((int)row_bytes);
@@ -362,7 +364,7 @@ WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   const int64_t halo = B * Hkv * 2 * chunks * kEvictHaloMax * row_bytes;
   // fused-eviction halo rows (decode): one K and one V row per worker, in the dtype
   int64_t dhalo = 0;
-  if (D == 128 && s.dtype != GQA_FP32) dhalo = 2 * int64_t(kDecodeMaxWorkers) * D * 2;
+  if (fast_decode) dhalo = 2 * int64_t(kDecodeMaxWorkers) * D * 2;
   // prefill split partials: [row blocks, splits] slots (only when splitting;
   // a one-token shape that the split-KV decode serves never runs the prefill)
   int64_t pf_items = 0, pf_partial = 0;

@@ -206,7 +206,7 @@ hipError_t launch_evict(const Problem& p, int incoming, int max_drop, void* ws,
 // must already hold this call's appended rows.
 hipError_t launch_attention_simple(const Problem& p, hipStream_t st);
 
-// Fast decode (fp16/bf16, D == 128, S == 1): fused append + split-KV + merge.
+// Fast decode (fp16/bf16, D == 128 or 64, S == 1): fused append + split-KV + merge.
 bool decode_fast_supported(const Problem& p);
 // Eviction folded into the decode (the window covers the buffer, one head
 // group per kv head): each kept row is moved by the wave that reads it.

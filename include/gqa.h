@@ -53,7 +53,7 @@
  *      gives its shape) takes bias[b, h, i, j + d_b] for the key at row j
  *      after an eviction of d_b rows, i.e. its column is the key's position
  *      in past ++ new. With a bias the split-KV decode (S = 1, fp16/bf16,
- *      D = 128) and the MFMA prefill (fp16/bf16, D = 128, bias_total a
+ *      D = 128 or 64) and the MFMA prefill (fp16/bf16, D = 128, bias_total a
  *      multiple of 4, bias 8-byte aligned) keep their kernels; other calls
  *      use the plain kernel.
  *
@@ -197,7 +197,7 @@ gqa_status gqa_attention_prefill(const gqa_shape* shape, const gqa_options* opts
 
 /*
  * The whole op for exactly one new token per sequence (S must be 1):
- * split-KV attention (fp16/bf16, D = 128, one launch per 64 sequences; the
+ * split-KV attention (fp16/bf16, D = 128 or 64, one launch per 64 sequences; the
  * plain kernel otherwise). The valid 16-key blocks of all (sequence, kv head) units form
  * one list cut into equal slices, one per wave; each wave streams its slice
  * once, with the new token's append fused, and a unit cut between

@@ -127,6 +127,15 @@ SMALL = [
     ("fp16", 2, 70, 8, 2, 128, 256, [255, 256], 16, True, 1, "prefill"),
     ("fp32", 2, 9, 4, 2, 8, 40, [35, 40], 40, False, 0, "prefill"),
     ("bf16", 2, 5, 6, 3, 64, 48, [48, 44], 20, True, 0, "prefill"),
+    # head size 64 on the split-KV decode: half a row per lane group, the
+    # rotation's pairs at the half-size table stride, one head group and two
+    # (G = 32), the fused eviction of a full window and the eviction kernel
+    ("bf16", 3, 1, 16, 2, 64, 700, [699, 5, 300], -1, True, 0, "decode"),
+    ("fp16", 2, 1, 32, 1, 64, 520, [519, 100], -1, True, 1, "decode"),
+    ("bf16", 2, 1, 16, 2, 64, 300, [300, 17], 300, False, 0, "decode"),
+    ("fp16", 2, 1, 8, 2, 64, 300, [299, 17], 64, True, 0, "decode"),
+    ("bf16", 64, 1, 4, 1, 64, 192, [192 if i % 3 == 0 else (29 * i) % 192 for i in range(64)],
+     192, True, 0, "decode"),
 ]
 
 
@@ -263,6 +272,8 @@ BIAS = [
     ("bf16", 2, 33, 16, 2, 128, 200, [100, 0], 40, False, "B1", 3, 0),            # window
     ("fp16", 2, 130, 28, 4, 128, 512, [380, 0], -1, False, "BH", 2, 0),           # several row blocks
     ("bf16", 2, 20, 8, 2, 128, 128, [128, 120], 128, False, "11", 1, 0),          # staging, plain kernel
+    ("fp16", 3, 1, 16, 2, 64, 600, [0, 300, 599], -1, True, "BH", 2, 0),          # D = 64 decode
+    ("bf16", 2, 1, 8, 2, 64, 256, [256, 100], 256, False, "1H", 0, 0),            # D = 64 fused
 ]
 
 
@@ -313,21 +324,22 @@ def test_many_sequences_evicting_decode(spec):
 
 
 @pytest.mark.parametrize("spec", [
-    # dtype, B, H, Hkv, M, W, rotary: more than 64 sequences run the split-KV
-    # decode as consecutive launches of 64 (here 64 + 64 + 2, and 64 + 6 with
-    # the fused eviction of a full window)
-    ("fp16", 130, 8, 2, 256, -1, True),
-    ("bf16", 70, 8, 8, 128, 128, False),
-], ids=["fp16-B130", "bf16-B70-window"])
+    # dtype, B, H, Hkv, D, M, W, rotary: more than 64 sequences run the
+    # split-KV decode as consecutive launches of 64 (here 64 + 64 + 2, and
+    # 64 + 6 with the fused eviction of a full window)
+    ("fp16", 130, 8, 2, 128, 256, -1, True),
+    ("bf16", 70, 8, 8, 128, 128, 128, False),
+    ("fp16", 70, 8, 2, 64, 128, 128, True),
+], ids=["fp16-B130", "bf16-B70-window", "fp16-B70-D64-window"])
 def test_decode_more_than_64_sequences(spec):
-    dt, B, H, Hkv, M, W, rot = spec
+    dt, B, H, Hkv, D, M, W, rot = spec
     seed = sum(map(ord, repr(spec))) % 1000
     rng = np.random.default_rng(seed)
     if W > 0:
         lens = [M if i % 4 else int(rng.integers(0, M)) for i in range(B)]
     else:
         lens = rng.integers(0, M, B).tolist()
-    case = gi.make_case("many-decode", dt, B, 1, H, Hkv, 128, M, lens, seed, window=W, rotary=rot,
+    case = gi.make_case("many-decode", dt, B, 1, H, Hkv, D, M, lens, seed, window=W, rotary=rot,
                         rotary_rows=2 * M)
     check_full(case, "decode", f"decode {B} sequences {spec}")
 
