@@ -369,7 +369,7 @@ WorkspaceLayout workspace_layout(const gqa_shape& s, int window) {
   // a one-token shape that the split-KV decode serves never runs the prefill)
   int64_t pf_items = 0, pf_partial = 0;
   const bool decode_only = s.new_tokens == 1;
-  if (D == 128 && s.dtype != GQA_FP32 && s.new_tokens > 0 && !decode_only) {
+  if ((D == 128 || D == 64) && s.dtype != GQA_FP32 && s.new_tokens > 0 && !decode_only) {
     if (prefill_may_split(B, s.new_tokens, G, Hkv, M)) {
       pf_items = ((s.new_tokens * G + kPrefillWgRows - 1) / kPrefillWgRows) * B * Hkv;
       // the plan may give one row block up to kPrefillMaxSplits ranges

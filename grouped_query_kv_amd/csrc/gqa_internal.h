@@ -214,7 +214,7 @@ bool decode_fused_evict_supported(const Problem& p);
 hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
                               hipStream_t st, bool fuse_evict);
 
-// Fast prefill (fp16/bf16, D == 128): MFMA flash attention over the cache.
+// Fast prefill (fp16/bf16, D == 128 or 64): MFMA flash attention over the cache.
 bool prefill_fast_supported(const Problem& p);
 hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout& lay,
                                hipStream_t st);

@@ -1,4 +1,5 @@
-// Flash-style attention for S >= 1 new tokens, fp16/bf16, head_size 128.
+// Flash-style attention for S >= 1 new tokens, fp16/bf16, head_size 128 or 64
+// (the template parameter D).
 //
 // One workgroup (8 waves) takes one (b, kv head) and 256 query rows, where
 // the rows of a kv head are its (position i, local head j) pairs flattened as
@@ -72,7 +73,6 @@ template <> struct Mma32<BF16> {
   }
 };
 
-constexpr int kD = 128;
 constexpr int kPrefillArgBatch = 64;          // batches whose lengths travel in the arguments
 constexpr int kBK = 64;                       // keys per tile
 #ifndef GQA_PREFILL_SETPRIO
@@ -130,17 +130,19 @@ struct PrefillArgs {
   int ho[kPrefillArgBatch];   // the same from the host, valid with hl_ok
 };
 
-// The cos/sin values one lane needs for its row's 8 B-operand chunks; chunk
-// ks holds dims 16 ks + 8 c + e. Rotate-half pairs (d, d + 64) are chunks
-// (ks, ks + 4) of the same lane and use entry 8 ks + e (table index
-// 16 ks + 8 c + e); interleaved pairs are neighbours inside a chunk and use
-// entry 4 ks + e / 2 (table index 8 ks + 4 c + e / 2). All sixteen 16-byte
+// The cos/sin values one lane needs for its row's D / 16 B-operand chunks;
+// chunk ks holds dims 16 ks + 8 c + e. Rotate-half pairs (d, d + D / 2) are
+// chunks (ks, ks + D / 32) of the same lane and use entry 8 ks + e (table
+// index 16 ks + 8 c + e); interleaved pairs are neighbours inside a chunk
+// and use entry 4 ks + e / 2 (table index 8 ks + 4 c + e / 2). Either way a
+// lane needs D / 4 entries (D / 16 float4 of each table); all its 16-byte
 // loads are issued together, before any of them is used.
 struct RotVals {
   float4 c0, c1, c2, c3, c4, c5, c6, c7;
   float4 s0, s1, s2, s3, s4, s5, s6, s7;
 };
 
+template <int D>
 __device__ __forceinline__ void load_rot(RotVals& r, const float* cosr, const float* sinr, int c,
                                          int interleaved) {
   const float4* cv = reinterpret_cast<const float4*>(cosr);
@@ -150,9 +152,13 @@ __device__ __forceinline__ void load_rot(RotVals& r, const float* cosr, const fl
   const int st = interleaved ? 2 : 1;
   auto idx = [&](int m) { return interleaved ? o0 + st * m : 4 * (m >> 1) + o0 + (m & 1); };
   r.c0 = cv[idx(0)]; r.c1 = cv[idx(1)]; r.c2 = cv[idx(2)]; r.c3 = cv[idx(3)];
-  r.c4 = cv[idx(4)]; r.c5 = cv[idx(5)]; r.c6 = cv[idx(6)]; r.c7 = cv[idx(7)];
   r.s0 = sv[idx(0)]; r.s1 = sv[idx(1)]; r.s2 = sv[idx(2)]; r.s3 = sv[idx(3)];
-  r.s4 = sv[idx(4)]; r.s5 = sv[idx(5)]; r.s6 = sv[idx(6)]; r.s7 = sv[idx(7)];
+  if (D == 128) {
+    r.c4 = cv[idx(4)]; r.c5 = cv[idx(5)]; r.c6 = cv[idx(6)]; r.c7 = cv[idx(7)];
+    r.s4 = sv[idx(4)]; r.s5 = sv[idx(5)]; r.s6 = sv[idx(6)]; r.s7 = sv[idx(7)];
+  } else {
+    r.c4 = r.c5 = r.c6 = r.c7 = r.s4 = r.s5 = r.s6 = r.s7 = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 }
 
 __device__ __forceinline__ float rot_entry(const RotVals& r, int i, bool sine) {
@@ -173,19 +179,19 @@ __device__ __forceinline__ float rot_entry(const RotVals& r, int i, bool sine) {
 // tolerance; K rows written to the cache use the exact rule of
 // rotate_pair. The fp64 form here was about a third of each workgroup's
 // start (fp64 conversions run at a quarter of the fp32 rate).
-template <class T>
-__device__ __forceinline__ void apply_rot_q(uint4 (&qv)[8], const RotVals& r, int interleaved) {
+template <class T, int D>
+__device__ __forceinline__ void apply_rot_q(uint4 (&qv)[D / 16], const RotVals& r, int interleaved) {
   using Bits = typename T::bits;
   auto lo = [](uint32_t w) { return T::to_float(Bits(w & 0xFFFFu)); };
   auto hi = [](uint32_t w) { return T::to_float(Bits(w >> 16)); };
   if (!interleaved) {
-    // pairs (chunk ks element e, chunk ks + 4 element e): two per word
+    // pairs (chunk ks element e, chunk ks + D / 32 element e): two per word
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t& wx = (&qv[ks].x)[j];
-        uint32_t& wy = (&qv[ks + 4].x)[j];
+        uint32_t& wy = (&qv[ks + D / 32].x)[j];
         const float c0 = rot_entry(r, 8 * ks + 2 * j, false), s0 = rot_entry(r, 8 * ks + 2 * j, true);
         const float c1 = rot_entry(r, 8 * ks + 2 * j + 1, false);
         const float s1 = rot_entry(r, 8 * ks + 2 * j + 1, true);
@@ -197,7 +203,7 @@ __device__ __forceinline__ void apply_rot_q(uint4 (&qv)[8], const RotVals& r, in
   } else {
     // pairs are the two elements of a word
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t& w = (&qv[ks].x)[j];
@@ -210,43 +216,58 @@ __device__ __forceinline__ void apply_rot_q(uint4 (&qv)[8], const RotVals& r, in
 }
 
 // ---------------------------------------------------------------------------
-// Tiles in LDS. K and V tiles are row-major, 64 keys x 256 bytes, filled
+// Tiles in LDS. K and V tiles are row-major, 64 keys x 2 D bytes, filled
 // straight from HBM by buffer_load_dwordx4 ... lds (no register staging): one
-// instruction moves four 256-byte rows, lane i writing 16-byte slot i. The
-// buffer range ends at the valid length, so rows past it read as zeros.
-// Within a row the sixteen 16-byte chunks are XOR-swizzled per key so that
-// the operand reads below are free of bank conflicts (16 lanes of a b128
-// read, 32 lanes of a b64 read per cycle):
-//   K: chunk ^ (key & 15)     (b128 reads of 16 consecutive keys)
-//   V: chunk ^ 4 (key & 3)    (transposing b64 reads, 4 keys x 2 dim groups)
+// instruction moves 1 KB, lane i writing 16-byte slot i (four 256-byte rows
+// at D = 128, eight 128-byte rows at D = 64). The buffer range ends at the
+// valid length, so rows past it read as zeros. Within a row the D / 8
+// 16-byte chunks are XOR-swizzled per key so that the operand reads below
+// are free of bank conflicts (64 banks of 4 bytes: 16 lanes of a b128 read,
+// 32 lanes of a b64 read per cycle, 256 bytes either way):
+//   D = 128  K: chunk ^ (key & 15)          (b128 reads of 16 consecutive keys)
+//            V: chunk ^ 4 (key & 3)         (transposing b64 reads, 4 keys x 2 dim groups)
+//   D = 64   K: chunk ^ ((key >> 1) & 7)    (two keys per 256 bytes: 2 x 8 chunks)
+//            V: chunk ^ 4 ((key >> 1) & 1)  (4 keys x 4 chunks x 2 halves)
 // ---------------------------------------------------------------------------
-constexpr int kTileBytes = kBK * kD * 2;      // 16 KB
+template <int D> constexpr int tile_bytes() { return kBK * D * 2; }   // 16 KB or 8 KB
 
-__device__ inline int swz_k(int key) { return key & 15; }
-__device__ inline int swz_v(int key) { return (key & 3) << 2; }
+template <int D> __device__ inline int swz_k(int key) { return D == 128 ? key & 15 : (key >> 1) & 7; }
+template <int D> __device__ inline int swz_v(int key) {
+  return D == 128 ? (key & 3) << 2 : ((key >> 1) & 1) << 2;
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Per-lane byte offsets of the tile loads, relative to the tile's first key.
-// Wave w moves rows 8 w + 4 q + lane / 16 (q = 0, 1); the K swizzle depends
-// on the row only through key & 15 = (8 w + 4 q + lane / 16) & 15 (tiles
-// start at multiples of 64), the V swizzle only through lane / 16.
+// Wave w moves rows 8 w .. 8 w + 7 of a tile. D = 128: rows 8 w + 4 q +
+// lane / 16 (q = 0, 1); the K swizzle depends on the row only through
+// key & 15 = (8 w + 4 q + lane / 16) & 15 (tiles start at multiples of 64),
+// the V swizzle only through lane / 16. D = 64: one instruction, row
+// 8 w + lane / 8, chunk lane % 8.
 struct LoadOffsets {
   int k[2];
   int v;         // V: one pattern; quad q adds 1024 q
 };
 
+template <int D>
 __device__ inline LoadOffsets load_offsets(int wave, int lane) {
   LoadOffsets lo;
-  const int lr = lane >> 4, slot = lane & 15;
+  if (D == 128) {
+    const int lr = lane >> 4, slot = lane & 15;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int rrow = 8 * wave + 4 * q + lr;
-    lo.k[q] = rrow * 256 + 16 * (slot ^ swz_k(rrow));
+    for (int q = 0; q < 2; ++q) {
+      const int rrow = 8 * wave + 4 * q + lr;
+      lo.k[q] = rrow * 256 + 16 * (slot ^ swz_k<D>(rrow));
+    }
+    lo.v = (8 * wave + lr) * 256 + 16 * (slot ^ swz_v<D>(lr));
+  } else {
+    const int rrow = 8 * wave + (lane >> 3), slot = lane & 7;
+    lo.k[0] = rrow * 128 + 16 * (slot ^ swz_k<D>(rrow));
+    lo.k[1] = lo.k[0];
+    lo.v = rrow * 128 + 16 * (slot ^ swz_v<D>(rrow));
   }
-  lo.v = (8 * wave + lr) * 256 + 16 * (slot ^ swz_v(lr));
   return lo;
 }
 
@@ -269,15 +290,21 @@ __device__ inline void quad_load(__amdgpu_buffer_rsrc_t rsrc, unsigned char* til
                                              16, lo.k[Q], 0, 0, 0);
 }
 
-template <bool kIsV>
+template <bool kIsV, int D>
 __device__ inline void tile_load(const uint16_t* base, int kvalid, unsigned char* tile, int t0,
                                  const LoadOffsets& lo, int wave) {
   t0 = __builtin_amdgcn_readfirstlane(t0);      // the tile start is wave-uniform
   const int rows = max(0, kvalid - t0);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(base + int64_t(t0) * kD), 0, rows * kD * 2, 0x00020000);
-  quad_load<kIsV, 0>(rsrc, tile, lo, wave);
-  quad_load<kIsV, 1>(rsrc, tile, lo, wave);
+      const_cast<uint16_t*>(base + int64_t(t0) * D), 0, rows * D * 2, 0x00020000);
+  if (D == 128) {
+    quad_load<kIsV, 0>(rsrc, tile, lo, wave);
+    quad_load<kIsV, 1>(rsrc, tile, lo, wave);
+  } else {
+    // the wave's eight 128-byte rows in one instruction
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 8 * wave * 128), 16,
+                                             kIsV ? lo.v : lo.k[0], 0, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -296,8 +323,8 @@ struct BiasTile {
   uint2 v[8];
 };
 
-template <class T, bool kMask, bool kBias>
-__device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4], uint4 (&pk)[4],
+template <class T, bool kMask, bool kBias, int D>
+__device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[D / 32], uint4 (&pk)[4],
                                     float cs, int lim_hi, int span, const BiasTile& bt,
                                     float bias_mul) {
   if (kBias) {
@@ -346,7 +373,7 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
     const float use_new = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(rs.m_use - use_new);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
     rs.l *= alpha;
@@ -373,25 +400,26 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], RowState& rs, f32x16 (&o)[4]
 
 // S^T (64 keys) = K Q^T for the lane's row; A = K rows (key 32 h + col,
 // dims 16 kk + 8 c .. + 7), B = Q^T.
-template <class T>
-__device__ inline void scores_tile(const unsigned char* kt, const uint4 (&qv)[8], f32x16 (&s)[2],
-                                   int col, int c) {
+template <class T, int D>
+__device__ inline void scores_tile(const unsigned char* kt, const uint4 (&qv)[D / 16],
+                                   f32x16 (&s)[2], int col, int c) {
   // the two 32-key halves are independent accumulation chains: alternate
-  // them so that consecutive products never wait on each other
-  const unsigned char* k0 = kt + col * 256;
-  const unsigned char* k1 = kt + (32 + col) * 256;
-  const int sw = swz_k(col);
+  // them so that consecutive products never wait on each other (keys col
+  // and 32 + col share their swizzle)
+  const unsigned char* k0 = kt + col * (2 * D);
+  const unsigned char* k1 = kt + (32 + col) * (2 * D);
+  const int sw = swz_k<D>(col);
   s[0] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k0 + 16 * (c ^ sw)), qv[0], f32x16{});
   s[1] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k1 + 16 * (c ^ sw)), qv[0], f32x16{});
 #pragma unroll
-  for (int kk = 1; kk < 8; ++kk) {
+  for (int kk = 1; kk < D / 16; ++kk) {
     s[0] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k0 + 16 * ((2 * kk + c) ^ sw)), qv[kk], s[0]);
     s[1] = Mma32<T>::run(*reinterpret_cast<const uint4*>(k1 + 16 * ((2 * kk + c) ^ sw)), qv[kk], s[1]);
   }
   // operand reads kPrefetch products ahead
   __builtin_amdgcn_sched_group_barrier(0x100, GQA_PREFILL_READ_AHEAD, 0);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < D / 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
@@ -402,20 +430,20 @@ __device__ inline void scores_tile(const unsigned char* kt, const uint4 (&qv)[8]
 // from two transposing reads: in each 16-lane group, lane j points at key
 // kb + j / 4, dims 4 (j % 4) .. + 3 of the group's 16 dims, and lane 4 a + e
 // receives dim 4 a + e of the four keys.
-template <class T>
-__device__ inline void pv_tile(const unsigned char* vt, const uint4 (&pk)[4], f32x16 (&o)[4],
+template <class T, int D>
+__device__ inline void pv_tile(const unsigned char* vt, const uint4 (&pk)[4], f32x16 (&o)[D / 32],
                                int lane) {
   const int j = lane & 15, c = lane >> 5, g1 = (lane >> 4) & 1;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 32; ++dt) {
       uint32_t w[4];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int key = 16 * u + 8 * r + 4 * c + (j >> 2);
         const int ch = 4 * dt + 2 * g1 + ((j & 3) >> 1);
-        const unsigned char* ptr = vt + key * 256 + 16 * (ch ^ swz_v(key)) + 8 * (j & 1);
+        const unsigned char* ptr = vt + key * (2 * D) + 16 * (ch ^ swz_v<D>(key)) + 8 * (j & 1);
         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ptr));
         const uint2 xx = __builtin_bit_cast(uint2, x);
         w[2 * r] = xx.x;
@@ -427,7 +455,7 @@ __device__ inline void pv_tile(const unsigned char* vt, const uint4 (&pk)[4], f3
   // operand reads kPrefetch products ahead of the products that use them
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * GQA_PREFILL_READ_AHEAD, 0);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < D / 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
@@ -444,23 +472,24 @@ __device__ inline void pv_tile(const unsigned char* vt, const uint4 (&pk)[4], f3
 // and V(t) go to the free LDS buffers at the start of phase 2t (the tiles
 // they replace were last read in phase 2t - 1) and are waited for at the
 // end of phase 2t + 1.
-template <class T>
+template <class T, int D>
 __device__ inline void products(int t, int wt0, int wt1, const unsigned char* kt,
-                                const unsigned char* vt, const uint4 (&qv)[8], const uint4 (&pk)[4],
-                                f32x16 (&o)[4], f32x16 (&sc)[2], int col, int c, int lane) {
+                                const unsigned char* vt, const uint4 (&qv)[D / 16],
+                                const uint4 (&pk)[4], f32x16 (&o)[D / 32], f32x16 (&sc)[2], int col,
+                                int c, int lane) {
 #if GQA_PREFILL_SETPRIO
   __builtin_amdgcn_s_setprio(GQA_PREFILL_SETPRIO);
 #endif
-  if (t - 1 >= wt0 && t - 1 < wt1) pv_tile<T>(vt, pk, o, lane);
-  if (t >= wt0 && t < wt1) scores_tile<T>(kt, qv, sc, col, c);
+  if (t - 1 >= wt0 && t - 1 < wt1) pv_tile<T, D>(vt, pk, o, lane);
+  if (t >= wt0 && t < wt1) scores_tile<T, D>(kt, qv, sc, col, c);
 #if GQA_PREFILL_SETPRIO
   __builtin_amdgcn_s_setprio(0);
 #endif
 }
 
-template <class T, bool kBias>
+template <class T, bool kBias, int D>
 __device__ inline void softmax_step(int t, int wt0, int wt1, f32x16 (&sc)[2], RowState& rs,
-                                    f32x16 (&o)[4], uint4 (&pk)[4], float cs, int my_p, int span,
+                                    f32x16 (&o)[D / 32], uint4 (&pk)[4], float cs, int my_p, int span,
                                     int w_full_lo, int w_full_hi, int c, const BiasTile& bt,
                                     float bias_mul) {
   if (t < wt0 || t >= wt1) return;
@@ -468,9 +497,9 @@ __device__ inline void softmax_step(int t, int wt0, int wt1, f32x16 (&sc)[2], Ro
   const bool full = tb + kBK - 1 <= w_full_hi && tb >= w_full_lo;
   const int lim_hi = my_p - (tb + 4 * c);
   if (full)
-    softmax_tile<T, false, kBias>(sc, rs, o, pk, cs, lim_hi, span, bt, bias_mul);
+    softmax_tile<T, false, kBias, D>(sc, rs, o, pk, cs, lim_hi, span, bt, bias_mul);
   else
-    softmax_tile<T, true, kBias>(sc, rs, o, pk, cs, lim_hi, span, bt, bias_mul);
+    softmax_tile<T, true, kBias, D>(sc, rs, o, pk, cs, lim_hi, span, bt, bias_mul);
 }
 
 // The bias values of tile t for the lane's row. Columns are clamped to the
@@ -487,8 +516,10 @@ __device__ inline void bias_load(BiasTile& bt, const uint16_t* brow, int t, int 
     }
 }
 
-template <class T, bool kBias>
+template <class T, bool kBias, int D>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
+  constexpr int kTileBytes = tile_bytes<D>();
+  constexpr int kRowBytes = 2 * D;
   // four separately declared tiles, each used at fixed places of the
   // two-iteration loop body: the compiler can then tell the tiles being read
   // from the tiles being filled by direct-to-LDS loads and does not wait for
@@ -566,26 +597,27 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int wt0 = wave_has_rows ? max(w_kstart / kBK, t_begin) : t_end;
   const int wt1 = wave_has_rows ? min((w_kend + kBK - 1) / kBK, t_end) : t_end;
 
-  const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.kv_rows * kD;
+  const int64_t kvbase = (int64_t(b) * a.Hkv + g) * a.kv_rows * D;
   const uint16_t* kc = a.k_cache + kvbase;
   const uint16_t* vc = a.v_cache + kvbase;
   // tiles at or past `stage_from` come from the staging frame (same key rows)
   const int stage_from = a.k_stage ? (L & ~(kBK - 1)) : INT_MAX;
-  const int64_t sbase = (int64_t(b) * a.Hkv + g) * a.M * kD;
+  const int64_t sbase = (int64_t(b) * a.Hkv + g) * a.M * D;
   const uint16_t* k_frame = a.k_stage ? a.k_stage + sbase : kc;
   const uint16_t* v_frame = a.k_stage ? a.v_stage + sbase : vc;
 
-  const LoadOffsets lo = load_offsets(wave, lane);
-  tile_load<false>(t_begin * kBK < stage_from ? kc : k_frame, kvalid, k_even, t_begin * kBK, lo, wave);
+  const LoadOffsets lo = load_offsets<D>(wave, lane);
+  tile_load<false, D>(t_begin * kBK < stage_from ? kc : k_frame, kvalid, k_even, t_begin * kBK, lo,
+                      wave);
 
   // ---- Q^T (B operand): lane holds Q[row][16 ks + 8 c + e] ----
-  uint4 qv[8];
+  uint4 qv[D / 16];
   {
-    const uint16_t* qrow = a.q + ((int64_t(b) * S + my_i) * a.H + my_h) * kD + 8 * c;
+    const uint16_t* qrow = a.q + ((int64_t(b) * S + my_i) * a.H + my_h) * D + 8 * c;
     // lanes past the last row read a valid row (my_i = S - 1): rows never
     // mix, and those lanes store nothing, so no load waits on a branch
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
+    for (int ks = 0; ks < D / 16; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
     if (a.rot) {
       int off = 0;
       if (a.hl_ok) {
@@ -596,19 +628,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       }
       const int pos = clamp_len(len_raw + off + my_i, 0, a.rot_rows - 1);
       RotVals rv;
-      load_rot(rv, a.cosv + int64_t(pos) * (kD / 2), a.sinv + int64_t(pos) * (kD / 2), c,
-               a.interleaved);
-      apply_rot_q<T>(qv, rv, a.interleaved);
+      load_rot<D>(rv, a.cosv + int64_t(pos) * (D / 2), a.sinv + int64_t(pos) * (D / 2), c,
+                  a.interleaved);
+      apply_rot_q<T, D>(qv, rv, a.interleaved);
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks) {
       qv[ks].x ^= a.q_sign; qv[ks].y ^= a.q_sign; qv[ks].z ^= a.q_sign; qv[ks].w ^= a.q_sign;
     }
   }
 
-  f32x16 o[4];
+  f32x16 o[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
   RowState rs{-INFINITY, 0.f, 0.f};
@@ -639,8 +671,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   };
   auto loads = [&](int t, unsigned char* kn, unsigned char* vn) {
     if (t + 1 < t_end)
-      tile_load<false>((t + 1) * kBK < stage_from ? kc : k_frame, kvalid, kn, (t + 1) * kBK, lo, wave);
-    if (t < t_end) tile_load<true>(t * kBK < stage_from ? vc : v_frame, kvalid, vn, t * kBK, lo, wave);
+      tile_load<false, D>((t + 1) * kBK < stage_from ? kc : k_frame, kvalid, kn, (t + 1) * kBK, lo,
+                          wave);
+    if (t < t_end)
+      tile_load<true, D>(t * kBK < stage_from ? vc : v_frame, kvalid, vn, t * kBK, lo, wave);
   };
   // bias of tile t for this lane's row: group 0 issues it before the step's
   // tile loads and uses it after the products (its wait then does not take
@@ -656,20 +690,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
                    unsigned char* vn) {
     bias_tile(t);
     loads(t, kn, vn);
-    products<T>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
+    products<T, D>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
     phase_barrier();
-    softmax_step<T, kBias>(t, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c, bt,
-                           a.bias_mul);
+    softmax_step<T, kBias, D>(t, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c,
+                              bt, a.bias_mul);
     tiles_landed_barrier();
   };
   auto step1 = [&](int t, const unsigned char* kt, const unsigned char* vt, unsigned char* kn,
                    unsigned char* vn) {
     loads(t, kn, vn);
-    softmax_step<T, kBias>(t - 1, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi, c,
-                           bt, a.bias_mul);
+    softmax_step<T, kBias, D>(t - 1, wt0, wt1, sc, rs, o, pk, cs, my_p, span, w_full_lo, w_full_hi,
+                              c, bt, a.bias_mul);
     phase_barrier();
     bias_tile(t);
-    products<T>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
+    products<T, D>(t, wt0, wt1, kt, vt, qv, pk, o, sc, col, c, lane);
     tiles_landed_barrier();
   };
   if (grp == 0) {
@@ -693,7 +727,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     float* slots = a.partials + int64_t(item) * kPrefillMaxSplits * int64_t(kPrefillSlotFloats);
     float* mine = slots + int64_t(split) * kPrefillSlotFloats;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         __hip_atomic_store(mine + (wave * 64 + dt * 16 + v) * 64 + lane, o[dt][v],
@@ -738,9 +772,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       }
     }
     float l_acc = 0.f;
-    f32x16 acc[4];
+    f32x16 acc[D / 32];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
 #pragma unroll
@@ -751,12 +785,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
       if (j == split) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[dt][v] = fmaf(o[dt][v], wj, acc[dt][v]);
       } else {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             acc[dt][v] = fmaf(__hip_atomic_load(sj + (wave * 64 + dt * 16 + v) * 64 + lane,
@@ -766,41 +800,43 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     }
     l_row = l_acc;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = acc[dt];
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = acc[dt];
   }
   // ---- the output. A lane holds dims 32 dt + 8 v4 + 4 c .. + 3 of its row,
   // so storing from registers writes 16-byte pieces of 32 rows per
-  // instruction; instead the wave's 32 rows go through its own 8 KB of LDS
-  // (the tiles are free: every wave has passed the last tile's barrier) and
-  // each store instruction writes four whole 256-byte rows. Chunks are
-  // XOR-swizzled by row, so the 8-byte writes and the 16-byte reads are
-  // free of bank conflicts. ----
+  // instruction; instead the wave's 32 rows go through its own 64 D bytes
+  // of LDS (the tiles are free: every wave has passed the last tile's
+  // barrier) and each store instruction writes 1 KB of whole rows. Chunks
+  // are XOR-swizzled by row like the K tile. ----
   const float inv = row_ok ? 1.f / l_row : 0.f;
   unsigned char* stage = (wave < 2 ? k_even : wave < 4 ? k_odd : wave < 6 ? v_even : v_odd) +
                          (wave & 1) * (kTileBytes / 2);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
       uint2 w;
       w.x = Mma32<T>::pack2(o[dt][4 * v4] * inv, o[dt][4 * v4 + 1] * inv);
       w.y = Mma32<T>::pack2(o[dt][4 * v4 + 2] * inv, o[dt][4 * v4 + 3] * inv);
-      *reinterpret_cast<uint2*>(stage + col * 256 + (((4 * dt + v4) ^ (col & 15)) << 4) + 8 * c) = w;
+      *reinterpret_cast<uint2*>(stage + col * kRowBytes + (((4 * dt + v4) ^ swz_k<D>(col)) << 4) +
+                                8 * c) = w;
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // lane: row 4 k + lane / 16 of the wave, chunk lane % 16
-  const int ch = lane & 15;
-  int out_i = (wr0 + (lane >> 4)) / G;
-  int out_j = wr0 + (lane >> 4) - out_i * G;
+  // lane: row kRowsPer k + lane / kChunks of the wave, chunk lane % kChunks
+  constexpr int kChunks = D / 8;                 // 16-byte chunks per row
+  constexpr int kRowsPer = 64 / kChunks;         // rows per store instruction
+  const int ch = lane % kChunks;
+  int out_i = (wr0 + lane / kChunks) / G;
+  int out_j = wr0 + lane / kChunks - out_i * G;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int rr = 4 * k + (lane >> 4);
-    const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * 256 + ((ch ^ (rr & 15)) << 4));
+  for (int k = 0; k < 32 / kRowsPer; ++k) {
+    const int rr = kRowsPer * k + lane / kChunks;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * kRowBytes + ((ch ^ swz_k<D>(rr)) << 4));
     if (wr0 + rr < nrows)
-      *reinterpret_cast<uint4*>(a.out + ((int64_t(b) * S + out_i) * a.H + g * G + out_j) * kD + 8 * ch) = v;
-    out_j += 4;
+      *reinterpret_cast<uint4*>(a.out + ((int64_t(b) * S + out_i) * a.H + g * G + out_j) * D + 8 * ch) = v;
+    out_j += kRowsPer;
     while (out_j >= G) {
       out_j -= G;
       ++out_i;
@@ -819,11 +855,25 @@ bool prefill_fast_supported(const Problem& p) {
                                        reinterpret_cast<uintptr_t>(p.sin)) & 15) == 0;
   // a bias is read four columns per 8-byte load
   const bool bias_ok = !p.bias || (p.bias_T % 4 == 0 && (reinterpret_cast<uintptr_t>(p.bias) & 7) == 0);
-  return p.D == 128 && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) && p.M <= (1 << 23) &&
+  return (p.D == 128 || p.D == 64) && (p.dtype == GQA_FP16 || p.dtype == GQA_BF16) &&
+         p.M <= (1 << 23) &&
          rot_aligned && bias_ok;
 }
 
 namespace {
+template <int D>
+void launch_prefill_kernel(const Problem& p, const PrefillArgs& a, int blocks, hipStream_t st) {
+  const bool fp16 = p.dtype == GQA_FP16;
+  if (p.bias && fp16)
+    hipLaunchKernelGGL((prefill_kernel<F16, true, D>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else if (p.bias)
+    hipLaunchKernelGGL((prefill_kernel<BF16, true, D>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else if (fp16)
+    hipLaunchKernelGGL((prefill_kernel<F16, false, D>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<BF16, false, D>), dim3(blocks), dim3(kThreads), 0, st, a);
+}
+
 int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -914,15 +964,8 @@ hipError_t launch_prefill_fast(const Problem& p, void* ws, const WorkspaceLayout
     }
     blocks = a.plan_n;
   }
-  const bool fp16 = p.dtype == GQA_FP16;
-  if (p.bias && fp16)
-    hipLaunchKernelGGL((prefill_kernel<F16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else if (p.bias)
-    hipLaunchKernelGGL((prefill_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else if (fp16)
-    hipLaunchKernelGGL((prefill_kernel<F16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+  if (p.D == 128) launch_prefill_kernel<128>(p, a, blocks, st);
+  else launch_prefill_kernel<64>(p, a, blocks, st);
   return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@
  *      gives its shape) takes bias[b, h, i, j + d_b] for the key at row j
  *      after an eviction of d_b rows, i.e. its column is the key's position
  *      in past ++ new. With a bias the split-KV decode (S = 1, fp16/bf16,
- *      D = 128 or 64) and the MFMA prefill (fp16/bf16, D = 128, bias_total a
+ *      D = 128 or 64) and the MFMA prefill (fp16/bf16, D = 128 or 64, bias_total a
  *      multiple of 4, bias 8-byte aligned) keep their kernels; other calls
  *      use the plain kernel.
  *
@@ -171,7 +171,7 @@ gqa_status gqa_append_kv(const gqa_shape* shape, const gqa_options* opts,
 
 /*
  * The whole op for S >= 1 new tokens per sequence (steps 1-4): fused
- * flash-style attention on MFMA for fp16/bf16 with D = 128, a plain
+ * flash-style attention on MFMA for fp16/bf16 with D = 128 or 64, a plain
  * kernel otherwise. When the shape has too few 256-row blocks to fill the
  * GPU, each block's key range is split over several workgroups whose
  * partials (kept in the workspace) the last one merges by log-sum-exp.

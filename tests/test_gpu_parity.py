@@ -136,6 +136,16 @@ SMALL = [
     ("fp16", 2, 1, 8, 2, 64, 300, [299, 17], 64, True, 0, "decode"),
     ("bf16", 64, 1, 4, 1, 64, 192, [192 if i % 3 == 0 else (29 * i) % 192 for i in range(64)],
      192, True, 0, "decode"),
+    # head size 64 on the MFMA prefill: 128-byte tile rows, four products per
+    # score tile and two output tiles; several row blocks, G = 7, the
+    # key-split plan (plain and windowed), both rotary pair orders and a
+    # windowed chunk that evicts (staging frame)
+    ("bf16", 2, 130, 32, 8, 64, 512, [0, 300], -1, True, 0, "prefill"),
+    ("fp16", 2, 64, 28, 4, 64, 300, [63, 1], -1, False, 0, "prefill"),
+    ("fp16", 3, 40, 8, 2, 64, 2048, [0, 700, 1999], -1, True, 1, "prefill"),
+    ("bf16", 2, 33, 16, 2, 64, 2048, [1500, 0], 100, False, 0, "prefill"),
+    ("fp16", 2, 70, 8, 2, 64, 256, [255, 256], 16, True, 1, "prefill"),
+    ("bf16", 2, 40, 8, 2, 64, 2048, [2040, 1000], 1024, True, 0, "prefill"),
 ]
 
 
@@ -274,6 +284,8 @@ BIAS = [
     ("bf16", 2, 20, 8, 2, 128, 128, [128, 120], 128, False, "11", 1, 0),          # staging, plain kernel
     ("fp16", 3, 1, 16, 2, 64, 600, [0, 300, 599], -1, True, "BH", 2, 0),          # D = 64 decode
     ("bf16", 2, 1, 8, 2, 64, 256, [256, 100], 256, False, "1H", 0, 0),            # D = 64 fused
+    ("fp16", 2, 33, 8, 2, 64, 200, [0, 100], -1, True, "BH", 3, 0),               # D = 64 prefill
+    ("bf16", 3, 40, 8, 2, 64, 2048, [0, 700, 1999], -1, False, "1H", 1, 0),       # D = 64 split
 ]
 
 
@@ -658,7 +670,7 @@ def test_concurrent_streams_with_own_workspaces():
 # prefill then decodes equals a one-shot prefill (the worked example's story)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp32", 8)])
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("fp32", 8)])
 def test_prefill_then_decodes_match_one_shot(dt, D):
     import torch
     n, k = 70, 5
@@ -684,7 +696,7 @@ def test_prefill_then_decodes_match_one_shot(dt, D):
 
 
 @pytest.mark.parametrize("dt,D,lens", [("fp16", 128, [0, 0]), ("bf16", 128, [0, 0]),
-                                       ("fp32", 8, [0, 0])])
+                                       ("bf16", 64, [0, 0]), ("fp32", 8, [0, 0])])
 def test_prefill_then_chunks_match_one_shot(dt, D, lens):
     """A prefill of n tokens followed by continuation chunks of 37 and 90
     tokens gives, for each chunk, the same rows as a one-shot prefill of all

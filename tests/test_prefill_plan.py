@@ -57,8 +57,9 @@ def layout(B, S, H, Hkv, D, M, dt_bytes, window):
     G = H // Hkv
     hg = cdiv(G, DECODE_HG)
     counters_bytes = align256(B * Hkv * hg * 4)
-    fast = D == 128 and dt_bytes == 2
-    partial = (DECODE_WG + B * Hkv * hg) * DECODE_HG * (D + 2) * 4 if fast else 0
+    fast = D in (128, 64) and dt_bytes == 2
+    # decode partial slots are laid out for head size 128 (D = 64 uses half)
+    partial = (DECODE_WG + B * Hkv * hg) * DECODE_HG * (128 + 2) * 4 if fast else 0
     row_bytes = D * dt_bytes
     halo = B * Hkv * 2 * cdiv(M, EVICT_CHUNK_ROWS) * EVICT_HALO_MAX * row_bytes
     dhalo = 2 * DECODE_WG * DECODE_WAVES * D * 2 if fast else 0
@@ -170,9 +171,9 @@ def check_call(B, S, H, Hkv, M, W, lens, cap, cus=256, dt_bytes=2):
     return len(entries)
 
 
-def lib_workspace(B, S, H, Hkv, M, W, dt):
+def lib_workspace(B, S, H, Hkv, M, W, dt, D=128):
     import grouped_query_kv_amd as gqa
-    shape = gqa.Shape(B, S, H, Hkv, 128, M, dt)
+    shape = gqa.Shape(B, S, H, Hkv, D, M, dt)
     opts = gqa.Options(0.0, W, None, None, 0, 0)
     return int(gqa.lib.gqa_workspace_bytes(ctypes.byref(shape), ctypes.byref(opts)))
 
@@ -230,15 +231,16 @@ def test_plan_bounds_on_random_shapes():
 
 def test_model_workspace_equals_the_library():
     """The model's layout is the library's: equal gqa_workspace_bytes for the
-    named shapes, random shapes and both 2-byte dtypes, with and without a
-    window."""
+    named shapes, random shapes, head sizes 128, 64 and 8 and all three
+    dtypes, with and without a window."""
     shapes = [(s[0], s[1], s[2], s[3], s[4], s[5]) for s in NAMED]
     shapes += [(B, S, H, Hkv, M, W) for B, S, H, Hkv, M, W, _, _ in random_shapes(150, 9)]
     shapes += [(16, 1, 32, 8, 4096, -1), (8, 1, 32, 8, 4096, 4096), (66, 1, 8, 2, 96, 64)]
     for B, S, H, Hkv, M, W in shapes:
-        for dt in (1, 2):
-            assert lib_workspace(B, S, H, Hkv, M, W, dt) == layout(B, S, H, Hkv, 128, M, 2, W)[0], \
-                (B, S, H, Hkv, M, W, dt)
+        for D in (128, 64, 8):
+            for dt in (0, 1, 2):
+                want = layout(B, S, H, Hkv, D, M, 4 if dt == 0 else 2, W)[0]
+                assert lib_workspace(B, S, H, Hkv, M, W, dt, D) == want, (B, S, H, Hkv, M, W, dt, D)
 
 
 def test_ragged_continuation_is_split():
