@@ -49,8 +49,8 @@ DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
                 "18888959ac127026e4519d190334f2a6a4eca49f9babe47caf957e46958b39df",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "9375556f61ec86da828769c99791203ec998440fccd61fa074bbbf7e60d46258"},
-    "fetch_kib": 73702.938, "write_kib": 1050.305,
+                "c416f1afc0f6b23e8ab84a09f5eb6598e0f1945376d49eafded9a328ed61c3f8"},
+    "fetch_kib": 73704.760, "write_kib": 1050.339,
     "fetch_scale": 524288.0 / 262157.088, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
