@@ -766,10 +766,17 @@ def test_split_prefill_repeated_calls_share_workspace(gpu):
 # seeded random combinations of the features (fixed seeds: a regular test)
 # --------------------------------------------------------------------------
 
-def _random_case(k):
+def _random_case(k, head_size=None, salt=0):
+    """Case k of the random feature mix; with `head_size`, a 2-byte dtype at
+    that head size (its own seeds through `salt`)."""
+    k = k + salt
     rng = np.random.default_rng(1000 + k)
-    dt = ["fp16", "bf16", "fp32"][rng.integers(0, 3)]
-    D = 128 if dt != "fp32" and rng.random() < 0.8 else int(rng.choice([8, 64, 128]))
+    if head_size is None:
+        dt = ["fp16", "bf16", "fp32"][rng.integers(0, 3)]
+        D = 128 if dt != "fp32" and rng.random() < 0.8 else int(rng.choice([8, 64, 128]))
+    else:
+        dt = ["fp16", "bf16"][rng.integers(0, 2)]
+        D = head_size
     Hkv = int(rng.choice([1, 2, 4]))
     G = int(rng.choice([1, 2, 4, 7]))
     B = int(rng.integers(1, 5))
@@ -804,10 +811,19 @@ def _random_case(k):
 
 @pytest.mark.parametrize("k", range(40))
 def test_random_feature_combinations(k):
+    _check_random(k, 0, *_random_case(k))
+
+
+# the same mix at head size 64, where fp16/bf16 run the MFMA kernels too
+@pytest.mark.parametrize("k", range(24))
+def test_random_feature_combinations_head_size_64(k):
+    _check_random(k, 10000, *_random_case(k, head_size=64, salt=10000))
+
+
+def _check_random(k, salt, case, present_rows):
     import grouped_query_kv_amd as gqa
-    case, present_rows = _random_case(k)
     entry = "decode" if case.new_tokens == 1 else "prefill"
-    desc = (f"random {k}: {case.dtype} B={case.batch} S={case.new_tokens} H={case.num_heads} "
+    desc = (f"random {k} (salt {salt}): {case.dtype} B={case.batch} S={case.new_tokens} H={case.num_heads} "
             f"Hkv={case.kv_num_heads} D={case.head_size} M={case.max_seq_len} W={case.local_window_size} "
             f"greedy={case.greedy_eviction} rot={case.cos is not None} "
             f"bias={None if case.attention_bias is None else case.attention_bias.shape} "
@@ -817,7 +833,7 @@ def test_random_feature_combinations(k):
         check_full(case, entry, desc)
         return
     say(f"[gpu] {desc}")
-    rng = np.random.default_rng(3000 + k)
+    rng = np.random.default_rng(3000 + k + salt)
     past_k = gi.fill_cache(rng, case.batch, case.kv_num_heads, present_rows, case.head_size,
                            case.seqlens_k, case.dtype)
     past_v = gi.fill_cache(rng, case.batch, case.kv_num_heads, present_rows, case.head_size,
