@@ -618,6 +618,34 @@ def test_ragged_continuation_full_size():
     check_full(case, "prefill", f"ragged continuation (every row) lens={case.seqlens_k.tolist()}")
 
 
+# the shapes of the decode, window, causal prefill and continuation
+# workloads at head size 64: every output against the oracle, both caches
+# bit for bit
+HEAD64_FULL = [
+    ("decode", "fp16", 16, 1, 32, 8, 4096, "U512-4095", -1, False),
+    ("decode", "bf16", 8, 1, 32, 8, 4096, "full", 4096, False),
+    ("prefill", "bf16", 4, 2048, 32, 8, 4096, "empty", -1, True),
+    ("prefill", "fp16", 8, 128, 28, 4, 4096, "U0-3072", -1, False),
+]
+
+
+@pytest.mark.parametrize("spec", HEAD64_FULL, ids=["decode", "window", "causal", "continuation"])
+def test_head_size_64_full_shapes(spec):
+    entry, dt, B, S, H, Hkv, M, kind, W, rot = spec
+    seed = sum(map(ord, repr(spec))) % 1000
+    rng = np.random.default_rng(seed)
+    if kind == "full":
+        lens = [M] * B
+    elif kind == "empty":
+        lens = [0] * B
+    else:
+        lo, hi = (int(x) for x in kind[1:].split("-"))
+        lens = rng.integers(lo, hi + 1, B).tolist()
+    case = gi.make_case("head64-full", dt, B, S, H, Hkv, 64, M, lens, seed, window=W, rotary=rot,
+                        rotary_rows=(M if rot else None))
+    check_full(case, entry, f"head size 64 {spec} lens={lens}")
+
+
 # --------------------------------------------------------------------------
 # no shared state: two calls in flight on two streams, own workspaces
 # --------------------------------------------------------------------------
