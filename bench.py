@@ -7,7 +7,9 @@ Prints ONE JSON line. The headline step is the fp16 split-KV decode
 The same line carries the bf16 causal prefill (B=4, H=32, Hkv=8, D=128,
 S=2048, rotary; TFLOP/s over causal pairs), the fp16 ragged continuation
 (B=8, H=28, Hkv=4, S=128) and the bf16 sliding-window decode (B=8, M=W=4096,
-cache full, evict one row per step), each with its roofline fraction.
+cache full, evict one row per step), each with its roofline fraction, then
+the secondary legs (windowed chunks, separate past/present, greedy eviction,
+attention bias, and the decode and causal prefill at head size 64).
 
 Timing: inputs are resident in HBM before the timed region; each step rotates
 over enough independent input sets (>= 1 GiB) that the 256 MB Infinity Cache
@@ -383,7 +385,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="decode,prefill,continuation,window,chunks,present,greedy,bias",
+    ap.add_argument("--only", default="decode,prefill,continuation,window,chunks,present,greedy,bias,"
+                                      "head64",
                     help="workloads to run, comma-separated; the split-KV decode (the headline) "
                          "always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -413,7 +416,7 @@ def main():
     torch.cuda.set_device(0)
     which = set(args.only.split(","))
     unknown = which - {"decode", "prefill", "continuation", "window", "chunks", "present", "greedy",
-                       "bias"}
+                       "bias", "head64"}
     if unknown:
         sys.exit(f"--only: unknown workloads {sorted(unknown)}")
     result = {}
@@ -577,6 +580,29 @@ def main():
             "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
             "frac_mfma_peak": fl / (st["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
             "ms_per_call_wall": w, **st}
+
+    if "head64" in which:
+        # the headline decode and the causal prefill at head size 64 (the same
+        # past lengths; fresh draws of the values)
+        d64 = gi.make_case("split-kv-decode-fp16-d64", "fp16", 16, 1, 32, 8, 64, 4096,
+                           dec.seqlens_k, 12)
+        w, st = run_leg(torch, "decode, head size 64", d64, decode_call(gqa), args.steps, args.warmup)
+        byts = decode_bytes(d64, [int(x) for x in d64.seqlens_k])
+        extra["decode_head64"] = {
+            "workload": "fp16 decode B=16 H=32 Hkv=8 D=64 M=4096, the headline's past lengths",
+            "gbs": byts / (st["mean_ms"] * 1e-3) / 1e9, "bytes_per_call": byts,
+            "frac_hbm_peak": byts / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_per_call_wall": w, **st}
+        p64 = gi.make_case("causal-prefill-bf16-d64", "bf16", 4, 2048, 32, 8, 64, 4096, [0] * 4, 13,
+                           rotary=True, rotary_rows=4096)
+        w, st = run_leg(torch, "causal prefill, head size 64", p64, prefill_call(gqa),
+                        max(5, args.steps // 2), max(2, args.warmup // 2))
+        fl = prefill_flops(p64)
+        extra["causal_prefill_head64"] = {
+            "workload": "bf16 causal prefill B=4 H=32 Hkv=8 D=64 S=2048 rotary",
+            "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
+            "frac_mfma_peak": fl / (st["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+            "flops": fl, "ms_per_call_wall": w, **st}
 
     cpu = None
     if not args.no_cpu_baseline:
