@@ -97,6 +97,9 @@ struct DecodeArgs {
   uint16_t* halo_k;                     // fused eviction: one row per worker, [workers, D]: the
   uint16_t* halo_v;                     //   source row after its slice that the next slice overwrites
   int shift;                            // fused eviction on: full sequences drop their oldest row
+  const uint16_t* past_k;               // fused past copy: the rows [0, L_b) are read from these
+  const uint16_t* past_v;               //   buffers (past_rows rows per (b, kv head)) and written
+  int past_rows;                        //   to k_cache/v_cache at the same row (past_k != nullptr)
   int B, H, Hkv, G, M, W;
   int cap;                              // rows an evicting sequence keeps: M - 1, or W - 1 (greedy)
   int rot, rot_rows, interleaved;
@@ -314,8 +317,16 @@ __device__ inline KV load_kv(const DecodeArgs& a, const Blk& k, int n, int q4, b
   // here rather than kept live through the stream)
   const int worker = int(blockIdx.x) * kDecodeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t hrow = int64_t(worker) * D + 8 * q4;
-  const uint16_t* kp = halo ? a.halo_k + hrow : k.kc + int64_t(src) * D + 8 * q4;
-  const uint16_t* vp = halo ? a.halo_v + hrow : k.vc + int64_t(src) * D + 8 * q4;
+  const uint16_t* kb = k.kc;
+  const uint16_t* vb = k.vc;
+  if (a.past_k) {
+    // fused past copy: the unit's rows come from the past buffers
+    const int64_t pbase = (int64_t(k.b) * a.Hkv + k.g) * a.past_rows * D;
+    kb = a.past_k + pbase;
+    vb = a.past_v + pbase;
+  }
+  const uint16_t* kp = halo ? a.halo_k + hrow : kb + int64_t(src) * D + 8 * q4;
+  const uint16_t* vp = halo ? a.halo_v + hrow : vb + int64_t(src) * D + 8 * q4;
   if (k.Lp < k.kb + kKeys) {
     // the block of the new token: that key's K and V rows come from k_new
     // and v_new (the cache row is written when the block is computed), in
@@ -418,10 +429,12 @@ __device__ inline void compute(Acc& s, KV r, const Q4& qv, const Blk& k,
       }
     }
   }
-  if (k.d && k.ub % a.n_hg == 0 && k.kb + n < k.kend) {
+  if ((k.d || a.past_k) && k.ub % a.n_hg == 0 && k.kb + n < k.kend) {
     // fused eviction: key kb + n now lives in buffer row kb + n (its source
     // rows of this block are already in registers; the row this overwrites
-    // for the previous block was read from the halo copy)
+    // for the previous block was read from the halo copy). Fused past copy
+    // (d = 0): the row read from the past buffer goes to the same row of
+    // the cache.
     const int64_t crow = int64_t(k.kb + n) * D + 8 * q4;
     uint4* kc = reinterpret_cast<uint4*>(const_cast<uint16_t*>(k.kc) + crow);
     uint4* vc = reinterpret_cast<uint4*>(const_cast<uint16_t*>(k.vc) + crow);
@@ -1006,6 +1019,9 @@ hipError_t launch_decode_batch(const Problem& p, void* ws, const WorkspaceLayout
   a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scratch);
   a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) + lay.counters);
   a.shift = fuse_evict ? 1 : 0;
+  a.past_k = static_cast<const uint16_t*>(p.past_k);
+  a.past_v = static_cast<const uint16_t*>(p.past_v);
+  a.past_rows = p.past_rows;
   a.halo_k = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.decode_halo);
   a.halo_v = a.halo_k + int64_t(kDecodeMaxWorkers) * p.D;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.G = p.G; a.M = p.M; a.W = p.window; a.cap = p.cap;
@@ -1066,6 +1082,11 @@ hipError_t launch_decode_fast(const Problem& p, void* ws, const WorkspaceLayout&
     c.v_new = static_cast<const uint16_t*>(p.v_new) + kvrow;
     c.k_cache = static_cast<uint16_t*>(p.k_cache) + crow;
     c.v_cache = static_cast<uint16_t*>(p.v_cache) + crow;
+    if (p.past_k) {
+      const int64_t prow = int64_t(b0) * p.Hkv * p.past_rows * p.D;
+      c.past_k = static_cast<const uint16_t*>(p.past_k) + prow;
+      c.past_v = static_cast<const uint16_t*>(p.past_v) + prow;
+    }
     c.lens_host = p.lens_host + b0;
     c.lens_dev = p.lens_dev ? p.lens_dev + b0 : nullptr;
     c.off_host = p.off_host ? p.off_host + b0 : nullptr;

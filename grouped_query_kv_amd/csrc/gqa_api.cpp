@@ -258,6 +258,18 @@ gqa_status static_layout(const WorkspaceLayout& lay, WorkspaceLayout* out) {
   return GQA_OK;
 }
 
+// Whether the split-KV decode can read a call's past rows straight from
+// separate past buffers and write them to the cache itself: one new token,
+// the MFMA decode, nothing evicted, and every row [0, L_b) attended (no
+// window, or one that reaches row 0 of every sequence).
+bool past_reads_fused(const Problem& P, bool needs_evict) {
+  if (P.S != 1 || needs_evict || !decode_fast_supported(P)) return false;
+  if (P.window > 0)
+    for (int b = 0; b < P.B; ++b)
+      if (P.lens_host[b] + 1 > P.window) return false;
+  return true;
+}
+
 // The kernels of one validated call, on the workspace `ws` carved as `lay`.
 // S == 1 takes the split-KV decode route.
 gqa_status execute(const Problem& P, bool needs_evict, int max_drop, void* ws,
@@ -294,7 +306,8 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
                          const void* q, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, const int32_t* lens_host, const int32_t* lens_dev,
                          void* out, void* ws, size_t ws_bytes, void* stream,
-                         bool static_scratch = false) {
+                         bool static_scratch = false, const void* past_k = nullptr,
+                         const void* past_v = nullptr, int past_rows = 0) {
   g_err[0] = '\0';
   Problem P;
   bool needs_evict;
@@ -302,6 +315,15 @@ gqa_status run_attention(Entry entry, const gqa_shape* shape, const gqa_options*
   gqa_status st = validate(entry, shape, opts, q, k_new, v_new, k_cache, v_cache, lens_host,
                            lens_dev, out, &P, &needs_evict, &max_drop);
   if (st != GQA_OK) return st;
+  if (past_k) {
+    // the split-KV decode copies the past rows on its way (the caller
+    // checked that it reads all of them)
+    if (!past_reads_fused(P, needs_evict))
+      return fail(GQA_ERR_INVALID_ARG, "fused past copy requested for a call that cannot take it");
+    P.past_k = past_k;
+    P.past_v = past_v;
+    P.past_rows = past_rows;
+  }
   WorkspaceLayout lay;
   if (static_scratch) {
     st = static_layout(workspace_layout(*shape, P.window), &lay);
@@ -477,6 +499,13 @@ gqa_status gqa_attention_present(const gqa_shape* shape, const gqa_options* opts
   st = check_workspace(shape, P.window, workspace, workspace_bytes, &lay);
   if (st != GQA_OK) return st;
   if (P.B == 0) return GQA_OK;
+  if (!same && past_reads_fused(P, needs_evict)) {
+    // one new token on the split-KV decode: it reads every past row once
+    // anyway, so it writes them into present as it goes (no separate copy)
+    return run_attention(kPrefill, shape, opts, q, k_new, v_new, present_key, present_value,
+                         seqlens_k_host, seqlens_k_dev, out, workspace, workspace_bytes, stream,
+                         false, past_key, past_value, past_rows);
+  }
   if (!same) {
     hipError_t e = launch_copy_prefix(past_key, past_value, past_rows, present_key, present_value,
                                       P.M, seqlens_k_dev, P.B, P.Hkv,

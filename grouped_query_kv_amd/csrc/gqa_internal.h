@@ -49,6 +49,13 @@ struct Problem {
   const void* stage_k = nullptr;
   const void* stage_v = nullptr;
   int cache_rows = 0;
+  // separate past buffers read by the split-KV decode, which writes every
+  // past row it reads into k_cache/v_cache at the same row (past_k !=
+  // nullptr; past_rows rows per (b, kv head)); only when the decode reads
+  // rows [0, L_b) of every sequence (no eviction, window off or covering)
+  const void* past_k = nullptr;
+  const void* past_v = nullptr;
+  int past_rows = 0;
 };
 
 // Workspace carving (byte offsets from the workspace base). The layout is a

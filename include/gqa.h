@@ -219,8 +219,12 @@ gqa_status gqa_attention_decode(const gqa_shape* shape, const gqa_options* opts,
  * and are only read; present_key/present_value [B, Hkv, M, D] (M =
  * shape->max_seq_len) receive past rows [0, L_b) at the same rows, then the
  * call proceeds exactly as gqa_attention_prefill on the present buffers
- * (any S >= 1; one token per sequence takes the split-KV decode). Present
- * rows [L_b + S, M) are not written, past is never written; afterwards the
+ * (any S >= 1; one token per sequence takes the split-KV decode). When the
+ * split-KV decode reads every row [0, L_b) (S = 1, fp16/bf16, D = 128 or
+ * 64, nothing evicted, the window off or reaching row 0) it moves the past
+ * rows itself as it reads them, with no separate copy; the result is the
+ * same. Present rows [L_b + S, M) are not written, past is never written;
+ * afterwards the
  * present buffers can serve as a shared buffer for the next call.
  * Passing the same K and V buffers as past and present (with past_rows = M)
  * is the shared mode and copies nothing; any other overlap of past and

@@ -169,6 +169,15 @@ PRESENT = [
     ("fp32", 2, 5, 4, 2, 8, 20, 25, [20, 3], -1, False, "prefill"),
     ("bf16", 2, 40, 8, 2, 128, 256, 256, [256, 200], 128, False, "prefill"),   # present evicts
     ("fp16", 2, 1, 8, 2, 128, 512, 512, [512, 100], 512, True, "decode"),     # decode evicts
+    # one new token on the split-KV decode, which copies the past rows into
+    # present as it reads them: head size 64 with a window reaching row 0,
+    # more than 64 sequences (the launches of 64 offset the past buffers
+    # too), two head groups (only the first writes), and a window that does
+    # not reach row 0 (the separate copy)
+    ("bf16", 4, 1, 16, 2, 64, 300, 400, [299, 0, 150, 17], 301, True, "decode"),
+    ("fp16", 70, 1, 8, 2, 128, 96, 128, [(13 * i) % 97 for i in range(70)], -1, False, "decode"),
+    ("bf16", 2, 1, 64, 2, 128, 200, 256, [199, 64], -1, True, "decode"),
+    ("fp16", 2, 1, 8, 2, 128, 256, 300, [255, 10], 100, False, "decode"),
 ]
 
 
