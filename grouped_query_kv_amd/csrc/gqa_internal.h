@@ -88,7 +88,7 @@ constexpr int kPrefillWgRows = 256;
 constexpr int kPrefillTargetWorkgroups = 256;   // one per CU
 constexpr int kPrefillMaxSplits = 4;            // slots per row block in the workspace
 constexpr int kPrefillPlanMax = 512;            // workgroups a split plan can list
-constexpr size_t kPrefillSlotFloats = 512 * 64 + 2 * 512;
+constexpr size_t kPrefillSlotFloats = 512 * 32 + 2 * 512;
 
 // A function of the shape only (the workspace is sized from it): whether the
 // row blocks may be split, i.e. they fill less than three quarters of the

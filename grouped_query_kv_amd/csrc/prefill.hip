@@ -89,6 +89,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWgRows = 32 * kWaves;          // query rows per workgroup
 static_assert(kWgRows == kPrefillWgRows && kThreads == 512, "split slots assume 512 lanes x 256 rows");
 constexpr float kLog2e = 1.4426950408889634f;
+// A split partial: [512 x 32] words of o / l (two 16-bit values each, lane
+// fastest), then the 512 lanes' running maxima and weight sums in fp32.
+constexpr int kSlotM = 512 * 32;
+constexpr int kSlotL = 512 * 33;
+static_assert(kSlotL + 512 == int(kPrefillSlotFloats), "split slot layout");
 // The running maximum used in the exponent is refreshed only when a score
 // exceeds it by more than this many binary orders, so weights stay <= 2^8:
 // exact in fp32, representable in fp16/bf16 with full relative precision.
@@ -723,17 +728,27 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   float l_row = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // the row's weight sum
   if (nsplit > 1) {
     // publish this split's partial, count it in; the last split to finish
-    // merges all of them in split order (the same sum whoever is last)
+    // merges all of them in split order (the same sum whoever is last). The
+    // partial output goes out normalised (o / l, a convex combination of V
+    // rows, so within the dtype's range) and rounded to the dtype, two
+    // values per word: half the bytes of the fp32 accumulators, which all
+    // splits write and the last one reads at the same moment at the end of
+    // the launch. The merging split rounds its own values the same way.
     float* slots = a.partials + int64_t(item) * kPrefillMaxSplits * int64_t(kPrefillSlotFloats);
     float* mine = slots + int64_t(split) * kPrefillSlotFloats;
+    const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
+    auto packed = [&](int dt, int v2) {
+      return Mma32<T>::pack2(o[dt][2 * v2] * inv_l, o[dt][2 * v2 + 1] * inv_l);
+    };
+    uint32_t* mine_o = reinterpret_cast<uint32_t*>(mine);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        __hip_atomic_store(mine + (wave * 64 + dt * 16 + v) * 64 + lane, o[dt][v],
+      for (int v2 = 0; v2 < 8; ++v2)
+        __hip_atomic_store(mine_o + (wave * 32 + dt * 8 + v2) * 64 + lane, packed(dt, v2),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(mine + 512 * 64 + tid, rs.m_use, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(mine + 512 * 65 + tid, l_row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + kSlotM + tid, rs.m_use, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + kSlotL + tid, l_row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // release/acquire handoff: the workgroup barrier orders every thread's
     // partial stores before the count; the counting thread's increment
     // releases them at agent scope (each increment continues the release
@@ -765,9 +780,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       if (j < nsplit) {
         const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
         mj[j] = j == split ? rs.m_use
-                           : __hip_atomic_load(sj + 512 * 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                           : __hip_atomic_load(sj + kSlotM + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lj[j] = j == split ? l_row
-                           : __hip_atomic_load(sj + 512 * 65 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                           : __hip_atomic_load(sj + kSlotL + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (lj[j] > 0.f) M = fmaxf(M, mj[j]);   // a split that saw no key of the row adds nothing
       }
     }
@@ -777,26 +792,24 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+    using Bits = typename T::bits;
 #pragma unroll
     for (int j = 0; j < kPrefillMaxSplits; ++j) {
       if (j >= nsplit) break;
       const float wj = lj[j] > 0.f ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
       l_acc = fmaf(lj[j], wj, l_acc);
-      const float* sj = slots + int64_t(j) * kPrefillSlotFloats;
-      if (j == split) {
+      const float cj = lj[j] * wj;          // weight of the normalised partial
+      const uint32_t* sj = reinterpret_cast<const uint32_t*>(slots + int64_t(j) * kPrefillSlotFloats);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[dt][v] = fmaf(o[dt][v], wj, acc[dt][v]);
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            acc[dt][v] = fmaf(__hip_atomic_load(sj + (wave * 64 + dt * 16 + v) * 64 + lane,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                              wj, acc[dt][v]);
-      }
+        for (int v2 = 0; v2 < 8; ++v2) {
+          const uint32_t w = j == split ? packed(dt, v2)
+                                        : __hip_atomic_load(sj + (wave * 32 + dt * 8 + v2) * 64 + lane,
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          acc[dt][2 * v2] = fmaf(T::to_float(Bits(w & 0xFFFFu)), cj, acc[dt][2 * v2]);
+          acc[dt][2 * v2 + 1] = fmaf(T::to_float(Bits(w >> 16)), cj, acc[dt][2 * v2 + 1]);
+        }
     }
     l_row = l_acc;
 #pragma unroll

@@ -23,7 +23,7 @@ import numpy as np
 import pytest
 
 WG_ROWS, BK, MAX_SPLITS, PLAN_MAX, TARGET_WG = 256, 64, 4, 512, 256
-SLOT_FLOATS = 512 * 64 + 2 * 512
+SLOT_FLOATS = 512 * 32 + 2 * 512
 DECODE_WG, DECODE_WAVES, DECODE_HG, DECODE_ARG_BATCH = 256, 8, 16, 64
 EVICT_HALO_MAX, EVICT_CHUNK_ROWS = 4, 128
 
