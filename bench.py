@@ -51,8 +51,8 @@ DECODE_TRAFFIC = {
     "sources": {"grouped_query_kv_amd/csrc/decode.hip":
                 "bd13273628e645f22c93f0a05b9da027d612a8adf8e743e40b7862c819c56b2a",
                 "grouped_query_kv_amd/csrc/gqa_internal.h":
-                "729acdc467b133de86bc1964da8c5e27ff15b009b36f5f8bb5738398d94dcbfa"},
-    "fetch_kib": 73713.957, "write_kib": 1050.329,
+                "4b62ef6cda1715062c2911657a2c20031b59281584c6ee04135249d3f3439172"},
+    "fetch_kib": 73715.043, "write_kib": 1050.310,
     "fetch_scale": 524288.0 / 262157.088, "write_scale": 1.0,
 }
 POISON16 = {"fp16": 0x7E5A, "bf16": 0x7FC5}
