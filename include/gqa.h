@@ -94,7 +94,8 @@ typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NO_ROOM = 1,      /* some L_b + S > M with the window off */
   GQA_ERR_INVALID_ARG = 2,  /* bad shape, option, pointer or length */
-  GQA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (no call returns it at present) */
+  GQA_ERR_UNSUPPORTED = 3,  /* valid but not served: gqa_attention_decode_noalloc on a device
+                               beyond the ones its static scratch covers */
   GQA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than needed */
   GQA_ERR_HIP = 5           /* a HIP launch failed */
 } gqa_status;
