@@ -278,10 +278,11 @@ gqa_status gqa_evict_window(const gqa_shape* shape, int32_t incoming,
  * array, which keeps the last call's contents: calls that overlap in time on
  * one GPU (two streams, two host threads) race and give undefined results.
  * The first call on a device, and the first after a GQA_ERR_HIP, zeroes the
- * array's counter area with a small kernel on `stream`. The work plan and
- * the past lengths the kernels use are taken from seqlens_k_host when the
+ * array's counter area with a small kernel on `stream`. The split-KV
+ * decode takes its work plan and past lengths from seqlens_k_host when the
  * call is made; under graph capture that is when it is captured, so a
- * replay repeats the call for the captured lengths.
+ * replay is valid only for the captured lengths (with seqlens_k_dev holding
+ * the same values).
  */
 gqa_status gqa_attention_decode_noalloc(const gqa_shape* shape, const gqa_options* opts,
                                         const void* q, const void* k_new, const void* v_new,
