@@ -371,6 +371,53 @@ def test_attention_bias_decode_full_size():
     check_full(case, "decode", "split-KV decode with a [B, H, 1, T] bias")
 
 
+# one-token calls with separate past and present buffers on the split-KV
+# decode, which moves the past rows itself: random shapes with bias, rotary
+# position offsets, several head groups and more than 64 sequences
+@pytest.mark.parametrize("k", range(12))
+def test_present_decode_fused_copy_random(k):
+    import grouped_query_kv_amd as gqa
+    rng = np.random.default_rng(9000 + k)
+    dt = ["fp16", "bf16"][int(rng.integers(0, 2))]
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 4, 7, 20]))
+    B = int(rng.choice([1, 3, 17, 66]))
+    P = int(rng.choice([64, 200, 513]))
+    M = P + int(rng.integers(1, 40))
+    lens = rng.integers(0, P + 1, B).tolist()
+    W = -1 if rng.random() < 0.6 else max(lens) + 1 + int(rng.integers(0, 5))
+    rot = bool(rng.random() < 0.5)
+    case = gi.make_case("present-fused", dt, B, 1, G * Hkv, Hkv, D, M, [0] * B, 9100 + k, window=W,
+                        rotary=rot, rotary_rows=(M + 41 if rot else None))
+    case.seqlens_k = np.asarray(lens, np.int32)
+    if rot and rng.random() < 0.5:
+        case.position_offset = rng.integers(0, 40, B).astype(np.int32)
+    if rng.random() < 0.4:
+        T = max(lens) + 1 + int(rng.integers(0, 5))
+        case.attention_bias = gi.to_bits(rng.standard_normal((B, G * Hkv, 1, T)), dt)
+    past_k = gi.fill_cache(rng, B, Hkv, P, D, lens, dt)
+    past_v = gi.fill_cache(rng, B, Hkv, P, D, lens, dt)
+    desc = f"present fused {k}: {dt} B={B} G={G} Hkv={Hkv} D={D} P={P} M={M} W={W} rot={rot}"
+    say(f"[gpu] {desc}")
+    st, want, kc, vc, _ = O.gqa_attention_present(case, past_k, past_v)
+    assert st == O.OK
+    dev = DevCase(case)
+    pk, pv = to_dev(past_k, dt), to_dev(past_v, dt)
+    out = gqa.gqa_attention_decode(dev.q, dev.k_new, dev.v_new, pk, pv, dev.lens_host, dev.lens_dev,
+                                   scale=case.scale, local_window_size=W, cos_cache=dev.cos,
+                                   sin_cache=dev.sin, present_key=dev.k_cache,
+                                   present_value=dev.v_cache, attention_bias=dev.bias,
+                                   position_offset=dev.off_host, position_offset_dev=dev.off_dev)
+    gk, gv = dev.caches()
+    assert_bits_equal(gk, kc, f"{desc} present k")
+    assert_bits_equal(gv, vc, f"{desc} present v")
+    assert_bits_equal(to_bits(pk), past_k, f"{desc} past k (never written)")
+    assert_bits_equal(to_bits(pv), past_v, f"{desc} past v (never written)")
+    err = assert_close(out_f64(out, dt), want, dt, desc)
+    say(f"[gpu]   max abs error {err:.3e}")
+
+
 # --------------------------------------------------------------------------
 # the halves: append and eviction on their own
 # --------------------------------------------------------------------------
